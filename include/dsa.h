@@ -1,0 +1,190 @@
+/*
+ * dsa.h -- C ABI of the indexed sparse attention (DSA) hot path for AMD
+ * Instinct MI355X (gfx950).
+ *
+ * For each query token the path runs three steps (pages: "Day-0 Inference
+ * Optimization for a New Sparse Attention Architecture: A Technical Deep
+ * Dive", section 1, Lightning Indexer and Sparse Flash Attention; "Inference
+ * Adaptation and Performance Optimization for New Large Language Model
+ * Architectures", the illustrative pseudocode in which a lightning indexer
+ * returns indices and sparse flash attention consumes them):
+ *
+ *   1. Lightning Indexer score of every causal history position s <= q_pos:
+ *        I[t,s] = sum_j w[t,j] * max(0, q_I[t,j,:] . k_I[s,:])
+ *      (one indexer key per position, shared by all H_I indexer heads);
+ *   2. Top-K: the K highest-scoring positions, ties to the lower position;
+ *   3. sparse absorbed-MLA attention of the token's H query heads over only
+ *      the selected latent rows: keys are the full 576-wide rows (512 latent
+ *      + 64 rope), values their first 512 features, softmax scale given.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Tensor pointers are DEVICE pointers, 16-byte aligned, row-major and
+ *   densely packed in the layouts stated per argument.  Scalars are host
+ *   values.  The caller owns every buffer; the library never allocates,
+ *   frees or synchronises.
+ * - bf16 tensors hold IEEE bfloat16 bit patterns (uint16).  FP8 tensors hold
+ *   OCP e4m3fn codes (uint8) with one OCP e8m0 scale code per 32 consecutive
+ *   features of a row (the "MX block-32" layout: page "Optimizing Inference
+ *   for New Model Architectures", section 4, one shared scale per group of
+ *   32; the "Technical Deep Dive" page, section 2, names it MXFP8).  The
+ *   value of element i of a row is e4m3(code[i]) * 2^(scale[i/32] - 127).
+ *   Dequantisation is exact while the product is a normal bf16 number.
+ * - `stream` is a hipStream_t (NULL = the legacy default stream).  Every call
+ *   only enqueues kernels on it and returns.
+ * - Errors: argument and shape checks run on the host before any HIP call and
+ *   return a non-zero dsa_status without touching any buffer.  A launch
+ *   failure returns DSA_ERR_HIP.  Faults inside kernels surface at the
+ *   caller's next synchronisation.  dsa_last_error() gives a message for the
+ *   last failing call on the calling thread.
+ * - The library is stateless and thread-safe; calls that share an output or
+ *   workspace buffer on different streams race.
+ *
+ * Support set: indexer heads 1 <= H_I <= 64; indexer dim d_I in {64, 128};
+ * MLA heads 1 <= H <= 128; latent width 576, value width 512; 1 <= K <= 2048;
+ * page size 64.
+ */
+#ifndef DSA_H_
+#define DSA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum dsa_status {
+  DSA_OK = 0,
+  DSA_ERR_NULL = 1,         /* a required pointer is NULL                  */
+  DSA_ERR_SHAPE = 2,        /* a size is negative, zero or inconsistent    */
+  DSA_ERR_UNSUPPORTED = 3,  /* a size or dtype outside the support set     */
+  DSA_ERR_WORKSPACE = 4,    /* workspace missing or smaller than required  */
+  DSA_ERR_HIP = 5           /* a HIP launch failed                          */
+} dsa_status;
+
+typedef enum dsa_dtype {
+  DSA_BF16 = 0,             /* bfloat16 values                              */
+  DSA_E4M3_MX32 = 1         /* e4m3fn codes + one e8m0 scale per 32 values  */
+} dsa_dtype;
+
+/* Operation selector for dsa_workspace_size. */
+typedef enum dsa_op {
+  DSA_OP_INDEXER_SCORES = 0,
+  DSA_OP_TOPK = 1,
+  DSA_OP_SPARSE_MLA = 2,
+  DSA_OP_DECODE_STEP = 3
+} dsa_op;
+
+#define DSA_LATENT_DIM 576
+#define DSA_VALUE_DIM 512
+#define DSA_PAGE_SIZE 64
+#define DSA_MAX_TOPK 2048
+
+/*
+ * One layer's paged cache: indexer keys and latent KV in two page pools that
+ * share one page table (page "Optimizing Inference for New Model
+ * Architectures", section 3: the fused indexer reads the paged key cache
+ * directly).  Logical position s of sequence b lives in physical page
+ * page_table[b * max_pages_per_seq + s / 64], row s % 64.  Entries past a
+ * sequence's last page are never read.
+ */
+typedef struct dsa_paged_cache {
+  int32_t page_size;          /* tokens per page; must be 64                */
+  int32_t num_pages;          /* pages in each pool                          */
+  int32_t max_pages_per_seq;  /* columns of page_table                       */
+  int32_t kidx_dtype;         /* dsa_dtype of the indexer-key pool           */
+  int32_t kv_dtype;           /* dsa_dtype of the latent-KV pool             */
+  const void* kidx;           /* [num_pages, 64, d_I] bf16 or e4m3 codes     */
+  const uint8_t* kidx_scale;  /* [num_pages, 64, d_I/32] e8m0; NULL if bf16  */
+  const void* kv;             /* [num_pages, 64, 576] bf16 or e4m3 codes     */
+  const uint8_t* kv_scale;    /* [num_pages, 64, 18] e8m0; NULL if bf16      */
+  const int32_t* page_table;  /* [B, max_pages_per_seq] int32               */
+  const int32_t* seq_lens;    /* [B] tokens in the cache, current ones incl. */
+} dsa_paged_cache;
+
+/*
+ * Lightning Indexer scores over a contiguous key cache (step 1).
+ *   q_idx   [B, T, H_I, d_I] bf16   indexer queries
+ *   w       [B, T, H_I] fp32        head weights
+ *   k_idx   [B, L, d_I]             bf16, or e4m3 codes if k_dtype is MX
+ *   k_scale [B, L, d_I/32] e8m0     (NULL unless k_dtype == DSA_E4M3_MX32)
+ *   q_pos   [B, T] int32            position of each query, 0 <= q_pos < L
+ *   scores  [B, T, L] fp32 out      I[t,s] for s <= q_pos, -inf beyond
+ * Scores are summed in fp32; for integer-valued q/k and power-of-two
+ * weights they are exact.  -0 is written as +0.
+ */
+dsa_status dsa_indexer_scores(int B, int T, int L, int H_I, int d_I,
+                              const void* q_idx, const float* w,
+                              const void* k_idx, int k_dtype,
+                              const uint8_t* k_scale, const int32_t* q_pos,
+                              float* scores, void* stream);
+
+/*
+ * Top-K per score row (step 2).
+ *   scores [B, T, L] fp32; candidates of row (b,t) are positions
+ *          0..min(q_pos[b,t], L-1); NaN ranks below every number
+ *   q_pos  [B, T] int32
+ *   idx    [B, T, K] int32 out: the min(K, q_pos+1) positions with the
+ *          largest scores (equal scores: lower position first), in ascending
+ *          order, then -1 padding
+ *   workspace: dsa_workspace_size(DSA_OP_TOPK, ...) bytes (may be 0 / NULL)
+ */
+dsa_status dsa_topk(int B, int T, int L, int K, const float* scores,
+                    const int32_t* q_pos, int32_t* idx, void* workspace,
+                    size_t workspace_bytes, void* stream);
+
+/*
+ * Sparse absorbed-MLA attention over selected latent rows of a contiguous
+ * KV cache (step 3).
+ *   q        [B, T, H, 576] bf16    absorbed queries (512 latent + 64 rope)
+ *   kv       [B, L, 576]            bf16, or e4m3 codes if kv_dtype is MX
+ *   kv_scale [B, L, 18] e8m0        (NULL unless kv_dtype == DSA_E4M3_MX32)
+ *   idx      [B, T, K] int32        selected positions; -1 entries skipped;
+ *                                   valid entries must lie in [0, L)
+ *   out      [B, T, H, 512] fp32    softmax-weighted sum of value rows
+ *   lse      [B, T, H] fp32         natural-log sum of exp(scale * q.k);
+ *                                   a row with no valid index gets out = 0,
+ *                                   lse = -inf
+ *   workspace: dsa_workspace_size(DSA_OP_SPARSE_MLA, ...) bytes
+ */
+dsa_status dsa_sparse_mla_attn(int B, int T, int L, int H, int K,
+                               const void* q, const void* kv, int kv_dtype,
+                               const uint8_t* kv_scale, const int32_t* idx,
+                               float softmax_scale, float* out, float* lse,
+                               void* workspace, size_t workspace_bytes,
+                               void* stream);
+
+/*
+ * The whole path for T query tokens per sequence over a paged cache:
+ * indexer -> Top-K -> sparse attention, enqueued on one stream.
+ *   cache         see dsa_paged_cache; seq_lens[b] <= max_seq_len
+ *   max_seq_len   host upper bound of seq_lens (sizes the score workspace)
+ *   q_idx [B, T, H_I, d_I] bf16; w [B, T, H_I] fp32; q [B, T, H, 576] bf16
+ *   q_pos [B, T] int32, or NULL when T == 1: then q_pos = seq_lens[b] - 1
+ *   out [B, T, H, 512] fp32; lse [B, T, H] fp32
+ *   idx_out [B, T, K] int32 or NULL: the selected positions (as dsa_topk)
+ *   workspace: dsa_workspace_size(DSA_OP_DECODE_STEP, B, T, max_seq_len,
+ *              H, K) bytes
+ */
+dsa_status dsa_decode_step(int B, int T, int H_I, int d_I, int H, int K,
+                           float softmax_scale, const dsa_paged_cache* cache,
+                           int max_seq_len, const void* q_idx, const float* w,
+                           const void* q, const int32_t* q_pos, float* out,
+                           float* lse, int32_t* idx_out, void* workspace,
+                           size_t workspace_bytes, void* stream);
+
+/* Bytes of workspace an operation needs for these sizes (L = the context
+ * length, or max_seq_len for DSA_OP_DECODE_STEP).  0 for an unknown op. */
+size_t dsa_workspace_size(int op, int B, int T, int L, int H, int K);
+
+/* Static text for a status code. */
+const char* dsa_status_string(int status);
+
+/* Message describing the last failing call on this thread ("" if none). */
+const char* dsa_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DSA_H_ */

@@ -1,0 +1,275 @@
+// C ABI of the DSA hot path: argument validation (host only, before any HIP
+// call), workspace carving and the launch sequence on the caller's stream.
+// The operations and their semantics are documented in include/dsa.h.
+#include "../../include/dsa.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "dsa_launch.h"
+
+namespace {
+
+thread_local char g_last_error[256] = "";
+
+dsa_status fail(dsa_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+dsa_status ok() {
+  g_last_error[0] = '\0';
+  return DSA_OK;
+}
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool valid_dtype(int d) { return d == DSA_BF16 || d == DSA_E4M3_MX32; }
+
+// Grid limits: B*T query tokens index a grid dimension capped at 65535.
+constexpr int kMaxTokens = 65535;
+
+dsa_status check_indexer_dims(int B, int T, int H_I, int d_I) {
+  if (B < 1 || T < 1) return fail(DSA_ERR_SHAPE, "B and T must be >= 1");
+  if ((long long)B * T > kMaxTokens)
+    return fail(DSA_ERR_UNSUPPORTED, "B*T must be <= %d", kMaxTokens);
+  if (H_I < 1 || H_I > 64)
+    return fail(DSA_ERR_UNSUPPORTED, "H_I must be in [1, 64], got %d", H_I);
+  if (d_I != 64 && d_I != 128)
+    return fail(DSA_ERR_UNSUPPORTED, "d_I must be 64 or 128, got %d", d_I);
+  return DSA_OK;
+}
+
+dsa_status check_attn_dims(int B, int T, int H, int K) {
+  if (B < 1 || T < 1) return fail(DSA_ERR_SHAPE, "B and T must be >= 1");
+  if ((long long)B * T > kMaxTokens)
+    return fail(DSA_ERR_UNSUPPORTED, "B*T must be <= %d", kMaxTokens);
+  if (H < 1 || H > 128)
+    return fail(DSA_ERR_UNSUPPORTED, "H must be in [1, 128], got %d", H);
+  if (K < 1 || K > DSA_MAX_TOPK)
+    return fail(DSA_ERR_UNSUPPORTED, "K must be in [1, %d], got %d",
+                DSA_MAX_TOPK, K);
+  return DSA_OK;
+}
+
+size_t decode_ws(int B, int T, int L, int H, int K) {
+  const size_t tokens = (size_t)B * T;
+  return align_up(tokens * (size_t)L * sizeof(float)) +
+         align_up(tokens * (size_t)K * sizeof(int32_t)) +
+         align_up(dsa::attn_workspace_bytes((int)tokens, H, K));
+}
+
+dsa_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(DSA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* dsa_status_string(int status) {
+  switch (status) {
+    case DSA_OK: return "DSA_OK";
+    case DSA_ERR_NULL: return "DSA_ERR_NULL: a required pointer is NULL";
+    case DSA_ERR_SHAPE: return "DSA_ERR_SHAPE: invalid or inconsistent size";
+    case DSA_ERR_UNSUPPORTED: return "DSA_ERR_UNSUPPORTED: outside the support set";
+    case DSA_ERR_WORKSPACE: return "DSA_ERR_WORKSPACE: workspace too small";
+    case DSA_ERR_HIP: return "DSA_ERR_HIP: HIP launch failed";
+    default: return "unknown dsa_status";
+  }
+}
+
+const char* dsa_last_error(void) { return g_last_error; }
+
+size_t dsa_workspace_size(int op, int B, int T, int L, int H, int K) {
+  if (B < 1 || T < 1 || L < 1 || H < 1 || K < 1) return 0;
+  switch (op) {
+    case DSA_OP_INDEXER_SCORES: return 0;
+    case DSA_OP_TOPK: return 0;
+    case DSA_OP_SPARSE_MLA: return dsa::attn_workspace_bytes(B * T, H, K);
+    case DSA_OP_DECODE_STEP: return decode_ws(B, T, L, H, K);
+    default: return 0;
+  }
+}
+
+dsa_status dsa_indexer_scores(int B, int T, int L, int H_I, int d_I,
+                              const void* q_idx, const float* w,
+                              const void* k_idx, int k_dtype,
+                              const uint8_t* k_scale, const int32_t* q_pos,
+                              float* scores, void* stream) {
+  if (!q_idx || !w || !k_idx || !q_pos || !scores)
+    return fail(DSA_ERR_NULL, "dsa_indexer_scores: NULL tensor pointer");
+  if (dsa_status s = check_indexer_dims(B, T, H_I, d_I)) return s;
+  if (L < 1) return fail(DSA_ERR_SHAPE, "L must be >= 1");
+  if ((long long)B * L > 0x7fffffffLL)
+    return fail(DSA_ERR_UNSUPPORTED, "B*L must fit in int32");
+  if (!valid_dtype(k_dtype))
+    return fail(DSA_ERR_UNSUPPORTED, "unknown key dtype %d", k_dtype);
+  const bool fp8 = k_dtype == DSA_E4M3_MX32;
+  if (fp8 && !k_scale) return fail(DSA_ERR_NULL, "MX keys need k_scale");
+  dsa::IndexerLaunch a{};
+  a.B = B; a.T = T; a.H_I = H_I; a.d_I = d_I;
+  a.q_idx = static_cast<const uint16_t*>(q_idx);
+  a.w = w;
+  a.keys = dsa::CacheView{static_cast<const uint8_t*>(k_idx), k_scale, nullptr,
+                          0, L, fp8};
+  a.qp = dsa::QueryPos{q_pos, nullptr, T};
+  a.scores = scores;
+  a.row_len = L;
+  return hip_status(dsa::launch_indexer(a, (hipStream_t)stream),
+                    "dsa_indexer_scores");
+}
+
+dsa_status dsa_topk(int B, int T, int L, int K, const float* scores,
+                    const int32_t* q_pos, int32_t* idx, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  if (!scores || !q_pos || !idx)
+    return fail(DSA_ERR_NULL, "dsa_topk: NULL tensor pointer");
+  if (B < 1 || T < 1 || L < 1) return fail(DSA_ERR_SHAPE, "B, T, L must be >= 1");
+  if ((long long)B * T > 0x7fffffffLL)
+    return fail(DSA_ERR_UNSUPPORTED, "B*T too large");
+  if (K < 1 || K > DSA_MAX_TOPK)
+    return fail(DSA_ERR_UNSUPPORTED, "K must be in [1, %d], got %d",
+                DSA_MAX_TOPK, K);
+  dsa::TopkLaunch a{};
+  a.rows = B * T; a.T = T; a.L = L; a.K = K;
+  a.scores = scores;
+  a.qp = dsa::QueryPos{q_pos, nullptr, T};
+  a.idx = idx;
+  return hip_status(dsa::launch_topk(a, (hipStream_t)stream), "dsa_topk");
+}
+
+dsa_status dsa_sparse_mla_attn(int B, int T, int L, int H, int K,
+                               const void* q, const void* kv, int kv_dtype,
+                               const uint8_t* kv_scale, const int32_t* idx,
+                               float softmax_scale, float* out, float* lse,
+                               void* workspace, size_t workspace_bytes,
+                               void* stream) {
+  if (!q || !kv || !idx || !out || !lse)
+    return fail(DSA_ERR_NULL, "dsa_sparse_mla_attn: NULL tensor pointer");
+  if (dsa_status s = check_attn_dims(B, T, H, K)) return s;
+  if (L < 1) return fail(DSA_ERR_SHAPE, "L must be >= 1");
+  if ((long long)B * L > 0x7fffffffLL)
+    return fail(DSA_ERR_UNSUPPORTED, "B*L must fit in int32");
+  if (!valid_dtype(kv_dtype))
+    return fail(DSA_ERR_UNSUPPORTED, "unknown kv dtype %d", kv_dtype);
+  const bool fp8 = kv_dtype == DSA_E4M3_MX32;
+  if (fp8 && !kv_scale) return fail(DSA_ERR_NULL, "MX KV needs kv_scale");
+  const size_t need = dsa::attn_workspace_bytes(B * T, H, K);
+  if (need && (!workspace || workspace_bytes < need))
+    return fail(DSA_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", need,
+                workspace ? workspace_bytes : (size_t)0);
+  dsa::AttnLaunch a{};
+  a.B = B; a.T = T; a.H = H; a.K = K;
+  a.q = static_cast<const uint16_t*>(q);
+  a.kv = dsa::CacheView{static_cast<const uint8_t*>(kv), kv_scale, nullptr, 0,
+                        L, fp8};
+  a.idx = idx;
+  a.seq_lens = nullptr;
+  a.scale = softmax_scale;
+  a.out = out;
+  a.lse = lse;
+  a.partial = static_cast<float*>(workspace);
+  a.splits = dsa::attn_splits(B * T, K);
+  return hip_status(dsa::launch_sparse_mla(a, (hipStream_t)stream),
+                    "dsa_sparse_mla_attn");
+}
+
+dsa_status dsa_decode_step(int B, int T, int H_I, int d_I, int H, int K,
+                           float softmax_scale, const dsa_paged_cache* cache,
+                           int max_seq_len, const void* q_idx, const float* w,
+                           const void* q, const int32_t* q_pos, float* out,
+                           float* lse, int32_t* idx_out, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  if (!cache || !q_idx || !w || !q || !out || !lse)
+    return fail(DSA_ERR_NULL, "dsa_decode_step: NULL pointer");
+  if (!cache->kidx || !cache->kv || !cache->page_table || !cache->seq_lens)
+    return fail(DSA_ERR_NULL, "dsa_decode_step: NULL cache pointer");
+  if (dsa_status s = check_indexer_dims(B, T, H_I, d_I)) return s;
+  if (dsa_status s = check_attn_dims(B, T, H, K)) return s;
+  if (!q_pos && T != 1)
+    return fail(DSA_ERR_NULL, "q_pos may be NULL only when T == 1");
+  if (cache->page_size != DSA_PAGE_SIZE)
+    return fail(DSA_ERR_UNSUPPORTED, "page_size must be %d", DSA_PAGE_SIZE);
+  if (cache->num_pages < 1 || cache->max_pages_per_seq < 1)
+    return fail(DSA_ERR_SHAPE, "num_pages and max_pages_per_seq must be >= 1");
+  if ((long long)cache->num_pages * DSA_PAGE_SIZE > 0x7fffffffLL)
+    return fail(DSA_ERR_UNSUPPORTED, "num_pages * 64 must fit in int32");
+  if (max_seq_len < 1 ||
+      (long long)max_seq_len > (long long)cache->max_pages_per_seq * DSA_PAGE_SIZE)
+    return fail(DSA_ERR_SHAPE,
+                "max_seq_len must be in [1, max_pages_per_seq * 64]");
+  if (!valid_dtype(cache->kidx_dtype) || !valid_dtype(cache->kv_dtype))
+    return fail(DSA_ERR_UNSUPPORTED, "unknown cache dtype");
+  const bool kfp8 = cache->kidx_dtype == DSA_E4M3_MX32;
+  const bool vfp8 = cache->kv_dtype == DSA_E4M3_MX32;
+  if (kfp8 && !cache->kidx_scale)
+    return fail(DSA_ERR_NULL, "MX indexer keys need kidx_scale");
+  if (vfp8 && !cache->kv_scale)
+    return fail(DSA_ERR_NULL, "MX KV needs kv_scale");
+  const size_t need = decode_ws(B, T, max_seq_len, H, K);
+  if (!workspace || workspace_bytes < need)
+    return fail(DSA_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", need,
+                workspace ? workspace_bytes : (size_t)0);
+
+  const size_t tokens = (size_t)B * T;
+  char* ws = static_cast<char*>(workspace);
+  float* scores = reinterpret_cast<float*>(ws);
+  ws += align_up(tokens * (size_t)max_seq_len * sizeof(float));
+  int32_t* idx = reinterpret_cast<int32_t*>(ws);
+  ws += align_up(tokens * (size_t)K * sizeof(int32_t));
+  float* partial = reinterpret_cast<float*>(ws);
+  if (idx_out) idx = idx_out;
+
+  const hipStream_t st = (hipStream_t)stream;
+  const dsa::QueryPos qp{q_pos, cache->seq_lens, T};
+
+  dsa::IndexerLaunch ia{};
+  ia.B = B; ia.T = T; ia.H_I = H_I; ia.d_I = d_I;
+  ia.q_idx = static_cast<const uint16_t*>(q_idx);
+  ia.w = w;
+  ia.keys = dsa::CacheView{static_cast<const uint8_t*>(cache->kidx),
+                           cache->kidx_scale, cache->page_table,
+                           cache->max_pages_per_seq, 0, kfp8};
+  ia.qp = qp;
+  ia.scores = scores;
+  ia.row_len = max_seq_len;
+  if (hipError_t e = dsa::launch_indexer(ia, st))
+    return hip_status(e, "dsa_decode_step: indexer");
+
+  dsa::TopkLaunch ta{};
+  ta.rows = (int)tokens; ta.T = T; ta.L = max_seq_len; ta.K = K;
+  ta.scores = scores;
+  ta.qp = qp;
+  ta.idx = idx;
+  if (hipError_t e = dsa::launch_topk(ta, st))
+    return hip_status(e, "dsa_decode_step: topk");
+
+  dsa::AttnLaunch aa{};
+  aa.B = B; aa.T = T; aa.H = H; aa.K = K;
+  aa.q = static_cast<const uint16_t*>(q);
+  aa.kv = dsa::CacheView{static_cast<const uint8_t*>(cache->kv),
+                         cache->kv_scale, cache->page_table,
+                         cache->max_pages_per_seq, 0, vfp8};
+  aa.idx = idx;
+  aa.seq_lens = cache->seq_lens;
+  aa.scale = softmax_scale;
+  aa.out = out;
+  aa.lse = lse;
+  aa.partial = partial;
+  aa.splits = dsa::attn_splits((int)tokens, K);
+  return hip_status(dsa::launch_sparse_mla(aa, st),
+                    "dsa_decode_step: sparse attention");
+}
+
+}  // extern "C"

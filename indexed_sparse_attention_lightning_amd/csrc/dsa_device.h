@@ -1,0 +1,92 @@
+// Device helpers shared by the DSA kernels (gfx950 / CDNA4, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dsa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+constexpr int kLatent = 576;     // absorbed MLA key width (512 latent + 64 rope)
+constexpr int kValue = 512;      // value width
+constexpr int kPage = 64;        // tokens per cache page
+
+__device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+// D = A * B + C on one 32x32x16 bf16 matrix-core tile.
+// Operand layout (wave64): lane l holds row/col (l % 32) and the 8 k-slots
+// 8*(l/32) .. +7 of A resp. B; C/D lane l holds column l % 32 and rows
+// 8*(r/4) + 4*(l/32) + r%4 for accumulator register r = 0..15.
+__device__ __forceinline__ f32x16 mfma32(const uint4& a, const uint4& b,
+                                         f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+      __builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0, 0,
+      0);
+}
+
+// Value held by lane (l ^ 32): the two wave halves exchange registers.
+__device__ __forceinline__ float swap_halves(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(int, x),
+                                            __builtin_bit_cast(int, x), false,
+                                            false);
+  return __builtin_bit_cast(float, lane_id() < 32 ? r[1] : r[0]);
+}
+
+// Two fp32 -> packed bf16x2 (round to nearest even).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  bf16x2v v;
+  v[0] = (__bf16)lo;
+  v[1] = (__bf16)hi;
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// Eight e4m3fn codes (little-endian in a uint2) times 2^(scale_code - 127)
+// -> eight bf16 values (uint4).  The hardware conversion takes the scale as
+// the exponent field of an fp32.  Exact whenever the result is a normal bf16.
+__device__ __forceinline__ uint4 dequant8_e4m3(uint2 codes,
+                                               uint32_t scale_code) {
+  const float s = __builtin_bit_cast(float, scale_code << 23);
+  uint4 r;
+  r.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(
+                                         codes.x, s, false));
+  r.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(
+                                         codes.x, s, true));
+  r.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(
+                                         codes.y, s, false));
+  r.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(
+                                         codes.y, s, true));
+  return r;
+}
+
+// 128-bit non-temporal-hint-free global load / LDS access helpers.
+__device__ __forceinline__ uint4 ld16(const void* p) {
+  return *reinterpret_cast<const uint4*>(p);
+}
+__device__ __forceinline__ uint2 ld8(const void* p) {
+  return *reinterpret_cast<const uint2*>(p);
+}
+
+// Physical row index of logical position s of sequence b.
+// page_table == nullptr: contiguous [B, L, ...] storage (row = b*L + s).
+__device__ __forceinline__ int64_t cache_row(const int32_t* page_table,
+                                             int max_pages, int L, int b,
+                                             int s) {
+  if (page_table == nullptr) return (int64_t)b * L + s;
+  const int pg = page_table[(int64_t)b * max_pages + (s >> 6)];
+  return (int64_t)pg * kPage + (s & (kPage - 1));
+}
+
+// Order-preserving map float -> uint32: larger float <=> larger key.
+// -0 is folded onto +0 and every NaN onto key 0 (below all numbers).
+__device__ __forceinline__ uint32_t score_key(float x) {
+  if (x != x) return 0u;
+  const uint32_t u = __builtin_bit_cast(uint32_t, x + 0.0f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+}  // namespace dsa

@@ -1,0 +1,74 @@
+// Internal launch interface between the C-ABI layer (dsa_api.cpp) and the
+// kernel translation units.  Every function only enqueues work on `stream`
+// and returns hipGetLastError()'s result.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dsa {
+
+// Where a query's history lives: either a contiguous [B, L, width] tensor
+// (page_table == nullptr) or a paged pool read through a page table.
+struct CacheView {
+  const uint8_t* data;        // rows of `row_bytes` bytes
+  const uint8_t* scale;       // e8m0 codes, width/32 per row, or nullptr
+  const int32_t* page_table;  // [B, max_pages] or nullptr (contiguous)
+  int max_pages;
+  int L;                      // contiguous length (rows per sequence)
+  bool fp8;                   // e4m3 codes + MX-32 scales, else bf16
+};
+
+// Query positions: q_pos[b*T + t] if given, else seq_lens[b] - 1; with
+// seq_lens given, a position is clamped to seq_lens[b] - 1.
+struct QueryPos {
+  const int32_t* q_pos;
+  const int32_t* seq_lens;
+  int T;
+};
+
+__device__ __forceinline__ int query_pos(const QueryPos& qp, int b, int t) {
+  int p = qp.q_pos ? qp.q_pos[(int64_t)b * qp.T + t] : qp.seq_lens[b] - 1;
+  if (qp.seq_lens) p = min(p, qp.seq_lens[b] - 1);
+  return p;
+}
+
+struct IndexerLaunch {
+  int B, T, H_I, d_I;
+  const uint16_t* q_idx;   // [B, T, H_I, d_I] bf16
+  const float* w;          // [B, T, H_I]
+  CacheView keys;          // width d_I
+  QueryPos qp;
+  float* scores;           // [B*T, row_len]
+  int row_len;             // positions written per row (L or max_seq_len)
+};
+hipError_t launch_indexer(const IndexerLaunch& a, hipStream_t stream);
+
+struct TopkLaunch {
+  int rows, T, L, K;       // rows = B*T; scores row stride = L
+  const float* scores;
+  QueryPos qp;
+  int32_t* idx;            // [rows, K]
+};
+hipError_t launch_topk(const TopkLaunch& a, hipStream_t stream);
+
+struct AttnLaunch {
+  int B, T, H, K;
+  const uint16_t* q;       // [B, T, H, 576] bf16
+  CacheView kv;            // width 576
+  const int32_t* idx;      // [B*T, K]
+  const int32_t* seq_lens; // [B] valid positions per sequence, or nullptr
+                           // (contiguous: kv.L)
+  float scale;             // softmax scale
+  float* out;              // [B*T, H, 512]
+  float* lse;              // [B*T, H]
+  float* partial;          // workspace for split partials (may be unused)
+  int splits;              // row splits per token (>= 1)
+};
+// Number of row splits the attention uses for a shape, and the workspace
+// bytes its partials need.
+int attn_splits(int tokens, int K);
+size_t attn_workspace_bytes(int tokens, int H, int K);
+hipError_t launch_sparse_mla(const AttnLaunch& a, hipStream_t stream);
+
+}  // namespace dsa

@@ -1,0 +1,247 @@
+// Lightning Indexer score kernels (gfx950).
+//
+// Score of query t against history position s (page "Day-0 Inference
+// Optimization for a New Sparse Attention Architecture: A Technical Deep
+// Dive", section 1 -- relevance scoring with head weights; page "Day-0
+// Inference Adaptation and Performance Optimization for New-Architecture Large
+// Language Models", section "Fusing the Indexer to Reduce Intermediate
+// Write-Backs"):
+//     I[t,s] = sum_j w[t,j] * max(0, q_I[t,j,:] . k_I[s,:])
+//
+// Decode is a stream over the key cache: every key row is read exactly once
+// per query and scored against all indexer heads of that query on the matrix
+// cores (heads form the MFMA M dimension, keys the N dimension, the key
+// features the K dimension).  Per wave:
+//   * the query's q_I (all heads) sits in registers as MFMA A operands;
+//   * keys arrive in 32-key stages: coalesced 16-byte global loads into
+//     registers (two stages in flight), then a swizzled write into a
+//     wave-private LDS tile and MFMA-layout reads out of it (the transpose a
+//     row-major key cache needs; the XOR swizzle keeps both sides free of LDS
+//     bank conflicts);
+//   * FP8 keys are dequantised on the way into LDS (e4m3 x 2^(e8m0-127) is
+//     exact in bf16), so the MFMA path is the same for both cache formats;
+//   * the ReLU and head-weighted sum run on the accumulators, and the two wave
+//     halves combine with one cross-half swap.
+// Exactness: integer-valued bf16 inputs with power-of-two weights make every
+// partial sum a multiple of 1/8 below 2^24 in magnitude, so fp32 is exact in
+// any summation order.
+#include "dsa_device.h"
+#include "dsa_launch.h"
+
+namespace dsa {
+namespace {
+
+constexpr int kSub = 32;      // keys per stage == MFMA N
+constexpr int kWavesPerWG = 4;
+
+template <int DI>
+struct KeyLayout {
+  static constexpr int kChunks = DI * 2 / 16;            // 16-B bf16 chunks/row
+  static constexpr int kRowBytes = DI * 2;                // bf16 row in LDS
+  static constexpr int kTileBytes = kSub * kRowBytes;     // one stage in LDS
+  static constexpr int kLoadsBf16 = kTileBytes / (16 * kWave);
+  static constexpr int kCodeChunks = DI / 16;             // 16-B fp8 chunks/row
+  static constexpr int kLoadsFp8 = kSub * DI / (16 * kWave);
+  static constexpr int kSteps = DI / 16;                  // MFMA k-steps
+  // slot of chunk c of row n (bank-conflict-free writes and reads)
+  __device__ static __forceinline__ int slot(int n, int c) {
+    return c ^ (kChunks == 16 ? (n & 15) : ((n >> 1) & 7));
+  }
+};
+
+// Registers holding one 32-key stage on its way from HBM to LDS.
+template <int DI, bool FP8>
+struct Stage {
+  static constexpr int N = FP8 ? KeyLayout<DI>::kLoadsFp8
+                               : KeyLayout<DI>::kLoadsBf16;
+  uint4 v[N];
+  uint32_t sc[FP8 ? N : 1];
+};
+
+template <int DI, bool FP8>
+__device__ __forceinline__ void stage_load(Stage<DI, FP8>& st,
+                                           const CacheView& kc, int b,
+                                           int kbase, int lane) {
+  using KL = KeyLayout<DI>;
+  // the 32 keys of a stage share one page (stages are 32-aligned, pages 64)
+  int64_t row0;
+  bool clamp = false;
+  if (kc.page_table != nullptr) {
+    row0 = cache_row(kc.page_table, kc.max_pages, kc.L, b, kbase);
+  } else {
+    row0 = (int64_t)b * kc.L + kbase;
+    clamp = kbase + kSub > kc.L;
+  }
+#pragma unroll
+  for (int i = 0; i < Stage<DI, FP8>::N; ++i) {
+    const int id = i * kWave + lane;
+    if constexpr (!FP8) {
+      const int n = id / KL::kChunks, c = id % KL::kChunks;
+      int64_t row = row0 + n;
+      if (clamp) row = (int64_t)b * kc.L + min(kbase + n, kc.L - 1);
+      st.v[i] = ld16(kc.data + row * (DI * 2) + c * 16);
+    } else {
+      const int n = id / KL::kCodeChunks, c = id % KL::kCodeChunks;
+      int64_t row = row0 + n;
+      if (clamp) row = (int64_t)b * kc.L + min(kbase + n, kc.L - 1);
+      st.v[i] = ld16(kc.data + row * DI + c * 16);
+      st.sc[i] = kc.scale[row * (DI / 32) + (c >> 1)];
+    }
+  }
+}
+
+template <int DI, bool FP8>
+__device__ __forceinline__ void stage_store(const Stage<DI, FP8>& st,
+                                            uint4* tile, int lane) {
+  using KL = KeyLayout<DI>;
+#pragma unroll
+  for (int i = 0; i < Stage<DI, FP8>::N; ++i) {
+    const int id = i * kWave + lane;
+    if constexpr (!FP8) {
+      const int n = id / KL::kChunks, c = id % KL::kChunks;
+      tile[n * KL::kChunks + KL::slot(n, c)] = st.v[i];
+    } else {
+      const int n = id / KL::kCodeChunks, c = id % KL::kCodeChunks;
+      const uint4 lo = dequant8_e4m3(make_uint2(st.v[i].x, st.v[i].y), st.sc[i]);
+      const uint4 hi = dequant8_e4m3(make_uint2(st.v[i].z, st.v[i].w), st.sc[i]);
+      tile[n * KL::kChunks + KL::slot(n, 2 * c)] = lo;
+      tile[n * KL::kChunks + KL::slot(n, 2 * c + 1)] = hi;
+    }
+  }
+}
+
+// Scores of 32 keys (one LDS tile) for one query held in `a` (A operands)
+// with head weights `wv` in accumulator layout.  Returns, in every lane, the
+// score of key (lane % 32) of the tile.
+template <int DI, int MB>
+__device__ __forceinline__ float tile_scores(const uint4* tile,
+                                             const uint4 (&a)[MB][DI / 16],
+                                             const float (&wv)[MB][16],
+                                             int lane) {
+  using KL = KeyLayout<DI>;
+  const int n = lane & 31, h = lane >> 5;
+  f32x16 acc[MB];
+#pragma unroll
+  for (int m = 0; m < MB; ++m) acc[m] = f32x16{};
+#pragma unroll
+  for (int ks = 0; ks < KL::kSteps; ++ks) {
+    const uint4 bop = tile[n * KL::kChunks + KL::slot(n, 2 * ks + h)];
+#pragma unroll
+    for (int m = 0; m < MB; ++m) acc[m] = mfma32(a[m][ks], bop, acc[m]);
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int m = 0; m < MB; ++m)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s += wv[m][r] * fmaxf(acc[m][r], 0.f);
+  return s + swap_halves(s);
+}
+
+// Loads one query's indexer vectors as MFMA A operands and its head weights
+// in accumulator-row layout (heads >= H_I contribute zero).
+template <int DI, int MB>
+__device__ __forceinline__ void load_query(const uint16_t* q_idx,
+                                           const float* w, int H_I, int lane,
+                                           uint4 (&a)[MB][DI / 16],
+                                           float (&wv)[MB][16]) {
+  const int m32 = lane & 31, h = lane >> 5;
+#pragma unroll
+  for (int m = 0; m < MB; ++m) {
+    const int head = m * 32 + m32;
+#pragma unroll
+    for (int ks = 0; ks < DI / 16; ++ks)
+      a[m][ks] = head < H_I ? ld16(q_idx + head * DI + ks * 16 + h * 8)
+                            : make_uint4(0, 0, 0, 0);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int hr = m * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+      wv[m][r] = hr < H_I ? w[hr] : 0.f;
+    }
+  }
+}
+
+// Streaming indexer: grid (chunks, T, B); each wave scores `kpw`
+// consecutive positions of one query.
+template <int DI, int MB, bool FP8>
+__global__ __launch_bounds__(256, 2) void indexer_stream_kernel(
+    IndexerLaunch p, int kpw) {
+  using KL = KeyLayout<DI>;
+  __shared__ uint4 lds[kWavesPerWG][KL::kTileBytes / 16];
+  const int lane = lane_id();
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int b = blockIdx.z, t = blockIdx.y;
+  const int k0 = (blockIdx.x * kWavesPerWG + wave) * kpw;
+  if (k0 >= p.row_len) return;
+  const int k1 = min(k0 + kpw, p.row_len);
+  const int qpos = __builtin_amdgcn_readfirstlane(query_pos(p.qp, b, t));
+  float* srow = p.scores + ((int64_t)b * p.T + t) * p.row_len;
+
+  // positions past the query are masked
+  for (int s = max(k0, qpos + 1) + lane; s < k1; s += kWave)
+    srow[s] = -__builtin_inff();
+  const int kend = min(k1, qpos + 1);
+  if (kend <= k0) return;
+  const int nsub = (kend - k0 + kSub - 1) / kSub;
+
+  uint4 a[MB][DI / 16];
+  float wv[MB][16];
+  const int64_t qrow = (int64_t)b * p.T + t;
+  load_query<DI, MB>(p.q_idx + qrow * p.H_I * DI, p.w + qrow * p.H_I, p.H_I,
+                     lane, a, wv);
+
+  uint4* tile = lds[wave];
+  Stage<DI, FP8> s0, s1;
+  stage_load<DI, FP8>(s0, p.keys, b, k0, lane);
+  if (nsub > 1) stage_load<DI, FP8>(s1, p.keys, b, k0 + kSub, lane);
+  for (int i = 0; i < nsub; i += 2) {
+    stage_store<DI, FP8>(s0, tile, lane);
+    if (i + 2 < nsub) stage_load<DI, FP8>(s0, p.keys, b, k0 + (i + 2) * kSub, lane);
+    {
+      const float sc = tile_scores<DI, MB>(tile, a, wv, lane);
+      const int s = k0 + i * kSub + (lane & 31);
+      if (lane < 32 && s < kend) srow[s] = sc + 0.0f;
+    }
+    if (i + 1 < nsub) {
+      stage_store<DI, FP8>(s1, tile, lane);
+      if (i + 3 < nsub)
+        stage_load<DI, FP8>(s1, p.keys, b, k0 + (i + 3) * kSub, lane);
+      const float sc = tile_scores<DI, MB>(tile, a, wv, lane);
+      const int s = k0 + (i + 1) * kSub + (lane & 31);
+      if (lane < 32 && s < kend) srow[s] = sc + 0.0f;
+    }
+  }
+}
+
+template <int DI, int MB, bool FP8>
+hipError_t launch_stream(const IndexerLaunch& p, hipStream_t stream) {
+  // about 8 resident waves per CU on 256 CUs
+  const int64_t total = (int64_t)p.B * p.T * p.row_len;
+  int64_t kpw = (total + 2047) / 2048;
+  kpw = (kpw + kSub - 1) / kSub * kSub;
+  kpw = kpw < 64 ? 64 : (kpw > 4096 ? 4096 : kpw);
+  const int per_wg = (int)kpw * kWavesPerWG;
+  dim3 grid((p.row_len + per_wg - 1) / per_wg, p.T, p.B);
+  hipLaunchKernelGGL((indexer_stream_kernel<DI, MB, FP8>), grid, dim3(256), 0,
+                     stream, p, (int)kpw);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_indexer(const IndexerLaunch& p, hipStream_t stream) {
+  const bool mb1 = p.H_I <= 32;
+  if (p.d_I == 128) {
+    if (p.keys.fp8)
+      return mb1 ? launch_stream<128, 1, true>(p, stream)
+                 : launch_stream<128, 2, true>(p, stream);
+    return mb1 ? launch_stream<128, 1, false>(p, stream)
+               : launch_stream<128, 2, false>(p, stream);
+  }
+  if (p.keys.fp8)
+    return mb1 ? launch_stream<64, 1, true>(p, stream)
+               : launch_stream<64, 2, true>(p, stream);
+  return mb1 ? launch_stream<64, 1, false>(p, stream)
+             : launch_stream<64, 2, false>(p, stream);
+}
+
+}  // namespace dsa

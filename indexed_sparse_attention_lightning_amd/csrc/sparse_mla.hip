@@ -1,0 +1,496 @@
+// Sparse absorbed-MLA attention over the Top-K selected latent rows (gfx950).
+//
+// Sparse Flash Attention reads only the KV-cache entries at the indices the
+// indexer selected (page "Inference Optimization for New Open-Source LLM
+// Architectures", "Architectural Overview"; page "Day-0 Inference
+// Optimization for a New Sparse Attention Architecture: A Technical Deep
+// Dive", section 1).  With MLA absorbed, every query head attends over the
+// same 576-wide latent rows (512 latent + 64 rope) as keys and over their
+// first 512 features as values.
+//
+// One workgroup = one query token x one split of its selected rows; four
+// waves, wave w owns heads 32w..32w+31.  Per 32-row tile:
+//   * gather: direct-to-LDS 16-byte loads, three tiles in flight, the global
+//     address of each lane chosen so that the LDS tile lands XOR-swizzled
+//     (conflict-free for both read patterns below); FP8 rows land as codes
+//     and are dequantised once into a bf16 tile;
+//   * S^T = KV_tile . Q^T on the matrix cores (rows = M, heads = N, the 576
+//     features = K), Q held as B operands: 27 of its 36 k-steps in
+//     registers, the last 9 in LDS (registers are the scarce resource: O
+//     takes all 256 accumulation registers);
+//   * softmax in the log2 domain against a per-head reference fixed at the
+//     first valid tile (its max + 64), so O is never rescaled;
+//   * O^T += V^T . P^T: P comes straight from the S^T accumulators (its
+//     accumulator layout already is a valid B operand after a k-slot
+//     permutation), V^T is read with the transposing LDS read
+//     (ds_read_b64_tr_b16) using the same row permutation;
+//   * O (128 x 512 fp32 per token) lives in the accumulation registers.
+// Splits write (m, l, O) partials that a combine kernel merges by LSE.
+#include "dsa_device.h"
+#include "dsa_launch.h"
+
+namespace dsa {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kRowsT = 32;                      // rows per tile
+constexpr int kSlotsRow = kLatent * 2 / 16;     // 72 bf16 chunks per row
+constexpr int kTileSlots = kRowsT * kSlotsRow;  // 2304
+constexpr int kCodeSlotsRow = kLatent / 16;     // 36 fp8 chunks per row
+constexpr int kCodeTileSlots = kRowsT * kCodeSlotsRow;  // 1152
+constexpr int kCodeSegs = 20;                   // 18 real 64-lane segments + 2
+constexpr int kStageSlots = kCodeSegs * kWave;  // 1280
+constexpr int kMaxSplitRows = 2048;
+constexpr int kQRegSteps = 27;                  // Q k-steps kept in registers
+constexpr int kQLdsSteps = kLatent / 16 - kQRegSteps;   // 9 in LDS
+constexpr int kQLdsStride = 2 * kQLdsSteps + 1; // uint4 per head (padded)
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kRef = 64.0f;     // log2 headroom of the fixed softmax reference
+constexpr float kRange = 96.0f;   // largest logit excess (log2) handled exactly
+
+// chunk c of tile row R sits at slot R*72 + (c ^ swz(R)); swz < 8 keeps a
+// chunk inside its aligned group of 8, and 72 = 9 * 8.
+__device__ __forceinline__ int kv_swz(int R) {
+  return (((R >> 1) & 1) << 2) | ((R >> 2) & 3);
+}
+__device__ __forceinline__ int kv_slot(int R, int c) {
+  return R * kSlotsRow + (c ^ kv_swz(R));
+}
+
+__device__ __forceinline__ void wait_vm(int n) {
+  // s_waitcnt vmcnt(n) for the few counts this kernel needs
+  switch (n) {
+    case 0: __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8)); break;
+    case 9: __builtin_amdgcn_s_waitcnt(9 | (7 << 4) | (15 << 8)); break;
+    case 10: __builtin_amdgcn_s_waitcnt(10 | (7 << 4) | (15 << 8)); break;
+    case 18: __builtin_amdgcn_s_waitcnt(2 | (1 << 14) | (7 << 4) | (15 << 8)); break;
+    case 20: __builtin_amdgcn_s_waitcnt(4 | (1 << 14) | (7 << 4) | (15 << 8)); break;
+    default: __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8)); break;
+  }
+}
+// Workgroup barrier without the memory fence __syncthreads() implies (that
+// fence would wait for every in-flight direct-to-LDS load).  `lds` also
+// waits for this wave's own LDS writes first.
+__device__ __forceinline__ void barrier(bool lds) {
+  asm volatile("" ::: "memory");
+  if (lds) __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// The lane id behind an empty asm: values derived from it are recomputed
+// where used instead of being hoisted into long-lived registers.
+__device__ __forceinline__ int opaque(int x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
+struct Split {
+  int token, b, r0, r1, ntiles;
+  const int32_t* rows;   // LDS: physical row per split row, ~row if invalid
+};
+
+// Issue the direct-to-LDS loads of tile j (bf16 rows straight into a tile).
+__device__ __forceinline__ void issue_bf16(const AttnLaunch& p, const Split& s,
+                                           int j, uint4* dst, int wave) {
+  const int lane = opaque(lane_id());
+#pragma unroll
+  for (int k = 0; k < kTileSlots / kThreads; ++k) {
+    const int seg = k * 4 + wave;
+    const int q = seg * kWave + lane;
+    const int R = q / kSlotsRow, pch = q % kSlotsRow;
+    const int c = pch ^ kv_swz(R);
+    int ent = s.rows[j * kRowsT + R];
+    ent = ent >= 0 ? ent : ~ent;
+    const uint8_t* g = p.kv.data + ((uint64_t)(uint32_t)ent * (kLatent * 2) + c * 16);
+    __builtin_amdgcn_global_load_lds(g, dst + seg * kWave, 16, 0, 0);
+  }
+}
+
+// FP8: codes (linear, 36 chunks per row) by DMA, the scale code each of this
+// thread's conversion slots needs into registers.
+__device__ __forceinline__ void issue_fp8(const AttnLaunch& p, const Split& s,
+                                          int j, uint4* dst, uint32_t (&sc)[5],
+                                          int wave) {
+  const int lane = opaque(lane_id());
+  const int tid = wave * kWave + lane;
+#pragma unroll
+  for (int k = 0; k < kCodeSegs / 4; ++k) {
+    const int seg = k * 4 + wave;
+    const int q = min(seg * kWave + lane, kCodeTileSlots - 1);
+    const int R = q / kCodeSlotsRow, c = q % kCodeSlotsRow;
+    int ent = s.rows[j * kRowsT + R];
+    ent = ent >= 0 ? ent : ~ent;
+    const uint8_t* g = p.kv.data + (int64_t)ent * kLatent + c * 16;
+    __builtin_amdgcn_global_load_lds(g, dst + seg * kWave, 16, 0, 0);
+  }
+#pragma unroll
+  for (int k = 0; k < 5; ++k) {
+    const int q = min(tid + k * kThreads, kCodeTileSlots - 1);
+    const int R = q / kCodeSlotsRow, c = q % kCodeSlotsRow;
+    int ent = s.rows[j * kRowsT + R];
+    ent = ent >= 0 ? ent : ~ent;
+    sc[k] = p.kv.scale[(int64_t)ent * (kLatent / 32) + (c >> 1)];
+  }
+}
+
+// FP8 staging -> bf16 swizzled tile (exact: e4m3 * 2^k fits bf16).
+__device__ __forceinline__ void convert_fp8(const uint4* stg, uint4* tile,
+                                            const uint32_t (&sc)[5], int tid) {
+#pragma unroll
+  for (int k = 0; k < 5; ++k) {
+    const int q = tid + k * kThreads;
+    if (q < kCodeTileSlots) {
+      const int R = q / kCodeSlotsRow, c = q % kCodeSlotsRow;
+      const uint4 v = stg[q];
+      tile[kv_slot(R, 2 * c)] = dequant8_e4m3(make_uint2(v.x, v.y), sc[k]);
+      tile[kv_slot(R, 2 * c + 1)] = dequant8_e4m3(make_uint2(v.z, v.w), sc[k]);
+    }
+  }
+}
+
+struct HeadState {
+  uint4 qb[kQRegSteps];     // B operands: this lane's head, 8 features/k-step
+  f32x16 o[kValue / 32];    // O^T accumulators, 16 dv tiles of 32
+  float m, l;               // softmax reference (log2 units) and partial sum
+  bool bad;                 // a logit exceeded the representable range
+};
+
+__device__ __forceinline__ s16x4 lds_tr16(const char* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (s16x4 __attribute__((address_space(3)))*)(
+          (__attribute__((address_space(3))) char*)(p)));
+}
+
+// S^T accumulation in VGPRs.  The O accumulator fills all 256 AGPRs, so the
+// S^T chain uses the VGPR form of the 32x32x16 bf16 MFMA, issued directly:
+// the first starts from a zero accumulator, the chained ones accumulate into
+// exactly the same registers (back-to-back dependent accumulation, which the
+// hardware forwards), and the last is followed by enough wait states before
+// any VALU instruction reads the result.
+__device__ __forceinline__ void mfma32_vgpr_first(f32x16& c, const uint4& a,
+                                                  const uint4& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0"
+               : "=v"(c)
+               : "v"(__builtin_bit_cast(bf16x8, a)),
+                 "v"(__builtin_bit_cast(bf16x8, b)));
+}
+__device__ __forceinline__ void mfma32_vgpr(f32x16& c, const uint4& a,
+                                            const uint4& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0"
+               : "+v"(c)
+               : "v"(__builtin_bit_cast(bf16x8, a)),
+                 "v"(__builtin_bit_cast(bf16x8, b)));
+}
+__device__ __forceinline__ void mfma32_vgpr_last(f32x16& c, const uint4& a,
+                                                 const uint4& b) {
+  asm volatile(
+      "v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0\n\t"
+      "s_nop 7\n\ts_nop 7\n\ts_nop 7"
+      : "+v"(c)
+      : "v"(__builtin_bit_cast(bf16x8, a)), "v"(__builtin_bit_cast(bf16x8, b)));
+}
+
+// One 32-row tile for this wave's 32 heads.  `vmask` bit R says whether tile
+// row R is a real selected row.
+__device__ __forceinline__ void compute_tile(const uint4* tile,
+                                             const uint4* qrow, uint32_t vmask,
+                                             HeadState& st, float sl2,
+                                             int lane) {
+  const int n = lane & 31, h = lane >> 5;
+  const char* tb = reinterpret_cast<const char*>(tile);
+  // ---- S^T = KV . Q^T.  Chunk 2ks+h of row n; for ks = 4u + v the slot is
+  // 8u + ((2v + h) ^ swz(n)), so four base addresses plus 128-byte steps.
+  f32x16 acc;
+  {
+    const int sw = kv_swz(n);
+    const char* base[4];
+#pragma unroll
+    for (int v = 0; v < 4; ++v)
+      base[v] = tb + (n * kSlotsRow + ((2 * v + h) ^ sw)) * 16;
+#pragma unroll
+    for (int ks = 0; ks < kLatent / 16; ++ks) {
+      const uint4 a = *reinterpret_cast<const uint4*>(base[ks & 3] + 128 * (ks >> 2));
+      const uint4 b = ks < kQRegSteps ? st.qb[ks < kQRegSteps ? ks : 0]
+                                      : qrow[(ks - kQRegSteps) * 2];
+      if (ks == 0)
+        mfma32_vgpr_first(acc, a, b);
+      else if (ks + 1 < kLatent / 16)
+        mfma32_vgpr(acc, a, b);
+      else
+        mfma32_vgpr_last(acc, a, b);
+    }
+  }
+  // ---- online softmax (lane: head n, rows 8(r/4) + 4h + r%4 of the tile)
+  float tmax = -__builtin_inff();
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int R = 8 * (r >> 2) + 4 * h + (r & 3);
+    acc[r] = ((vmask >> R) & 1u) ? acc[r] * sl2 : -__builtin_inff();
+    tmax = fmaxf(tmax, acc[r]);
+  }
+  tmax = fmaxf(tmax, swap_halves(tmax));
+  // The reference max is fixed once per head, at the first tile with a valid
+  // row, 2^64 above that tile's max: later rows stay representable (p <= 2^32
+  // for logits up to 96 above it) and O never needs rescaling.  A logit
+  // beyond that range marks the head as out of range (its LSE becomes NaN).
+  if (st.m == -__builtin_inff() && tmax != -__builtin_inff()) st.m = tmax + kRef;
+  if (tmax > st.m + kRange) st.bad = true;
+  const bool live = st.m != -__builtin_inff();
+  uint4 pb[2];
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk) {
+    float p[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      p[e] = live ? exp2f(acc[8 * kk + e] - st.m) : 0.f;
+      st.l += p[e];
+    }
+    pb[kk] = make_uint4(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
+                        pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7]));
+  }
+  // ---- O^T += V^T . P^T with transposing LDS reads.  Lane (G = lane/16,
+  // i = lane%16) supplies the address of row Ra = 16kk + 4h + i/4 (Rb = Ra+8
+  // for k-slots 4..7) at features 32t + f0, f0 = 16(G&1) + 4(i&3).  Chunk
+  // 4t + c0 of a row sits at slot 4(t ^ s2) + (c0 ^ s01) with s2, s01 the
+  // row's swizzle bits, which gives two bases (even/odd t) per row parity.
+  {
+    const int G = lane >> 4, i = lane & 15;
+    const int f0 = 16 * (G & 1) + 4 * (i & 3);
+    const int c0 = f0 >> 3, e0 = (f0 & 7) * 2;
+    const int Ra = 4 * h + (i >> 2), Rb = Ra + 8;
+    const int swa = kv_swz(Ra), swb = kv_swz(Rb);
+    const int s2 = (swa >> 2) * 64;          // same for Ra and Rb
+    const char* pa = tb + Ra * (kSlotsRow * 16) + (c0 ^ (swa & 3)) * 16 + e0;
+    const char* pbp = tb + Rb * (kSlotsRow * 16) + (c0 ^ (swb & 3)) * 16 + e0;
+    const char* pa_e = pa + s2;
+    const char* pa_o = pa - s2;
+    const char* pb_e = pbp + s2;
+    const char* pb_o = pbp - s2;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+#pragma unroll
+      for (int t = 0; t < kValue / 32; ++t) {
+        const int off = kk * 16 * kSlotsRow * 16 + 64 * t;
+        const uint2 ua = __builtin_bit_cast(uint2, lds_tr16(((t & 1) ? pa_o : pa_e) + off));
+        const uint2 ub = __builtin_bit_cast(uint2, lds_tr16(((t & 1) ? pb_o : pb_e) + off));
+        st.o[t] = mfma32(make_uint4(ua.x, ua.y, ub.x, ub.y), pb[kk], st.o[t]);
+      }
+    }
+  }
+}
+
+template <bool FP8>
+__global__ __launch_bounds__(kThreads, 1) void sparse_mla_kernel(
+    AttnLaunch p, int rows_per_split) {
+  constexpr int kBufSlots = FP8 ? kStageSlots : kTileSlots;
+  __shared__ uint4 buf0[kBufSlots];
+  __shared__ uint4 buf1[kBufSlots];
+  __shared__ uint4 buf2[kBufSlots];
+  __shared__ uint4 ftile[FP8 ? kTileSlots : 1];
+  __shared__ int32_t rows[kMaxSplitRows];
+  __shared__ uint4 qlds[128 * kQLdsStride];
+
+  const int tid = threadIdx.x, lane = lane_id();
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  Split s;
+  s.token = blockIdx.y;
+  s.b = s.token / p.T;
+  s.r0 = blockIdx.x * rows_per_split;
+  s.r1 = min(s.r0 + rows_per_split, p.K);
+  s.ntiles = (s.r1 - s.r0 + kRowsT - 1) / kRowsT;
+  s.rows = rows;
+  const int32_t* idx = p.idx + (int64_t)s.token * p.K;
+
+  // physical rows of this split; entries that are -1 or out of range hold
+  // ~(row of position 0), a valid and finite row, so that their loads stay in
+  // bounds (their logits are masked)
+  const int nvalid = p.seq_lens ? p.seq_lens[s.b] : p.kv.L;
+  const int dummy = nvalid > 0 ? (int)cache_row(p.kv.page_table,
+                                                p.kv.max_pages, p.kv.L, s.b, 0)
+                                 : 0;
+  for (int i = tid; i < s.ntiles * kRowsT; i += kThreads) {
+    const int r = s.r0 + i;
+    const int pos = r < s.r1 ? idx[r] : -1;
+    rows[i] = (pos >= 0 && pos < nvalid)
+                  ? (int)cache_row(p.kv.page_table, p.kv.max_pages, p.kv.L,
+                                   s.b, pos)
+                  : ~dummy;
+  }
+  barrier(true);
+
+  const int n = lane & 31, h = lane >> 5;
+  const int head = wave * 32 + n;
+  const bool active = wave * 32 < p.H;   // wave-uniform
+  HeadState st;
+  st.m = -__builtin_inff();
+  st.l = 0.f;
+  st.bad = false;
+#pragma unroll
+  for (int t = 0; t < kValue / 32; ++t) st.o[t] = f32x16{};
+  {
+    const uint16_t* qh = p.q + ((int64_t)s.token * p.H + min(head, p.H - 1)) * kLatent;
+    const uint32_t keep = head < p.H ? 0xffffffffu : 0u;
+#pragma unroll
+    for (int ks = 0; ks < kQRegSteps; ++ks) {
+      const uint4 v = ld16(qh + ks * 16 + h * 8);
+      st.qb[ks] = make_uint4(v.x & keep, v.y & keep, v.z & keep, v.w & keep);
+    }
+    // the last k-steps of every head of this token into LDS
+    for (int i = tid; i < 128 * 2 * kQLdsSteps; i += kThreads) {
+      const int hd = i / (2 * kQLdsSteps), r = i % (2 * kQLdsSteps);
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (hd < p.H)
+        v = ld16(p.q + ((int64_t)s.token * p.H + hd) * kLatent +
+                 (kQRegSteps + (r >> 1)) * 16 + (r & 1) * 8);
+      qlds[hd * kQLdsStride + r] = v;
+    }
+  }
+  barrier(true);
+  const uint4* qrow = qlds + (wave * 32 + n) * kQLdsStride + h;
+  const float sl2 = p.scale * kLog2e;
+
+  if (s.ntiles > 0) {
+    uint32_t sc0[5], sc1[5], sc2[5];
+    constexpr int per_tile = FP8 ? 10 : 9;
+    auto issue = [&](int j, uint4* dst, uint32_t (&sc)[5]) {
+      if constexpr (FP8) issue_fp8(p, s, j, dst, sc, wave);
+      else issue_bf16(p, s, j, dst, wave);
+    };
+    auto step = [&](int j, uint4* cur, uint4* nxt, uint32_t (&scc)[5],
+                    uint32_t (&scn)[5]) {
+      if (j + 2 < s.ntiles) issue(j + 2, nxt, scn);
+      wait_vm(per_tile * (min(s.ntiles - 1, j + 2) - j));
+      barrier(false);
+      const uint4* tile = cur;
+      if constexpr (FP8) {
+        convert_fp8(cur, ftile, scc, tid);
+        barrier(true);
+        tile = ftile;
+      }
+      if (active) {
+        const uint32_t vmask = (uint32_t)__builtin_amdgcn_ballot_w64(
+            s.rows[j * kRowsT + (lane & 31)] >= 0);
+        compute_tile(tile, qrow, vmask, st, sl2, lane);
+      }
+      barrier(false);
+    };
+    issue(0, buf0, sc0);
+    if (s.ntiles > 1) issue(1, buf1, sc1);
+    for (int j = 0; j < s.ntiles; j += 3) {
+      step(j, buf0, buf2, sc0, sc2);
+      if (j + 1 < s.ntiles) step(j + 1, buf1, buf0, sc1, sc0);
+      if (j + 2 < s.ntiles) step(j + 2, buf2, buf1, sc2, sc1);
+    }
+  }
+  if (!active || head >= p.H) return;
+
+  const float ltot = st.l + swap_halves(st.l);
+  const int dvb = 4 * h;   // first of this lane's 4 consecutive dv per group
+  if (gridDim.x == 1) {
+    const float inv = ltot > 0.f ? 1.0f / ltot : 0.f;
+    float* o = p.out + ((int64_t)s.token * p.H + head) * kValue;
+#pragma unroll
+    for (int t = 0; t < kValue / 32; ++t)
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        *reinterpret_cast<float4*>(o + 32 * t + 8 * g + dvb) =
+            make_float4(st.o[t][4 * g] * inv, st.o[t][4 * g + 1] * inv,
+                        st.o[t][4 * g + 2] * inv, st.o[t][4 * g + 3] * inv);
+    if (h == 0)
+      p.lse[(int64_t)s.token * p.H + head] =
+          st.bad ? __builtin_nanf("")
+                 : (ltot > 0.f ? (st.m + __builtin_log2f(ltot)) * kLn2
+                               : -__builtin_inff());
+  } else {
+    const int64_t slot = ((int64_t)s.token * gridDim.x + blockIdx.x) * p.H + head;
+    float* o = p.partial + slot * (kValue + 2);
+#pragma unroll
+    for (int t = 0; t < kValue / 32; ++t)
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        *reinterpret_cast<float4*>(o + 32 * t + 8 * g + dvb) =
+            make_float4(st.o[t][4 * g], st.o[t][4 * g + 1], st.o[t][4 * g + 2],
+                        st.o[t][4 * g + 3]);
+    if (h == 0) {
+      o[kValue] = st.bad ? __builtin_nanf("") : (ltot > 0.f ? st.m : -__builtin_inff());
+      o[kValue + 1] = ltot;
+    }
+  }
+}
+
+// Merge split partials (m in log2 units, l, unnormalised O) by LSE.
+__global__ __launch_bounds__(128) void combine_kernel(AttnLaunch p,
+                                                      int splits) {
+  const int token = blockIdx.x, head = blockIdx.y;
+  const int dv = threadIdx.x * 4;
+  const float* base =
+      p.partial + ((int64_t)token * splits * p.H + head) * (kValue + 2);
+  const int64_t sstride = (int64_t)p.H * (kValue + 2);
+  float M = -__builtin_inff();
+  for (int sp = 0; sp < splits; ++sp) M = fmaxf(M, base[sp * sstride + kValue]);
+  float wsum = 0.f;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (M != -__builtin_inff()) {
+    for (int sp = 0; sp < splits; ++sp) {
+      const float* o = base + sp * sstride;
+      const float m = o[kValue];
+      if (m == -__builtin_inff()) continue;
+      const float f = exp2f(m - M);
+      wsum += f * o[kValue + 1];
+      const float4 v = *reinterpret_cast<const float4*>(o + dv);
+      acc.x += f * v.x;
+      acc.y += f * v.y;
+      acc.z += f * v.z;
+      acc.w += f * v.w;
+    }
+  }
+  const float inv = wsum > 0.f ? 1.0f / wsum : 0.f;
+  *reinterpret_cast<float4*>(p.out + ((int64_t)token * p.H + head) * kValue +
+                             dv) =
+      make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+  if (threadIdx.x == 0)
+    p.lse[(int64_t)token * p.H + head] =
+        wsum > 0.f ? (M + __builtin_log2f(wsum)) * kLn2 : -__builtin_inff();
+}
+
+}  // namespace
+
+int attn_splits(int tokens, int K) {
+  const int tiles = (K + kRowsT - 1) / kRowsT;
+  int s = (256 + tokens - 1) / tokens;
+  s = s < 1 ? 1 : s;
+  s = s > 16 ? 16 : s;
+  s = s > tiles ? tiles : s;
+  return s;
+}
+
+size_t attn_workspace_bytes(int tokens, int H, int K) {
+  const int s = attn_splits(tokens, K);
+  if (s <= 1) return 0;
+  return (size_t)tokens * s * H * (kValue + 2) * sizeof(float);
+}
+
+hipError_t launch_sparse_mla(const AttnLaunch& p, hipStream_t stream) {
+  const int tokens = p.B * p.T;
+  const int splits = p.splits;
+  // rows per split: whole tiles
+  int rps = (p.K + splits - 1) / splits;
+  rps = (rps + kRowsT - 1) / kRowsT * kRowsT;
+  const int used = (p.K + rps - 1) / rps;   // splits that own rows
+  dim3 grid(used, tokens);
+  if (p.kv.fp8)
+    hipLaunchKernelGGL(sparse_mla_kernel<true>, grid, dim3(kThreads), 0,
+                       stream, p, rps);
+  else
+    hipLaunchKernelGGL(sparse_mla_kernel<false>, grid, dim3(kThreads), 0,
+                       stream, p, rps);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || used == 1) return e;
+  hipLaunchKernelGGL(combine_kernel, dim3(tokens, p.H), dim3(128), 0, stream,
+                     p, used);
+  return hipGetLastError();
+}
+
+}  // namespace dsa

@@ -1,0 +1,166 @@
+"""HIP path vs CPU oracle, through the C ABI (needs an MI355X).
+
+Top-K index sets must match exactly; indexer scores bit-exactly (integer
+inputs make them exact in fp32); attention outputs within
+max|diff| <= 1e-2 * max|oracle| and LSE within 1e-3.
+"""
+import numpy as np
+import pytest
+import torch
+
+import indexed_sparse_attention_lightning_amd as dsa
+import oracle
+import workloads as wk
+from workloads.device import to_device
+
+from gpu_helpers import (assert_attn_close, assert_idx_equal, check_workload,
+                         run_decode_step, run_separate_ops)
+
+pytestmark = pytest.mark.gpu
+
+W = wk.WORKLOADS
+
+
+def test_tiny_workload():
+    """Batch 1, position 511 over L=512, H_I=4, d_I=64, K=64, 16 heads."""
+    check_workload(W["tiny"])
+
+
+# Reduced shapes: several tiles, ragged tails, both cache formats, paging.
+SMALL = {
+    "decode_bf16": wk.scaled(W["decode"], B=3, L=2048, top_k=256, seed=101),
+    "decode_fp8": wk.scaled(W["decode_fp8"], B=3, L=2048, top_k=256, seed=101),
+    "decode_ragged_tail": wk.scaled(W["decode"], B=2, L=1000, top_k=300,
+                                    seed=102),
+    "prefill_chunk": wk.scaled(W["prefill"], T=40, L=1536, first_pos=1400,
+                               top_k=512, H=64, seed=103),
+    "paged_fp8": wk.scaled(W["ragged"], B=3, L_min=100, L_max=3000,
+                           top_k=512, seed=104),
+    "paged_small_heads": wk.scaled(W["ragged"], B=2, L_min=700, L_max=1300,
+                                   top_k=128, H=40, H_I=20, d_I=64, seed=105),
+    "odd_heads_bf16": wk.scaled(W["decode"], B=2, L=1024, top_k=96, H=100,
+                                H_I=48, seed=106),
+}
+
+
+@pytest.mark.parametrize("name", sorted(SMALL))
+def test_small_workloads(name):
+    check_workload(SMALL[name])
+
+
+def test_topk_covers_whole_history_is_dense_attention():
+    """K larger than the history: every position is selected and the
+    attention equals dense attention (the oracle's dense-equivalence pin)."""
+    wl = wk.scaled(W["tiny"], top_k=1024, seed=7)
+    inp, d, ref, (idx, out, lse) = check_workload(wl)
+    assert idx[0, 0, :512].tolist() == list(range(512))
+    assert np.all(idx[0, 0, 512:] == -1)
+
+
+def test_all_zero_queries_tie_break():
+    """q_I = 0 makes every score 0: ties resolve to the lowest positions."""
+    wl = wk.scaled(W["decode"], B=2, L=2048, top_k=256, H=32, seed=8)
+    inp = wk.generate(wl)
+    inp.q_idx[:] = 0
+    d = to_device(inp)
+    idx, out, lse = run_decode_step(inp, d)
+    for b in range(2):
+        assert idx[b, 0].tolist() == list(range(256))
+    ref = oracle.decode_path(inp)
+    assert_attn_close(out, lse, ref, [(0, 0), (1, 0)])
+
+
+def test_short_histories_and_padding():
+    """Queries near the start of the cache: fewer candidates than K."""
+    wl = wk.scaled(W["prefill"], T=6, L=512, first_pos=0, top_k=64, H=32,
+                   seed=9)
+    inp = wk.generate(wl)
+    inp.q_pos[0] = [0, 1, 2, 31, 63, 64]
+    d = to_device(inp)
+    ref = oracle.decode_path(inp, want_scores=True)
+    rows = [(0, t) for t in range(6)]
+    idx, out, lse = run_decode_step(inp, d)
+    assert_idx_equal(idx, ref["idx"], rows)
+    assert_attn_close(out, lse, ref, rows)
+    scores, idx2, out2, lse2 = run_separate_ops(inp, d)
+    assert_idx_equal(idx2, ref["idx"], rows)
+    assert_attn_close(out2, lse2, ref, rows)
+    assert np.all(idx[0, 0, 1:] == -1) and idx[0, 0, 0] == 0
+
+
+def test_invalid_indices_are_skipped():
+    """-1 entries in idx contribute nothing to the attention."""
+    wl = wk.scaled(W["decode"], B=2, L=1024, top_k=128, H=32, seed=10)
+    inp = wk.generate(wl)
+    d = to_device(inp)
+    rng = np.random.default_rng(0)
+    idx = np.full((2, 1, 128), -1, dtype=np.int32)
+    for b in range(2):
+        sel = np.sort(rng.choice(1024, size=50, replace=False))
+        idx[b, 0, rng.choice(128, size=50, replace=False)] = sel
+    out, lse = dsa.sparse_mla_attn(d["q"], d["kv_c"],
+                                   torch.from_numpy(idx).cuda(),
+                                   wl.softmax_scale)
+    torch.cuda.synchronize()
+    out, lse = out.cpu().numpy(), lse.cpu().numpy()
+    for b in range(2):
+        chosen = idx[b, 0][idx[b, 0] >= 0]
+        kv = oracle.cache_rows(inp.kv.data, None, False, inp.page_table[b],
+                               chosen)
+        ro, rl = oracle.sparse_mla_row(oracle.decode_bf16(inp.q[b, 0]), kv,
+                                       wl.softmax_scale)
+        assert np.abs(out[b, 0] - ro).max() <= 1e-2 * np.abs(ro).max()
+        assert np.abs(lse[b, 0] - rl).max() <= 1e-3
+
+
+def test_deterministic():
+    wl = SMALL["paged_fp8"]
+    inp = wk.generate(wl)
+    d = to_device(inp)
+    a = run_decode_step(inp, d)
+    b = run_decode_step(inp, d)
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
+
+
+# ------------------------------------------------------- full-size workloads
+
+def test_full_decode_bf16():
+    """B=32, L=32768, K=2048, 128 heads: every row checked."""
+    check_workload(W["decode"])
+
+
+def test_full_decode_fp8():
+    inp, d, ref, (idx, out, lse) = check_workload(W["decode_fp8"])
+
+
+def test_full_prefill_sampled_rows():
+    """4096 queries at 61440..65535 of a 65536 context; rows sampled."""
+    rows = [(0, t) for t in (0, 1, 777, 2048, 3001, 4094, 4095)]
+    check_workload(W["prefill"], rows=rows, separate=True)
+
+
+def test_full_ragged_paged():
+    check_workload(W["ragged"])
+
+
+def test_contiguous_api_unaligned_length():
+    """Separate entry points over a contiguous cache whose length is not a
+    multiple of the 32-key stage (the last stage is clamped in-bounds)."""
+    wl = wk.scaled(W["decode"], B=2, L=1000, top_k=200, H=64, seed=11)
+    inp = wk.generate(wl)
+    d = to_device(inp)
+    B, L = 2, 1000
+    kidx_c = d["kidx"].view(B, -1, wl.d_I)[:, :L].contiguous()
+    kv_c = d["kv"].view(B, -1, 576)[:, :L].contiguous()
+    ref = oracle.decode_path(inp, want_scores=True)
+    scores = dsa.indexer_scores(d["q_idx"], d["w"], kidx_c, d["q_pos"])
+    idx = dsa.topk(scores, d["q_pos"], wl.top_k)
+    out, lse = dsa.sparse_mla_attn(d["q"], kv_c, idx, wl.softmax_scale)
+    torch.cuda.synchronize()
+    rows = [(0, 0), (1, 0)]
+    sc = scores.cpu().numpy()
+    for b, t in rows:
+        assert np.array_equal(sc[b, t].astype(np.float64), ref["scores"][(b, t)])
+    assert_idx_equal(idx.cpu().numpy(), ref["idx"], rows)
+    assert_attn_close(out.cpu().numpy(), lse.cpu().numpy(), ref, rows)
