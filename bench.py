@@ -1,0 +1,236 @@
+"""Benchmark of the DSA decode step on one MI355X.
+
+One step = indexer -> Top-K -> sparse attention for a batch of 32 decode
+tokens, each over a 32768-token bf16 cache, top_k = 2048, 64 indexer heads of
+width 128 and 128 MLA heads of width 576 (512 + 64), through
+dsa_decode_step on the caller's stream.  Inputs are seeded synthetic tensors
+resident in HBM before the timed region; three input replicas rotate so that
+consecutive steps never find their operands in the 256 MB Infinity Cache.
+
+Prints ONE JSON line: throughput in tokens/s, the step's algorithmic HBM
+bandwidth against the 8 TB/s peak, the roofline of the dominant kernel (the
+indexer stream, timed with HIP events on its own stream), and the CPU oracle
+timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBPS = 8000.0
+METRIC = ("DSA decode tokens/sec at B=32,L=32K,k=2048; achieved HBM GB/s vs "
+          "peak")
+REPLICAS = 3
+
+
+def algorithmic_bytes(wl, L):
+    """Bytes the method must move per decode step (whole batch): every
+    indexer key once, every selected latent row once, the queries, weights,
+    indices and outputs.  The score round-trip between kernels is excluded."""
+    per_tok = (L * wl.d_I * 2                      # indexer keys, bf16
+               + wl.top_k * 576 * 2                # selected latent rows
+               + wl.H_I * wl.d_I * 2 + wl.H_I * 4  # q_I, w
+               + wl.H * 576 * 2                    # q
+               + wl.H * 512 * 4 + wl.H * 4         # out, lse
+               + wl.top_k * 4)                     # indices
+    return wl.B * wl.T * per_tok
+
+
+def indexer_bytes(wl, L):
+    """Algorithmic bytes of one indexer launch: keys + queries + weights."""
+    return wl.B * wl.T * (L * wl.d_I * 2 + wl.H_I * wl.d_I * 2 + wl.H_I * 4)
+
+
+def time_loop(fn, steps, warmup, stream):
+    import torch
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for i in range(steps):
+        fn(i)
+    end.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / steps   # ms per call
+
+
+def traffic_record(kernel_src):
+    """HBM bytes per indexer launch from the committed rocprofv3 counter
+    summary, if it was taken on the current kernel source (else None)."""
+    path = os.path.join(ROOT, "profiles", "indexer_stream_decode_traffic.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    h = hashlib.sha256(open(kernel_src, "rb").read()).hexdigest()
+    if rec.get("kernel_source_sha256") != h:
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(inp, budget_s=12.0):
+    """The CPU oracle, as it stands, on whole decode rows of the same
+    workload until about `budget_s` seconds of work (at least one row)."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        cores = 1
+    rows, t0 = [], time.perf_counter()
+    for b in range(inp.wl.B):
+        oracle.decode_path(inp, rows=[(b, 0)])
+        rows.append(b)
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": len(rows) / dt, "unit": "tokens/s", "cores": cores,
+            "kind": "oracle",
+            "sample": f"{len(rows)} of {inp.wl.B} decode tokens (full "
+                      f"indexer over {inp.L} keys, top-k, attention), "
+                      f"{dt:.1f} s"}
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args(argv)
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: the DSA hot path here is a "
+              "single-GPU kernel set (decode batches shard by sequence with "
+              "no exchange); run with --gpus 1", file=sys.stderr)
+        return 2
+
+    import torch
+    import indexed_sparse_attention_lightning_amd as dsa
+    import workloads as wk
+    from workloads.device import to_device
+
+    wl = wk.WORKLOADS["decode"]
+    inp = wk.generate(wl)
+    L = inp.L
+    reps = [to_device(inp)]
+    for _ in range(REPLICAS - 1):
+        d = {k: (None if v is None else v.clone())
+             for k, v in reps[0].items() if not k.endswith("_c")}
+        d["kidx_c"] = d["kidx"].view(wl.B, L, wl.d_I)
+        d["kv_c"] = d["kv"].view(wl.B, L, 576)
+        reps.append(d)
+    stream = torch.cuda.current_stream()
+    caches = [dsa.PagedCache(kidx=d["kidx"], kv=d["kv"],
+                             page_table=d["page_table"],
+                             seq_lens=d["seq_lens"]) for d in reps]
+    ws = torch.empty(dsa.workspace_size(dsa.OP_DECODE_STEP, wl.B, 1, L, wl.H,
+                                        wl.top_k), dtype=torch.uint8,
+                     device="cuda")
+    outs = [(torch.empty((wl.B, 1, wl.H, 512), device="cuda"),
+             torch.empty((wl.B, 1, wl.H), device="cuda"),
+             torch.empty((wl.B, 1, wl.top_k), dtype=torch.int32,
+                         device="cuda")) for _ in range(REPLICAS)]
+
+    def step(i):
+        r = i % REPLICAS
+        d = reps[r]
+        o, l, ix = outs[r]
+        dsa.decode_step(caches[r], d["q_idx"], d["w"], d["q"], wl.top_k,
+                        wl.softmax_scale, max_seq_len=L, out=o, lse=l,
+                        idx_out=ix, workspace=ws)
+
+    ms = time_loop(step, args.steps, args.warmup, stream)
+
+    # per-kernel timing of the three stages through the separate entry points
+    scores = [torch.empty((wl.B, 1, L), device="cuda") for _ in range(REPLICAS)]
+
+    def ix_call(i):
+        r = i % REPLICAS
+        dsa.indexer_scores(reps[r]["q_idx"], reps[r]["w"], reps[r]["kidx_c"],
+                           reps[r]["q_pos"], out=scores[r])
+
+    ms_idx = time_loop(ix_call, args.steps, args.warmup, stream)
+
+    def tk_call(i):
+        r = i % REPLICAS
+        dsa.topk(scores[r], reps[r]["q_pos"], wl.top_k, out=outs[r][2])
+
+    ms_topk = time_loop(tk_call, args.steps, args.warmup, stream)
+    attn_ws = torch.empty(max(1, dsa.workspace_size(
+        dsa.OP_SPARSE_MLA, wl.B, 1, L, wl.H, wl.top_k)), dtype=torch.uint8,
+        device="cuda")
+
+    def at_call(i):
+        r = i % REPLICAS
+        dsa.sparse_mla_attn(reps[r]["q"], reps[r]["kv_c"], outs[r][2],
+                            wl.softmax_scale, out=outs[r][0], lse=outs[r][1],
+                            workspace=attn_ws)
+
+    ms_attn = time_loop(at_call, args.steps, args.warmup, stream)
+
+    # a plain device copy of a 1 GiB buffer: the practical streaming ceiling
+    a = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+    bcopy = torch.empty_like(a)
+    ms_copy = time_loop(lambda i: bcopy.copy_(a), 10, 3, stream)
+    copy_gbps = 2 * a.numel() * 4 / (ms_copy * 1e-3) / 1e9
+    del a, bcopy
+
+    step_bytes = algorithmic_bytes(wl, L)
+    tok_s = wl.B * wl.T / (ms * 1e-3)
+    step_gbps = step_bytes / (ms * 1e-3) / 1e9
+    ib = indexer_bytes(wl, L)
+    idx_gbps = ib / (ms_idx * 1e-3) / 1e9
+    src = os.path.join(ROOT, "indexed_sparse_attention_lightning_amd", "csrc",
+                       "indexer.hip")
+    line = {
+        "metric": METRIC,
+        "value": round(tok_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "decode_bf16: batch 32, every sequence at 32768 "
+                        "cached tokens, top_k 2048, indexer 64 heads x 128, "
+                        "MLA 128 heads x (512+64), bf16 cache read through "
+                        "an identity page table",
+            "global_batch": wl.B, "seq_len": L, "top_k": wl.top_k,
+            "parallelism": "single GPU"},
+        "step_hbm_gbps": round(step_gbps, 1),
+        "step_frac_of_peak": round(step_gbps / PEAK_HBM_GBPS, 4),
+        "step_algorithmic_bytes": step_bytes,
+        "kernel_ms": {"indexer": round(ms_idx, 5), "topk": round(ms_topk, 5),
+                      "sparse_mla_attn": round(ms_attn, 5)},
+        "copy_gbps_measured": round(copy_gbps, 1),
+        "roofline": {
+            "kernel": "indexer_stream_kernel (dsa_indexer_scores)",
+            "bound": "hbm", "achieved": round(idx_gbps, 1),
+            "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+            "frac": round(idx_gbps / PEAK_HBM_GBPS, 4),
+            "traffic": traffic_record(src),
+            "algorithmic_bytes_per_launch": ib},
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(inp)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

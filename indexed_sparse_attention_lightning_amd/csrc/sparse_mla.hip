@@ -171,22 +171,21 @@ __device__ __forceinline__ s16x4 lds_tr16(const char* p) {
 // any VALU instruction reads the result.
 __device__ __forceinline__ void mfma32_vgpr_first(f32x16& c, const uint4& a,
                                                   const uint4& b) {
-  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0"
+  asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0"
                : "=v"(c)
                : "v"(__builtin_bit_cast(bf16x8, a)),
                  "v"(__builtin_bit_cast(bf16x8, b)));
 }
 __device__ __forceinline__ void mfma32_vgpr(f32x16& c, const uint4& a,
                                             const uint4& b) {
-  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0"
+  asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0"
                : "+v"(c)
                : "v"(__builtin_bit_cast(bf16x8, a)),
                  "v"(__builtin_bit_cast(bf16x8, b)));
 }
 __device__ __forceinline__ void mfma32_vgpr_last(f32x16& c, const uint4& a,
                                                  const uint4& b) {
-  asm volatile(
-      "v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0\n\t"
+  asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0\n\t"
       "s_nop 7\n\ts_nop 7\n\ts_nop 7"
       : "+v"(c)
       : "v"(__builtin_bit_cast(bf16x8, a)), "v"(__builtin_bit_cast(bf16x8, b)));
@@ -205,22 +204,45 @@ __device__ __forceinline__ void compute_tile(const uint4* tile,
   f32x16 acc;
   {
     const int sw = kv_swz(n);
-    const char* base[4];
+    int aoff[4];
 #pragma unroll
     for (int v = 0; v < 4; ++v)
-      base[v] = tb + (n * kSlotsRow + ((2 * v + h) ^ sw)) * 16;
+      aoff[v] = (n * kSlotsRow + ((2 * v + h) ^ sw)) * 16;
+    auto a_at = [&](int ks) {
+      return *reinterpret_cast<const uint4*>(tb + aoff[ks & 3] + 128 * (ks >> 2));
+    };
+    auto b_at = [&](int ks) {
+      return ks < kQRegSteps ? st.qb[ks < kQRegSteps ? ks : 0]
+                             : qrow[(ks - kQRegSteps) * 2];
+    };
+    // two independent accumulation chains (even / odd k-steps) and operands
+    // fetched three k-steps ahead keep the matrix core fed
+    constexpr int kS = kLatent / 16;   // 36 k-steps
+    constexpr int kAhead = 3;
+    uint4 aq[kAhead + 1], bq[kAhead + 1];
 #pragma unroll
-    for (int ks = 0; ks < kLatent / 16; ++ks) {
-      const uint4 a = *reinterpret_cast<const uint4*>(base[ks & 3] + 128 * (ks >> 2));
-      const uint4 b = ks < kQRegSteps ? st.qb[ks < kQRegSteps ? ks : 0]
-                                      : qrow[(ks - kQRegSteps) * 2];
-      if (ks == 0)
-        mfma32_vgpr_first(acc, a, b);
-      else if (ks + 1 < kLatent / 16)
-        mfma32_vgpr(acc, a, b);
-      else
-        mfma32_vgpr_last(acc, a, b);
+    for (int i = 0; i < kAhead; ++i) {
+      aq[i] = a_at(i);
+      bq[i] = b_at(i);
     }
+    f32x16 acc1;
+#pragma unroll
+    for (int ks = 0; ks < kS; ++ks) {
+      if (ks + kAhead < kS) {
+        aq[(ks + kAhead) % (kAhead + 1)] = a_at(ks + kAhead);
+        bq[(ks + kAhead) % (kAhead + 1)] = b_at(ks + kAhead);
+      }
+      const uint4 a = aq[ks % (kAhead + 1)], b = bq[ks % (kAhead + 1)];
+      f32x16& c = (ks & 1) ? acc1 : acc;
+      if (ks < 2)
+        mfma32_vgpr_first(c, a, b);
+      else if (ks + 2 < kS)
+        mfma32_vgpr(c, a, b);
+      else
+        mfma32_vgpr_last(c, a, b);
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[r] += acc1[r];
   }
   // ---- online softmax (lane: head n, rows 8(r/4) + 4h + r%4 of the tile)
   float tmax = -__builtin_inff();
@@ -262,21 +284,29 @@ __device__ __forceinline__ void compute_tile(const uint4* tile,
     const int Ra = 4 * h + (i >> 2), Rb = Ra + 8;
     const int swa = kv_swz(Ra), swb = kv_swz(Rb);
     const int s2 = (swa >> 2) * 64;          // same for Ra and Rb
-    const char* pa = tb + Ra * (kSlotsRow * 16) + (c0 ^ (swa & 3)) * 16 + e0;
-    const char* pbp = tb + Rb * (kSlotsRow * 16) + (c0 ^ (swb & 3)) * 16 + e0;
-    const char* pa_e = pa + s2;
-    const char* pa_o = pa - s2;
-    const char* pb_e = pbp + s2;
-    const char* pb_o = pbp - s2;
+    const int pa = Ra * (kSlotsRow * 16) + (c0 ^ (swa & 3)) * 16 + e0;
+    const int pbo = Rb * (kSlotsRow * 16) + (c0 ^ (swb & 3)) * 16 + e0;
+    const int pa_e = pa + s2, pa_o = pa - s2;
+    const int pb_e = pbo + s2, pb_o = pbo - s2;
+    auto rd = [&](int kk, int t) {
+      const int off = kk * 16 * kSlotsRow * 16 + 64 * t;
+      const uint2 ua = __builtin_bit_cast(uint2, lds_tr16(tb + ((t & 1) ? pa_o : pa_e) + off));
+      const uint2 ub = __builtin_bit_cast(uint2, lds_tr16(tb + ((t & 1) ? pb_o : pb_e) + off));
+      return make_uint4(ua.x, ua.y, ub.x, ub.y);
+    };
+    // V^T operands read three MFMAs ahead
+    constexpr int kN = 2 * (kValue / 32);   // 32 MFMAs
+    constexpr int kAhead = 7;
+    uint4 vq[kAhead + 1];
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
+    for (int i = 0; i < kAhead; ++i) vq[i] = rd(i / (kValue / 32), i % (kValue / 32));
 #pragma unroll
-      for (int t = 0; t < kValue / 32; ++t) {
-        const int off = kk * 16 * kSlotsRow * 16 + 64 * t;
-        const uint2 ua = __builtin_bit_cast(uint2, lds_tr16(((t & 1) ? pa_o : pa_e) + off));
-        const uint2 ub = __builtin_bit_cast(uint2, lds_tr16(((t & 1) ? pb_o : pb_e) + off));
-        st.o[t] = mfma32(make_uint4(ua.x, ua.y, ub.x, ub.y), pb[kk], st.o[t]);
-      }
+    for (int i = 0; i < kN; ++i) {
+      if (i + kAhead < kN)
+        vq[(i + kAhead) % (kAhead + 1)] =
+            rd((i + kAhead) / (kValue / 32), (i + kAhead) % (kValue / 32));
+      const int kk = i / (kValue / 32), t = i % (kValue / 32);
+      st.o[t] = mfma32(vq[i % (kAhead + 1)], pb[kk], st.o[t]);
     }
   }
 }
@@ -310,15 +340,35 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_kernel(
   const int dummy = nvalid > 0 ? (int)cache_row(p.kv.page_table,
                                                 p.kv.max_pages, p.kv.L, s.b, 0)
                                  : 0;
-  for (int i = tid; i < s.ntiles * kRowsT; i += kThreads) {
+  // all index loads of a thread first, then the page-table lookups
+  constexpr int kRowIter = kMaxSplitRows / kThreads;   // 8
+  int pos[kRowIter];
+#pragma unroll
+  for (int u = 0; u < kRowIter; ++u) {
+    const int i = tid + u * kThreads;
     const int r = s.r0 + i;
-    const int pos = r < s.r1 ? idx[r] : -1;
-    rows[i] = (pos >= 0 && pos < nvalid)
-                  ? (int)cache_row(p.kv.page_table, p.kv.max_pages, p.kv.L,
-                                   s.b, pos)
-                  : ~dummy;
+    pos[u] = (i < s.ntiles * kRowsT && r < s.r1) ? idx[r] : -1;
+    if (!(pos[u] >= 0 && pos[u] < nvalid)) pos[u] = -1;
+  }
+#pragma unroll
+  for (int u = 0; u < kRowIter; ++u) {
+    const int i = tid + u * kThreads;
+    if (i < s.ntiles * kRowsT)
+      rows[i] = pos[u] >= 0 ? (int)cache_row(p.kv.page_table, p.kv.max_pages,
+                                              p.kv.L, s.b, pos[u])
+                            : ~dummy;
   }
   barrier(true);
+
+  // the first two tiles are in flight while the queries load
+  uint32_t sc0[5], sc1[5], sc2[5];
+  constexpr int per_tile = FP8 ? 10 : 9;
+  auto issue = [&](int j, uint4* dst, uint32_t (&sc)[5]) {
+    if constexpr (FP8) issue_fp8(p, s, j, dst, sc, wave);
+    else issue_bf16(p, s, j, dst, wave);
+  };
+  issue(0, buf0, sc0);
+  issue(min(1, s.ntiles - 1), buf1, sc1);
 
   const int n = lane & 31, h = lane >> 5;
   const int head = wave * 32 + n;
@@ -337,52 +387,60 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_kernel(
       const uint4 v = ld16(qh + ks * 16 + h * 8);
       st.qb[ks] = make_uint4(v.x & keep, v.y & keep, v.z & keep, v.w & keep);
     }
-    // the last k-steps of every head of this token into LDS
-    for (int i = tid; i < 128 * 2 * kQLdsSteps; i += kThreads) {
+    // the last k-steps of every head of this token into LDS (all loads of
+    // a thread issued before any store)
+    constexpr int kQL = 128 * 2 * kQLdsSteps / kThreads;   // 9 per thread
+    uint4 qv[kQL];
+#pragma unroll
+    for (int u = 0; u < kQL; ++u) {
+      const int i = tid + u * kThreads;
       const int hd = i / (2 * kQLdsSteps), r = i % (2 * kQLdsSteps);
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (hd < p.H)
-        v = ld16(p.q + ((int64_t)s.token * p.H + hd) * kLatent +
-                 (kQRegSteps + (r >> 1)) * 16 + (r & 1) * 8);
-      qlds[hd * kQLdsStride + r] = v;
+      qv[u] = ld16(p.q + ((int64_t)s.token * p.H + min(hd, p.H - 1)) * kLatent +
+                   (kQRegSteps + (r >> 1)) * 16 + (r & 1) * 8);
+    }
+#pragma unroll
+    for (int u = 0; u < kQL; ++u) {
+      const int i = tid + u * kThreads;
+      const int hd = i / (2 * kQLdsSteps), r = i % (2 * kQLdsSteps);
+      qlds[hd * kQLdsStride + r] = hd < p.H ? qv[u] : make_uint4(0, 0, 0, 0);
     }
   }
   barrier(true);
   const uint4* qrow = qlds + (wave * 32 + n) * kQLdsStride + h;
   const float sl2 = p.scale * kLog2e;
 
-  if (s.ntiles > 0) {
-    uint32_t sc0[5], sc1[5], sc2[5];
-    constexpr int per_tile = FP8 ? 10 : 9;
-    auto issue = [&](int j, uint4* dst, uint32_t (&sc)[5]) {
-      if constexpr (FP8) issue_fp8(p, s, j, dst, sc, wave);
-      else issue_bf16(p, s, j, dst, wave);
-    };
+  {
+    // Every step issues the loads of tile j+2 (clamped to the last tile, an
+    // L2 hit, when past the end) and the step count is padded to a multiple
+    // of three: each path then issues the same loads into the same buffers,
+    // which keeps the compiler from falling back to waiting for all of them.
     auto step = [&](int j, uint4* cur, uint4* nxt, uint32_t (&scc)[5],
                     uint32_t (&scn)[5]) {
-      if (j + 2 < s.ntiles) issue(j + 2, nxt, scn);
-      wait_vm(per_tile * (min(s.ntiles - 1, j + 2) - j));
+      issue(min(j + 2, s.ntiles - 1), nxt, scn);
+      wait_vm(2 * per_tile);
       barrier(false);
-      const uint4* tile = cur;
-      if constexpr (FP8) {
-        convert_fp8(cur, ftile, scc, tid);
-        barrier(true);
-        tile = ftile;
-      }
-      if (active) {
-        const uint32_t vmask = (uint32_t)__builtin_amdgcn_ballot_w64(
-            s.rows[j * kRowsT + (lane & 31)] >= 0);
-        compute_tile(tile, qrow, vmask, st, sl2, lane);
+      if (j < s.ntiles) {
+        const uint4* tile = cur;
+        if constexpr (FP8) {
+          convert_fp8(cur, ftile, scc, tid);
+          barrier(true);
+          tile = ftile;
+        }
+        if (active) {
+          const uint32_t vmask = (uint32_t)__builtin_amdgcn_ballot_w64(
+              s.rows[j * kRowsT + (lane & 31)] >= 0);
+          compute_tile(tile, qrow, vmask, st, sl2, lane);
+        }
       }
       barrier(false);
     };
-    issue(0, buf0, sc0);
-    if (s.ntiles > 1) issue(1, buf1, sc1);
-    for (int j = 0; j < s.ntiles; j += 3) {
+    const int nsteps = (s.ntiles + 2) / 3 * 3;
+    for (int j = 0; j < nsteps; j += 3) {
       step(j, buf0, buf2, sc0, sc2);
-      if (j + 1 < s.ntiles) step(j + 1, buf1, buf0, sc1, sc0);
-      if (j + 2 < s.ntiles) step(j + 2, buf2, buf1, sc2, sc1);
+      step(j + 1, buf1, buf0, sc1, sc0);
+      step(j + 2, buf2, buf1, sc2, sc1);
     }
+    wait_vm(0);
   }
   if (!active || head >= p.H) return;
 
@@ -404,46 +462,59 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_kernel(
                  : (ltot > 0.f ? (st.m + __builtin_log2f(ltot)) * kLn2
                                : -__builtin_inff());
   } else {
+    // partial of this split: O / l in bf16 (relative rounding 2^-9, well
+    // inside the output tolerance) plus (m, l) in fp32
     const int64_t slot = ((int64_t)s.token * gridDim.x + blockIdx.x) * p.H + head;
-    float* o = p.partial + slot * (kValue + 2);
+    const float inv = ltot > 0.f ? 1.0f / ltot : 0.f;
+    uint16_t* o = reinterpret_cast<uint16_t*>(p.partial) + slot * kValue;
 #pragma unroll
     for (int t = 0; t < kValue / 32; ++t)
 #pragma unroll
       for (int g = 0; g < 4; ++g)
-        *reinterpret_cast<float4*>(o + 32 * t + 8 * g + dvb) =
-            make_float4(st.o[t][4 * g], st.o[t][4 * g + 1], st.o[t][4 * g + 2],
-                        st.o[t][4 * g + 3]);
+        *reinterpret_cast<uint2*>(o + 32 * t + 8 * g + dvb) =
+            make_uint2(pack_bf16x2(st.o[t][4 * g] * inv, st.o[t][4 * g + 1] * inv),
+                       pack_bf16x2(st.o[t][4 * g + 2] * inv,
+                                   st.o[t][4 * g + 3] * inv));
     if (h == 0) {
-      o[kValue] = st.bad ? __builtin_nanf("") : (ltot > 0.f ? st.m : -__builtin_inff());
-      o[kValue + 1] = ltot;
+      const int64_t nslots = (int64_t)gridDim.y * gridDim.x * p.H;
+      float* ml = reinterpret_cast<float*>(
+                      reinterpret_cast<uint16_t*>(p.partial) + nslots * kValue) +
+                  2 * slot;
+      ml[0] = st.bad ? __builtin_nanf("") : (ltot > 0.f ? st.m : -__builtin_inff());
+      ml[1] = ltot;
     }
   }
 }
 
-// Merge split partials (m in log2 units, l, unnormalised O) by LSE.
+// Merge split partials: out = sum_s w_s * (O_s / l_s) / sum_s w_s with
+// w_s = l_s * 2^(m_s - M), M the largest m_s; lse = ln(2^M * sum_s w_s).
 __global__ __launch_bounds__(128) void combine_kernel(AttnLaunch p,
                                                       int splits) {
   const int token = blockIdx.x, head = blockIdx.y;
   const int dv = threadIdx.x * 4;
-  const float* base =
-      p.partial + ((int64_t)token * splits * p.H + head) * (kValue + 2);
-  const int64_t sstride = (int64_t)p.H * (kValue + 2);
+  const int64_t nslots = (int64_t)gridDim.x * splits * p.H;
+  const uint16_t* po = reinterpret_cast<const uint16_t*>(p.partial);
+  const float* ml = reinterpret_cast<const float*>(po + nslots * kValue);
+  const int64_t slot0 = (int64_t)token * splits * p.H + head;
   float M = -__builtin_inff();
-  for (int sp = 0; sp < splits; ++sp) M = fmaxf(M, base[sp * sstride + kValue]);
+  for (int sp = 0; sp < splits; ++sp) {
+    const float m = ml[2 * (slot0 + (int64_t)sp * p.H)];
+    M = (m != m || M != M) ? __builtin_nanf("") : fmaxf(M, m);
+  }
   float wsum = 0.f;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  if (M != -__builtin_inff()) {
+  if (M != -__builtin_inff() && M == M) {
     for (int sp = 0; sp < splits; ++sp) {
-      const float* o = base + sp * sstride;
-      const float m = o[kValue];
-      if (m == -__builtin_inff()) continue;
-      const float f = exp2f(m - M);
-      wsum += f * o[kValue + 1];
-      const float4 v = *reinterpret_cast<const float4*>(o + dv);
-      acc.x += f * v.x;
-      acc.y += f * v.y;
-      acc.z += f * v.z;
-      acc.w += f * v.w;
+      const int64_t slot = slot0 + (int64_t)sp * p.H;
+      const float m = ml[2 * slot], l = ml[2 * slot + 1];
+      if (m == -__builtin_inff() || !(l > 0.f)) continue;
+      const float f = l * exp2f(m - M);
+      wsum += f;
+      const uint2 v = *reinterpret_cast<const uint2*>(po + slot * kValue + dv);
+      acc.x += f * __builtin_bit_cast(float, v.x << 16);
+      acc.y += f * __builtin_bit_cast(float, v.x & 0xffff0000u);
+      acc.z += f * __builtin_bit_cast(float, v.y << 16);
+      acc.w += f * __builtin_bit_cast(float, v.y & 0xffff0000u);
     }
   }
   const float inv = wsum > 0.f ? 1.0f / wsum : 0.f;
@@ -452,7 +523,9 @@ __global__ __launch_bounds__(128) void combine_kernel(AttnLaunch p,
       make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
   if (threadIdx.x == 0)
     p.lse[(int64_t)token * p.H + head] =
-        wsum > 0.f ? (M + __builtin_log2f(wsum)) * kLn2 : -__builtin_inff();
+        M != M ? M
+               : (wsum > 0.f ? (M + __builtin_log2f(wsum)) * kLn2
+                             : -__builtin_inff());
 }
 
 }  // namespace
@@ -469,7 +542,7 @@ int attn_splits(int tokens, int K) {
 size_t attn_workspace_bytes(int tokens, int H, int K) {
   const int s = attn_splits(tokens, K);
   if (s <= 1) return 0;
-  return (size_t)tokens * s * H * (kValue + 2) * sizeof(float);
+  return (size_t)tokens * s * H * (kValue * sizeof(uint16_t) + 2 * sizeof(float));
 }
 
 hipError_t launch_sparse_mla(const AttnLaunch& p, hipStream_t stream) {

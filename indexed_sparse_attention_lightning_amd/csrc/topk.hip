@@ -65,7 +65,7 @@ __device__ __forceinline__ uint32_t key_at(const uint32_t* keys,
 template <bool CACHED>
 __global__ __launch_bounds__(kThreads, 1) void topk_kernel(TopkLaunch p) {
   __shared__ TopkShared sh;
-  __shared__ uint32_t keys[CACHED ? kCacheKeys : 1];
+  __shared__ __attribute__((aligned(16))) uint32_t keys[CACHED ? kCacheKeys : 4];
   const int tid = threadIdx.x, lane = lane_id();
   const int wave = tid / kWave;
   const int r = blockIdx.x;
@@ -82,9 +82,32 @@ __global__ __launch_bounds__(kThreads, 1) void topk_kernel(TopkLaunch p) {
     return;
   }
 
-  // ---- keys, min and max
+  // ---- keys, min and max (16-byte loads, eight in flight per thread)
   uint32_t kmin = 0xffffffffu, kmax = 0u;
-  for (int i = tid; i < n; i += kThreads) {
+  const bool vec = ((reinterpret_cast<uintptr_t>(row) & 15) == 0);
+  const int n4 = vec ? n / 4 : 0;
+  for (int base = 0; base < n4; base += 8 * kThreads) {
+    float4 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int i4 = base + u * kThreads + tid;
+      v[u] = i4 < n4 ? reinterpret_cast<const float4*>(row)[i4]
+                     : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int i4 = base + u * kThreads + tid;
+      if (i4 < n4) {
+        const uint32_t k0 = score_key(v[u].x), k1 = score_key(v[u].y);
+        const uint32_t k2 = score_key(v[u].z), k3 = score_key(v[u].w);
+        if constexpr (CACHED)
+          reinterpret_cast<uint4*>(keys)[i4] = make_uint4(k0, k1, k2, k3);
+        kmin = min(min(kmin, min(k0, k1)), min(k2, k3));
+        kmax = max(max(kmax, max(k0, k1)), max(k2, k3));
+      }
+    }
+  }
+  for (int i = 4 * n4 + tid; i < n; i += kThreads) {
     const uint32_t k = score_key(row[i]);
     if constexpr (CACHED) keys[i] = k;
     kmin = min(kmin, k);
@@ -125,6 +148,7 @@ __global__ __launch_bounds__(kThreads, 1) void topk_kernel(TopkLaunch p) {
     const uint32_t dmask = (1u << width) - 1u;
     for (int i = tid; i < kBins; i += kThreads) sh.hist[i] = 0;
     __syncthreads();
+#pragma unroll 8
     for (int i = tid; i < n; i += kThreads) {
       const uint32_t k = key_at<CACHED>(keys, row, i);
       const bool match = plen == 0 || (k >> (32 - plen)) == prefix;
@@ -164,6 +188,7 @@ __global__ __launch_bounds__(kThreads, 1) void topk_kernel(TopkLaunch p) {
   const int seg = ((n + kWaves - 1) / kWaves + kWave - 1) / kWave * kWave;
   const int lo = wave * seg, hi = min(n, lo + seg);
   uint32_t gt = 0, eq = 0;
+#pragma unroll 8
   for (int base = lo; base < hi; base += kWave) {
     const int i = base + lane;
     const uint32_t k = i < hi ? key_at<CACHED>(keys, row, i) : 0u;
