@@ -42,7 +42,7 @@
  *
  * Support set: indexer heads 1 <= H_I <= 64; indexer dim d_I in {64, 128};
  * MLA heads 1 <= H <= 128; latent width 576, value width 512; 1 <= K <= 2048;
- * page size 64.
+ * page size 64; Top-K rows (and decode-step sequences) up to 131072 tokens.
  */
 #ifndef DSA_H_
 #define DSA_H_
@@ -80,6 +80,7 @@ typedef enum dsa_op {
 #define DSA_VALUE_DIM 512
 #define DSA_PAGE_SIZE 64
 #define DSA_MAX_TOPK 2048
+#define DSA_MAX_CONTEXT 131072   /* longest score row / sequence */
 
 /*
  * One layer's paged cache: indexer keys and latent KV in two page pools that

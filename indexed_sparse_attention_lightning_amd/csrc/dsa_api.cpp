@@ -120,7 +120,8 @@ dsa_status dsa_indexer_scores(int B, int T, int L, int H_I, int d_I,
   a.q_idx = static_cast<const uint16_t*>(q_idx);
   a.w = w;
   a.keys = dsa::CacheView{static_cast<const uint8_t*>(k_idx), k_scale, nullptr,
-                          0, L, fp8};
+                          0, L, fp8,
+                          (uint64_t)B * L * d_I * (fp8 ? 1 : 2)};
   a.qp = dsa::QueryPos{q_pos, nullptr, T};
   a.scores = scores;
   a.row_len = L;
@@ -136,6 +137,8 @@ dsa_status dsa_topk(int B, int T, int L, int K, const float* scores,
   if (!scores || !q_pos || !idx)
     return fail(DSA_ERR_NULL, "dsa_topk: NULL tensor pointer");
   if (B < 1 || T < 1 || L < 1) return fail(DSA_ERR_SHAPE, "B, T, L must be >= 1");
+  if (L > DSA_MAX_CONTEXT)
+    return fail(DSA_ERR_UNSUPPORTED, "L must be <= %d", DSA_MAX_CONTEXT);
   if ((long long)B * T > 0x7fffffffLL)
     return fail(DSA_ERR_UNSUPPORTED, "B*T too large");
   if (K < 1 || K > DSA_MAX_TOPK)
@@ -173,7 +176,8 @@ dsa_status dsa_sparse_mla_attn(int B, int T, int L, int H, int K,
   a.B = B; a.T = T; a.H = H; a.K = K;
   a.q = static_cast<const uint16_t*>(q);
   a.kv = dsa::CacheView{static_cast<const uint8_t*>(kv), kv_scale, nullptr, 0,
-                        L, fp8};
+                        L, fp8,
+                        (uint64_t)B * L * DSA_LATENT_DIM * (fp8 ? 1 : 2)};
   a.idx = idx;
   a.seq_lens = nullptr;
   a.scale = softmax_scale;
@@ -205,6 +209,9 @@ dsa_status dsa_decode_step(int B, int T, int H_I, int d_I, int H, int K,
     return fail(DSA_ERR_SHAPE, "num_pages and max_pages_per_seq must be >= 1");
   if ((long long)cache->num_pages * DSA_PAGE_SIZE > 0x7fffffffLL)
     return fail(DSA_ERR_UNSUPPORTED, "num_pages * 64 must fit in int32");
+  if (max_seq_len > DSA_MAX_CONTEXT)
+    return fail(DSA_ERR_UNSUPPORTED, "max_seq_len must be <= %d",
+                DSA_MAX_CONTEXT);
   if (max_seq_len < 1 ||
       (long long)max_seq_len > (long long)cache->max_pages_per_seq * DSA_PAGE_SIZE)
     return fail(DSA_ERR_SHAPE,
@@ -240,7 +247,9 @@ dsa_status dsa_decode_step(int B, int T, int H_I, int d_I, int H, int K,
   ia.w = w;
   ia.keys = dsa::CacheView{static_cast<const uint8_t*>(cache->kidx),
                            cache->kidx_scale, cache->page_table,
-                           cache->max_pages_per_seq, 0, kfp8};
+                           cache->max_pages_per_seq, 0, kfp8,
+                           (uint64_t)cache->num_pages * DSA_PAGE_SIZE * d_I *
+                               (kfp8 ? 1 : 2)};
   ia.qp = qp;
   ia.scores = scores;
   ia.row_len = max_seq_len;
@@ -260,7 +269,9 @@ dsa_status dsa_decode_step(int B, int T, int H_I, int d_I, int H, int K,
   aa.q = static_cast<const uint16_t*>(q);
   aa.kv = dsa::CacheView{static_cast<const uint8_t*>(cache->kv),
                          cache->kv_scale, cache->page_table,
-                         cache->max_pages_per_seq, 0, vfp8};
+                         cache->max_pages_per_seq, 0, vfp8,
+                         (uint64_t)cache->num_pages * DSA_PAGE_SIZE *
+                             DSA_LATENT_DIM * (vfp8 ? 1 : 2)};
   aa.idx = idx;
   aa.seq_lens = cache->seq_lens;
   aa.scale = softmax_scale;

@@ -17,6 +17,7 @@ struct CacheView {
   int max_pages;
   int L;                      // contiguous length (rows per sequence)
   bool fp8;                   // e4m3 codes + MX-32 scales, else bf16
+  uint64_t bytes;             // size of `data` in bytes
 };
 
 // Query positions: q_pos[b*T + t] if given, else seq_lens[b] - 1; with

@@ -91,9 +91,28 @@ struct Split {
   const int32_t* rows;   // LDS: physical row per split row, ~row if invalid
 };
 
+// One 16-byte direct-to-LDS load per lane: lane l's bytes land at
+// dst + 16*l.  With BUF the load is a buffer load through `rsrc` (pools under
+// 4 GiB): the compiler tracks it as a plain vector-memory load, where the
+// global (FLAT) form would be treated as possibly touching LDS out of order
+// and turn every LDS wait into a full drain.
+template <bool BUF>
+__device__ __forceinline__ void dma16(const uint8_t* base,
+                                      __amdgpu_buffer_rsrc_t rsrc,
+                                      uint64_t off, uint4* dst) {
+  if constexpr (BUF)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rsrc, (__attribute__((address_space(3))) void*)dst, 16, (uint32_t)off,
+        0, 0, 0);
+  else
+    __builtin_amdgcn_global_load_lds(base + off, dst, 16, 0, 0);
+}
+
 // Issue the direct-to-LDS loads of tile j (bf16 rows straight into a tile).
+template <bool BUF>
 __device__ __forceinline__ void issue_bf16(const AttnLaunch& p, const Split& s,
-                                           int j, uint4* dst, int wave) {
+                                           __amdgpu_buffer_rsrc_t rsrc, int j,
+                                           uint4* dst, int wave) {
   const int lane = opaque(lane_id());
 #pragma unroll
   for (int k = 0; k < kTileSlots / kThreads; ++k) {
@@ -103,15 +122,17 @@ __device__ __forceinline__ void issue_bf16(const AttnLaunch& p, const Split& s,
     const int c = pch ^ kv_swz(R);
     int ent = s.rows[j * kRowsT + R];
     ent = ent >= 0 ? ent : ~ent;
-    const uint8_t* g = p.kv.data + ((uint64_t)(uint32_t)ent * (kLatent * 2) + c * 16);
-    __builtin_amdgcn_global_load_lds(g, dst + seg * kWave, 16, 0, 0);
+    dma16<BUF>(p.kv.data, rsrc, (uint64_t)(uint32_t)ent * (kLatent * 2) + c * 16,
+               dst + seg * kWave);
   }
 }
 
 // FP8: codes (linear, 36 chunks per row) by DMA, the scale code each of this
 // thread's conversion slots needs into registers.
+template <bool BUF>
 __device__ __forceinline__ void issue_fp8(const AttnLaunch& p, const Split& s,
-                                          int j, uint4* dst, uint32_t (&sc)[5],
+                                          __amdgpu_buffer_rsrc_t rsrc, int j,
+                                          uint4* dst, uint32_t (&sc)[5],
                                           int wave) {
   const int lane = opaque(lane_id());
   const int tid = wave * kWave + lane;
@@ -122,8 +143,8 @@ __device__ __forceinline__ void issue_fp8(const AttnLaunch& p, const Split& s,
     const int R = q / kCodeSlotsRow, c = q % kCodeSlotsRow;
     int ent = s.rows[j * kRowsT + R];
     ent = ent >= 0 ? ent : ~ent;
-    const uint8_t* g = p.kv.data + (int64_t)ent * kLatent + c * 16;
-    __builtin_amdgcn_global_load_lds(g, dst + seg * kWave, 16, 0, 0);
+    dma16<BUF>(p.kv.data, rsrc, (uint64_t)(uint32_t)ent * kLatent + c * 16,
+               dst + seg * kWave);
   }
 #pragma unroll
   for (int k = 0; k < 5; ++k) {
@@ -311,7 +332,7 @@ __device__ __forceinline__ void compute_tile(const uint4* tile,
   }
 }
 
-template <bool FP8>
+template <bool FP8, bool BUF>
 __global__ __launch_bounds__(kThreads, 1) void sparse_mla_kernel(
     AttnLaunch p, int rows_per_split) {
   constexpr int kBufSlots = FP8 ? kStageSlots : kTileSlots;
@@ -324,10 +345,21 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_kernel(
 
   const int tid = threadIdx.x, lane = lane_id();
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  // Block -> (token, split).  Workgroups are dealt to the 8 XCDs round-robin
+  // by linear id; when the token count allows, all splits of a token go to
+  // one XCD so that its queries come from that XCD's L2 after the first read.
+  const int nsplit = gridDim.x, ntok = gridDim.y;
+  const int lin = blockIdx.y * nsplit + blockIdx.x;
+  int token = blockIdx.y, split = blockIdx.x;
+  if ((ntok & 7) == 0) {
+    const int xcd = lin & 7, slot = lin >> 3;
+    token = (slot / nsplit) * 8 + xcd;
+    split = slot % nsplit;
+  }
   Split s;
-  s.token = blockIdx.y;
+  s.token = token;
   s.b = s.token / p.T;
-  s.r0 = blockIdx.x * rows_per_split;
+  s.r0 = split * rows_per_split;
   s.r1 = min(s.r0 + rows_per_split, p.K);
   s.ntiles = (s.r1 - s.r0 + kRowsT - 1) / kRowsT;
   s.rows = rows;
@@ -360,12 +392,15 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_kernel(
   }
   barrier(true);
 
+  const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)p.kv.data, (short)0,
+      (int)(BUF ? (uint32_t)p.kv.bytes : 0u), 0x00020000);
   // the first two tiles are in flight while the queries load
   uint32_t sc0[5], sc1[5], sc2[5];
   constexpr int per_tile = FP8 ? 10 : 9;
   auto issue = [&](int j, uint4* dst, uint32_t (&sc)[5]) {
-    if constexpr (FP8) issue_fp8(p, s, j, dst, sc, wave);
-    else issue_bf16(p, s, j, dst, wave);
+    if constexpr (FP8) issue_fp8<BUF>(p, s, rsrc, j, dst, sc, wave);
+    else issue_bf16<BUF>(p, s, rsrc, j, dst, wave);
   };
   issue(0, buf0, sc0);
   issue(min(1, s.ntiles - 1), buf1, sc1);
@@ -414,11 +449,18 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_kernel(
     // L2 hit, when past the end) and the step count is padded to a multiple
     // of three: each path then issues the same loads into the same buffers,
     // which keeps the compiler from falling back to waiting for all of them.
+    // Step j: wait for tile j (tile j+1 may still be in flight), one barrier
+    // (every wave is done with step j-1, so its buffer is free), issue the
+    // loads of tile j+2 into that buffer, then compute tile j.  Every step
+    // issues the same loads (clamped to the last tile, an L2 hit, past the
+    // end) and the step count is padded to a multiple of three, so each path
+    // issues the same loads into the same buffers and the compiler keeps its
+    // exact per-buffer waits.
     auto step = [&](int j, uint4* cur, uint4* nxt, uint32_t (&scc)[5],
                     uint32_t (&scn)[5]) {
-      issue(min(j + 2, s.ntiles - 1), nxt, scn);
-      wait_vm(2 * per_tile);
+      wait_vm(per_tile);
       barrier(false);
+      issue(min(j + 2, s.ntiles - 1), nxt, scn);
       if (j < s.ntiles) {
         const uint4* tile = cur;
         if constexpr (FP8) {
@@ -431,8 +473,8 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_kernel(
               s.rows[j * kRowsT + (lane & 31)] >= 0);
           compute_tile(tile, qrow, vmask, st, sl2, lane);
         }
+        if constexpr (FP8) barrier(false);   // ftile is rewritten next step
       }
-      barrier(false);
     };
     const int nsteps = (s.ntiles + 2) / 3 * 3;
     for (int j = 0; j < nsteps; j += 3) {
@@ -464,7 +506,7 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_kernel(
   } else {
     // partial of this split: O / l in bf16 (relative rounding 2^-9, well
     // inside the output tolerance) plus (m, l) in fp32
-    const int64_t slot = ((int64_t)s.token * gridDim.x + blockIdx.x) * p.H + head;
+    const int64_t slot = ((int64_t)s.token * gridDim.x + split) * p.H + head;
     const float inv = ltot > 0.f ? 1.0f / ltot : 0.f;
     uint16_t* o = reinterpret_cast<uint16_t*>(p.partial) + slot * kValue;
 #pragma unroll
@@ -553,12 +595,23 @@ hipError_t launch_sparse_mla(const AttnLaunch& p, hipStream_t stream) {
   rps = (rps + kRowsT - 1) / kRowsT * kRowsT;
   const int used = (p.K + rps - 1) / rps;   // splits that own rows
   dim3 grid(used, tokens);
-  if (p.kv.fp8)
-    hipLaunchKernelGGL(sparse_mla_kernel<true>, grid, dim3(kThreads), 0,
-                       stream, p, rps);
-  else
-    hipLaunchKernelGGL(sparse_mla_kernel<false>, grid, dim3(kThreads), 0,
-                       stream, p, rps);
+  // buffer-form loads address the pool with 32-bit offsets
+  const bool buf = p.kv.bytes < (1ull << 32);
+  if (p.kv.fp8) {
+    if (buf)
+      hipLaunchKernelGGL((sparse_mla_kernel<true, true>), grid, dim3(kThreads),
+                         0, stream, p, rps);
+    else
+      hipLaunchKernelGGL((sparse_mla_kernel<true, false>), grid,
+                         dim3(kThreads), 0, stream, p, rps);
+  } else {
+    if (buf)
+      hipLaunchKernelGGL((sparse_mla_kernel<false, true>), grid,
+                         dim3(kThreads), 0, stream, p, rps);
+    else
+      hipLaunchKernelGGL((sparse_mla_kernel<false, false>), grid,
+                         dim3(kThreads), 0, stream, p, rps);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || used == 1) return e;
   hipLaunchKernelGGL(combine_kernel, dim3(tokens, p.H), dim3(128), 0, stream,

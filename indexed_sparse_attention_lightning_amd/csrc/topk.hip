@@ -8,18 +8,16 @@
 // selection on chip, outputs only the final indices).  Equal scores go to the
 // lower position; the chosen positions are written in ascending order.
 //
-// One 1024-thread workgroup per score row:
-//   1. scores become order-preserving uint32 keys (cached in LDS when the row
-//      fits), with the row's min and max key;
-//   2. radix passes of up to 11 bits, starting just below the common prefix
-//      of min and max, narrow down the exact K-th largest key `thr` and how
-//      many keys equal to it are taken (`need`);
-//   3. an ordered pass over the row: every wave owns a contiguous range of
-//      positions, ranks its keys with ballot/mbcnt prefix counts, and writes
-//      each position with key > thr, plus the first `need` positions with
-//      key == thr, at its final ascending slot.
-// Everything is integer work on bit patterns, so the result is exact and
-// deterministic.
+// One 1024-thread workgroup per score row.  Scores become order-preserving
+// uint32 keys (cached in LDS when the row fits).  The exact K-th largest key
+// `thr` is found digit by digit, 12 + 12 + 8 bits from the top: each pass
+// histograms the keys that share the digits fixed so far, and a block scan in
+// descending digit order finds the digit holding the K-th key.  A last pass
+// marks, with one wave ballot per 64 positions, a bitmap of keys > thr and one
+// of keys == thr; the first `need` set bits of the second (in position order)
+// join the first, and word-level prefix popcounts give every selected
+// position its ascending output slot.  All of it is integer work on bit
+// patterns: exact and deterministic.
 #include "dsa_device.h"
 #include "dsa_launch.h"
 
@@ -28,23 +26,15 @@ namespace {
 
 constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / kWave;
-constexpr int kCacheKeys = 32768;   // rows up to this length live in LDS
-constexpr int kBins = 2048;         // 11-bit digits
+constexpr int kCacheKeys = 32768;          // rows up to this length live in LDS
+constexpr int kBins = 4096;                // 12-bit digits
+constexpr int kMaxRow = 131072;            // longest row of the uncached path
+constexpr int kMaxWords = kMaxRow / 32;    // bitmap words for that row
 
-struct TopkShared {
-  uint32_t hist[kBins];
-  uint32_t red[2][kWaves];
-  uint32_t wtot[kWaves];
-  uint32_t gt_w[kWaves];
-  uint32_t eq_w[kWaves];
-  uint32_t pick[2];       // chosen digit, keys above it
+struct alignas(16) Small {
+  uint32_t wsum[kWaves];
+  uint32_t pick[2];      // chosen digit, keys in larger digits
 };
-
-__device__ __forceinline__ uint32_t prefix_below(uint64_t mask) {
-  // number of set bits of `mask` in lanes below this one
-  return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
-                                   __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0));
-}
 
 __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v, int lane) {
 #pragma unroll
@@ -53,6 +43,59 @@ __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v, int lane) {
     if (lane >= off) v += o;
   }
   return v;
+}
+
+// Exclusive prefix of v over the block in thread order; also returns the
+// block total.  Two barriers.
+__device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, Small& sm,
+                                                   int tid, int lane,
+                                                   uint32_t& total) {
+  const int wave = tid / kWave;
+  const uint32_t incl = wave_incl_scan(v, lane);
+  if (lane == kWave - 1) sm.wsum[wave] = incl;
+  __syncthreads();
+  uint32_t base = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    const uint32_t x = sm.wsum[w];
+    base += w < wave ? x : 0u;
+    tot += x;
+  }
+  total = tot;
+  __syncthreads();
+  return base + incl - v;
+}
+
+// The digit holding the `remaining`-th largest key: thread tid owns digits
+// nbins-1-4*tid .. nbins-4-4*tid (descending order across the block).
+// Returns the digit and the count of keys in larger digits, to every thread.
+__device__ __forceinline__ void pick_digit(const uint32_t* hist, int nbins,
+                                           uint32_t remaining, Small& sm,
+                                           int tid, int lane,
+                                           uint32_t& digit, uint32_t& above) {
+  uint32_t c[4];
+  uint32_t s = 0;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int d = nbins - 1 - 4 * tid - u;
+    c[u] = d >= 0 ? hist[d] : 0u;
+    s += c[u];
+  }
+  uint32_t total;
+  uint32_t run = block_excl_scan(s, sm, tid, lane, total);
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int d = nbins - 1 - 4 * tid - u;
+    if (c[u] && run < remaining && remaining <= run + c[u]) {
+      sm.pick[0] = (uint32_t)d;
+      sm.pick[1] = run;
+    }
+    run += c[u];
+  }
+  __syncthreads();
+  digit = sm.pick[0];
+  above = sm.pick[1];
+  __syncthreads();
 }
 
 template <bool CACHED>
@@ -64,8 +107,11 @@ __device__ __forceinline__ uint32_t key_at(const uint32_t* keys,
 
 template <bool CACHED>
 __global__ __launch_bounds__(kThreads, 1) void topk_kernel(TopkLaunch p) {
-  __shared__ TopkShared sh;
+  // LDS: key cache | histogram, reused afterwards for the two bitmaps
+  constexpr int kHist = CACHED ? kBins : 2 * kMaxWords;
   __shared__ __attribute__((aligned(16))) uint32_t keys[CACHED ? kCacheKeys : 4];
+  __shared__ __attribute__((aligned(16))) uint32_t hist[kHist];
+  __shared__ Small sm;
   const int tid = threadIdx.x, lane = lane_id();
   const int wave = tid / kWave;
   const int r = blockIdx.x;
@@ -82,149 +128,142 @@ __global__ __launch_bounds__(kThreads, 1) void topk_kernel(TopkLaunch p) {
     return;
   }
 
-  // ---- keys, min and max (16-byte loads, eight in flight per thread)
-  uint32_t kmin = 0xffffffffu, kmax = 0u;
-  const bool vec = ((reinterpret_cast<uintptr_t>(row) & 15) == 0);
-  const int n4 = vec ? n / 4 : 0;
-  for (int base = 0; base < n4; base += 8 * kThreads) {
-    float4 v[8];
+  // ---- pass 1: keys (cached), histogram of the top 12 bits
+  for (int i = tid; i < kBins; i += kThreads) hist[i] = 0;
+  __syncthreads();
+  {
+    const bool vec = ((reinterpret_cast<uintptr_t>(row) & 15) == 0);
+    const int n4 = vec ? n / 4 : 0;
+    for (int base = 0; base < n4; base += 8 * kThreads) {
+      float4 v[8];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int i4 = base + u * kThreads + tid;
-      v[u] = i4 < n4 ? reinterpret_cast<const float4*>(row)[i4]
-                     : make_float4(0.f, 0.f, 0.f, 0.f);
+      for (int u = 0; u < 8; ++u) {
+        const int i4 = base + u * kThreads + tid;
+        v[u] = i4 < n4 ? reinterpret_cast<const float4*>(row)[i4]
+                       : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int i4 = base + u * kThreads + tid;
+        if (i4 < n4) {
+          const uint32_t k0 = score_key(v[u].x), k1 = score_key(v[u].y);
+          const uint32_t k2 = score_key(v[u].z), k3 = score_key(v[u].w);
+          if constexpr (CACHED)
+            reinterpret_cast<uint4*>(keys)[i4] = make_uint4(k0, k1, k2, k3);
+          atomicAdd(&hist[k0 >> 20], 1u);
+          atomicAdd(&hist[k1 >> 20], 1u);
+          atomicAdd(&hist[k2 >> 20], 1u);
+          atomicAdd(&hist[k3 >> 20], 1u);
+        }
+      }
     }
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int i4 = base + u * kThreads + tid;
-      if (i4 < n4) {
-        const uint32_t k0 = score_key(v[u].x), k1 = score_key(v[u].y);
-        const uint32_t k2 = score_key(v[u].z), k3 = score_key(v[u].w);
-        if constexpr (CACHED)
-          reinterpret_cast<uint4*>(keys)[i4] = make_uint4(k0, k1, k2, k3);
-        kmin = min(min(kmin, min(k0, k1)), min(k2, k3));
-        kmax = max(max(kmax, max(k0, k1)), max(k2, k3));
+    for (int i = 4 * n4 + tid; i < n; i += kThreads) {
+      const uint32_t k = score_key(row[i]);
+      if constexpr (CACHED) keys[i] = k;
+      atomicAdd(&hist[k >> 20], 1u);
+    }
+  }
+  __syncthreads();
+  uint32_t d1, above;
+  pick_digit(hist, kBins, (uint32_t)kk, sm, tid, lane, d1, above);
+  uint32_t remaining = (uint32_t)kk - above;
+
+  // ---- pass 2: the next 12 bits among keys whose top 12 bits are d1
+  for (int i = tid; i < kBins; i += kThreads) hist[i] = 0;
+  __syncthreads();
+#pragma unroll 8
+  for (int i = tid; i < n; i += kThreads) {
+    const uint32_t k = key_at<CACHED>(keys, row, i);
+    if ((k >> 20) == d1) atomicAdd(&hist[(k >> 8) & 0xfffu], 1u);
+  }
+  __syncthreads();
+  uint32_t d2;
+  pick_digit(hist, kBins, remaining, sm, tid, lane, d2, above);
+  remaining -= above;
+  const uint32_t pre24 = (d1 << 12) | d2;
+
+  // ---- pass 3: the last 8 bits
+  for (int i = tid; i < 256; i += kThreads) hist[i] = 0;
+  __syncthreads();
+#pragma unroll 8
+  for (int i = tid; i < n; i += kThreads) {
+    const uint32_t k = key_at<CACHED>(keys, row, i);
+    if ((k >> 8) == pre24) atomicAdd(&hist[k & 0xffu], 1u);
+  }
+  __syncthreads();
+  uint32_t d3;
+  pick_digit(hist, 256, remaining, sm, tid, lane, d3, above);
+  const uint32_t thr = (pre24 << 8) | d3;
+  const uint32_t need = remaining - above;   // keys equal to thr that are taken
+
+  // ---- pass 4: bitmaps of keys > thr and keys == thr (one ballot per 64)
+  const int nwords = (n + 31) / 32;
+  uint32_t* gtw = hist;
+  uint32_t* eqw = hist + kHist / 2;
+#pragma unroll 4
+  for (int base = wave * kWave; base < n; base += kThreads) {
+    const int i = base + lane;
+    const uint32_t k = i < n ? key_at<CACHED>(keys, row, i) : 0u;
+    const uint64_t g = __ballot(i < n && k > thr);
+    const uint64_t e = __ballot(i < n && k == thr);
+    if (lane == 0) {
+      const int w = base / 32;
+      gtw[w] = (uint32_t)g;
+      eqw[w] = (uint32_t)e;
+      if (w + 1 < nwords) {
+        gtw[w + 1] = (uint32_t)(g >> 32);
+        eqw[w + 1] = (uint32_t)(e >> 32);
       }
     }
   }
-  for (int i = 4 * n4 + tid; i < n; i += kThreads) {
-    const uint32_t k = score_key(row[i]);
-    if constexpr (CACHED) keys[i] = k;
-    kmin = min(kmin, k);
-    kmax = max(kmax, k);
-  }
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    kmin = min(kmin, (uint32_t)__shfl_xor(kmin, off, kWave));
-    kmax = max(kmax, (uint32_t)__shfl_xor(kmax, off, kWave));
-  }
-  if (lane == 0) {
-    sh.red[0][wave] = kmin;
-    sh.red[1][wave] = kmax;
-  }
   __syncthreads();
-  kmin = sh.red[0][0];
-  kmax = sh.red[1][0];
-  for (int w = 1; w < kWaves; ++w) {
-    kmin = min(kmin, sh.red[0][w]);
-    kmax = max(kmax, sh.red[1][w]);
-  }
 
-  // ---- radix passes below the common prefix of kmin and kmax
-  uint32_t prefix = 0;   // value of the fixed top `plen` bits
-  int plen = 0;
-  uint32_t remaining = kk;
-  const uint32_t diff = kmin ^ kmax;
-  if (diff == 0) {
-    prefix = kmax;
-    plen = 32;
-  } else {
-    plen = __builtin_clz(diff);
-    prefix = plen ? (kmax >> (32 - plen)) : 0u;
-  }
-  while (plen < 32) {
-    const int width = min(11, 32 - plen);
-    const int shift = 32 - plen - width;
-    const uint32_t dmask = (1u << width) - 1u;
-    for (int i = tid; i < kBins; i += kThreads) sh.hist[i] = 0;
-    __syncthreads();
-#pragma unroll 8
-    for (int i = tid; i < n; i += kThreads) {
-      const uint32_t k = key_at<CACHED>(keys, row, i);
-      const bool match = plen == 0 || (k >> (32 - plen)) == prefix;
-      if (match) atomicAdd(&sh.hist[(k >> shift) & dmask], 1u);
-    }
-    __syncthreads();
-    // thread tid owns digits (2047 - 2*tid) and (2046 - 2*tid): a scan in
-    // descending digit order gives, per digit, the count of larger digits
-    const int d0 = kBins - 1 - 2 * tid, d1 = d0 - 1;
-    const uint32_t c0 = sh.hist[d0], c1 = sh.hist[d1];
-    const uint32_t incl = wave_incl_scan(c0 + c1, lane);
-    if (lane == kWave - 1) sh.wtot[wave] = incl;
-    __syncthreads();
-    uint32_t base = 0;
-    for (int w = 0; w < wave; ++w) base += sh.wtot[w];
-    const uint32_t above0 = base + incl - (c0 + c1);   // keys in digits > d0
-    const uint32_t above1 = above0 + c0;
-    if (c0 && above0 < remaining && remaining <= above0 + c0) {
-      sh.pick[0] = d0;
-      sh.pick[1] = above0;
-    }
-    if (c1 && above1 < remaining && remaining <= above1 + c1) {
-      sh.pick[0] = d1;
-      sh.pick[1] = above1;
-    }
-    __syncthreads();
-    const uint32_t dsel = sh.pick[0];
-    remaining -= sh.pick[1];
-    prefix = (plen == 0 ? 0u : (prefix << width)) | dsel;
-    plen += width;
-    __syncthreads();   // hist and pick are rewritten by the next pass
-  }
-  const uint32_t thr = prefix;
-  const uint32_t need = remaining;   // keys equal to thr that are taken
-
-  // ---- ordered output
-  const int seg = ((n + kWaves - 1) / kWaves + kWave - 1) / kWave * kWave;
-  const int lo = wave * seg, hi = min(n, lo + seg);
-  uint32_t gt = 0, eq = 0;
-#pragma unroll 8
-  for (int base = lo; base < hi; base += kWave) {
-    const int i = base + lane;
-    const uint32_t k = i < hi ? key_at<CACHED>(keys, row, i) : 0u;
-    gt += (i < hi && k > thr);
-    eq += (i < hi && k == thr);
-  }
+  // ---- keep the first `need` equal keys in position order, then emit the
+  // selected positions in ascending order
+  constexpr int kWPT = kHist / 2 / kThreads;   // bitmap words per thread
+  uint32_t ew[kWPT], sw[kWPT];
+  uint32_t ecount = 0;
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    gt += __shfl_xor(gt, off, kWave);
-    eq += __shfl_xor(eq, off, kWave);
+  for (int u = 0; u < kWPT; ++u) {
+    const int w = tid * kWPT + u;
+    ew[u] = w < nwords ? eqw[w] : 0u;
+    ecount += __builtin_popcount(ew[u]);
   }
-  if (lane == 0) {
-    sh.gt_w[wave] = gt;
-    sh.eq_w[wave] = eq;
+  uint32_t etotal;
+  uint32_t ebefore = block_excl_scan(ecount, sm, tid, lane, etotal);
+  uint32_t scount = 0;
+#pragma unroll
+  for (int u = 0; u < kWPT; ++u) {
+    const int w = tid * kWPT + u;
+    uint32_t e = ew[u];
+    const uint32_t c = __builtin_popcount(e);
+    if (ebefore >= need) {
+      e = 0;
+    } else if (ebefore + c > need) {
+      uint32_t keep = need - ebefore, m = e;   // the lowest `keep` set bits
+      e = 0;
+      while (keep--) {
+        const uint32_t lo = m & (0u - m);
+        e |= lo;
+        m ^= lo;
+      }
+    }
+    ebefore += c;
+    sw[u] = (w < nwords ? gtw[w] : 0u) | e;
+    scount += __builtin_popcount(sw[u]);
   }
-  __syncthreads();
-  uint32_t eq_before = 0, sel_before = 0;
-  for (int w = 0; w < wave; ++w) {
-    const uint32_t take = eq_before >= need ? 0u : min(sh.eq_w[w], need - eq_before);
-    sel_before += sh.gt_w[w] + take;
-    eq_before += sh.eq_w[w];
-  }
-  for (int base = lo; base < hi; base += kWave) {
-    const int i = base + lane;
-    const bool valid = i < hi;
-    const uint32_t k = valid ? key_at<CACHED>(keys, row, i) : 0u;
-    const bool is_gt = valid && k > thr;
-    const bool is_eq = valid && k == thr;
-    const uint64_t eq_mask = __ballot(is_eq);
-    const uint32_t eq_rank = eq_before + prefix_below(eq_mask);
-    const bool sel = is_gt || (is_eq && eq_rank < need);
-    const uint64_t sel_mask = __ballot(sel);
-    const uint32_t slot = sel_before + prefix_below(sel_mask);
-    if (sel && slot < (uint32_t)kk) out[slot] = i;
-    eq_before += __popcll(eq_mask);
-    sel_before += __popcll(sel_mask);
+  uint32_t stotal;
+  uint32_t slot = block_excl_scan(scount, sm, tid, lane, stotal);
+#pragma unroll
+  for (int u = 0; u < kWPT; ++u) {
+    const int w = tid * kWPT + u;
+    uint32_t m = sw[u];
+    while (m) {
+      const int bit = __builtin_ctz(m);
+      m &= m - 1;
+      if (slot < (uint32_t)kk) out[slot] = w * 32 + bit;
+      ++slot;
+    }
   }
 }
 

@@ -73,6 +73,7 @@ def test_topk_validation():
     assert f(L=0) == SHAPE
     assert f(K=0) == UNSUP
     assert f(K=4097) == UNSUP
+    assert f(L=131073) == UNSUP
 
 
 def test_sparse_mla_validation():
