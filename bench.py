@@ -107,6 +107,10 @@ def main(argv=None):
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--kernels-only", action="store_true",
+                    help="run one 256 MiB device copy (counter calibration) "
+                         "and one decode step, then exit (for rocprofv3 "
+                         "--pmc runs)")
     args = ap.parse_args(argv)
     if args.gpus != 1:
         print("bench.py measures one GPU only: the DSA hot path here is a "
@@ -148,6 +152,18 @@ def main(argv=None):
         dsa.decode_step(caches[r], d["q_idx"], d["w"], d["q"], wl.top_k,
                         wl.softmax_scale, max_seq_len=L, out=o, lse=l,
                         idx_out=ix, workspace=ws)
+
+    if args.kernels_only:
+        torch.cuda.synchronize()
+        src = torch.ones(1 << 26, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)                  # reads and writes exactly 256 MiB
+        torch.cuda.synchronize()
+        step(0)
+        torch.cuda.synchronize()
+        print(json.dumps({"kernels_only": True, "copy_bytes": 1 << 28}))
+        return 0
 
     ms = time_loop(step, args.steps, args.warmup, stream)
 
