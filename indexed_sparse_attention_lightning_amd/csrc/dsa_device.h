@@ -82,9 +82,11 @@ __device__ __forceinline__ int64_t cache_row(const int32_t* page_table,
 }
 
 // Order-preserving map float -> uint32: larger float <=> larger key.
-// -0 is folded onto +0 and every NaN onto key 0 (below all numbers).
+// -0 is folded onto +0 and every NaN onto key 1 (below all numbers, whose
+// keys start at 0x007fffff for -inf); key 0 is left free as a "no position"
+// marker.
 __device__ __forceinline__ uint32_t score_key(float x) {
-  if (x != x) return 0u;
+  if (x != x) return 1u;
   const uint32_t u = __builtin_bit_cast(uint32_t, x + 0.0f);
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }

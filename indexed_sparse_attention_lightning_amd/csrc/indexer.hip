@@ -212,6 +212,150 @@ __global__ __launch_bounds__(256, 2) void indexer_stream_kernel(
   }
 }
 
+// ---------------------------------------------------------------- prefill
+// Query-tiled indexer for many queries per sequence (prefill chunks): a
+// workgroup of 8 waves takes 8 consecutive queries (one per wave, two waves
+// per SIMD) and one chunk of keys.  The keys are staged once per workgroup
+// in 64-key LDS stages (double-buffered, the next stage's loads in flight in
+// registers) and every wave scores them against its own query, so each key
+// byte read from HBM feeds 8 queries x 64 heads of MFMA work.  Stages past
+// the last query of the tile are skipped (causal), and each wave skips the
+// 32-key halves that lie entirely past its own query.
+constexpr int kTileQ = 8;          // queries per workgroup (one per wave)
+constexpr int kStageKeys = 64;     // keys per LDS stage (one page)
+
+template <int DI, bool FP8>
+struct TileStage {
+  // 16-byte loads of one 64-key stage (bf16 rows are 2*DI bytes, FP8 rows DI
+  // codes plus DI/32 scales), spread over the workgroup's threads
+  static constexpr int kTotal = kStageKeys * (FP8 ? DI : 2 * DI) / 16;
+  static constexpr int kThreads = kTileQ * kWave;
+  static constexpr int kLoads = (kTotal + kThreads - 1) / kThreads;
+  static constexpr bool kPartial = kTotal % kThreads != 0;
+  uint4 v[kLoads];
+  uint32_t sc[FP8 ? kLoads : 1];
+};
+
+template <int DI, bool FP8>
+__device__ __forceinline__ void tile_load(TileStage<DI, FP8>& st,
+                                          const CacheView& kc, int b,
+                                          int kbase, int tid) {
+  using KL = KeyLayout<DI>;
+  int64_t row0;
+  bool clamp = false;
+  if (kc.page_table != nullptr) {
+    row0 = cache_row(kc.page_table, kc.max_pages, kc.L, b, kbase);
+  } else {
+    row0 = (int64_t)b * kc.L + kbase;
+    clamp = kbase + kStageKeys > kc.L;
+  }
+#pragma unroll
+  for (int i = 0; i < TileStage<DI, FP8>::kLoads; ++i) {
+    const int id = i * kTileQ * kWave + tid;
+    if (TileStage<DI, FP8>::kPartial && id >= TileStage<DI, FP8>::kTotal)
+      break;
+    if constexpr (!FP8) {
+      const int n = id / KL::kChunks, c = id % KL::kChunks;
+      int64_t row = row0 + n;
+      if (clamp) row = (int64_t)b * kc.L + min(kbase + n, kc.L - 1);
+      st.v[i] = ld16(kc.data + row * (DI * 2) + c * 16);
+    } else {
+      const int n = id / KL::kCodeChunks, c = id % KL::kCodeChunks;
+      int64_t row = row0 + n;
+      if (clamp) row = (int64_t)b * kc.L + min(kbase + n, kc.L - 1);
+      st.v[i] = ld16(kc.data + row * DI + c * 16);
+      st.sc[i] = kc.scale[row * (DI / 32) + (c >> 1)];
+    }
+  }
+}
+
+template <int DI, bool FP8>
+__device__ __forceinline__ void tile_store(const TileStage<DI, FP8>& st,
+                                           uint4* tile, int tid) {
+  using KL = KeyLayout<DI>;
+#pragma unroll
+  for (int i = 0; i < TileStage<DI, FP8>::kLoads; ++i) {
+    const int id = i * kTileQ * kWave + tid;
+    if (TileStage<DI, FP8>::kPartial && id >= TileStage<DI, FP8>::kTotal)
+      break;
+    if constexpr (!FP8) {
+      const int n = id / KL::kChunks, c = id % KL::kChunks;
+      tile[n * KL::kChunks + KL::slot(n, c)] = st.v[i];
+    } else {
+      const int n = id / KL::kCodeChunks, c = id % KL::kCodeChunks;
+      tile[n * KL::kChunks + KL::slot(n, 2 * c)] =
+          dequant8_e4m3(make_uint2(st.v[i].x, st.v[i].y), st.sc[i]);
+      tile[n * KL::kChunks + KL::slot(n, 2 * c + 1)] =
+          dequant8_e4m3(make_uint2(st.v[i].z, st.v[i].w), st.sc[i]);
+    }
+  }
+}
+
+template <int DI, int MB, bool FP8>
+__global__ __launch_bounds__(kTileQ * kWave, 2) void indexer_tile_kernel(
+    IndexerLaunch p, int keys_per_wg) {
+  using KL = KeyLayout<DI>;
+  constexpr int kTileU4 = kStageKeys * KL::kRowBytes / 16;
+  __shared__ uint4 lds[2][kTileU4];
+  const int tid = threadIdx.x, lane = lane_id();
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int b = blockIdx.z;
+  const int t = blockIdx.y * kTileQ + wave;
+  const bool has_q = t < p.T;
+  const int c0 = blockIdx.x * keys_per_wg;
+  const int c1 = min(c0 + keys_per_wg, p.row_len);
+  // causal extent of the tile: its last query
+  int qmax = -1;
+  for (int w = 0; w < kTileQ; ++w) {
+    const int tt = blockIdx.y * kTileQ + w;
+    if (tt < p.T) qmax = max(qmax, query_pos(p.qp, b, tt));
+  }
+  const int qpos = has_q ? __builtin_amdgcn_readfirstlane(query_pos(p.qp, b, t)) : -1;
+  float* srow = has_q ? p.scores + ((int64_t)b * p.T + t) * p.row_len : nullptr;
+  if (has_q)
+    for (int s = max(c0, qpos + 1) + lane; s < c1; s += kWave)
+      srow[s] = -__builtin_inff();
+  const int kend = min(c1, qmax + 1);
+  if (kend <= c0) return;   // workgroup-uniform
+  const int nst = (kend - c0 + kStageKeys - 1) / kStageKeys;
+
+  uint4 a[MB][DI / 16];
+  float wv[MB][16];
+  {
+    const int64_t qrow = (int64_t)b * p.T + (has_q ? t : 0);
+    load_query<DI, MB>(p.q_idx + qrow * p.H_I * DI, p.w + qrow * p.H_I, p.H_I,
+                       lane, a, wv);
+  }
+  TileStage<DI, FP8> st;
+  tile_load<DI, FP8>(st, p.keys, b, c0, tid);
+  for (int i = 0; i < nst; ++i) {
+    uint4* tile = lds[i & 1];
+    tile_store<DI, FP8>(st, tile, tid);
+    if (i + 1 < nst) tile_load<DI, FP8>(st, p.keys, b, c0 + (i + 1) * kStageKeys, tid);
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < kStageKeys / kSub; ++u) {
+      const int kb = c0 + i * kStageKeys + u * kSub;
+      if (has_q && kb <= qpos) {   // wave-uniform
+        const float sc = tile_scores<DI, MB>(tile + u * kSub * KL::kChunks, a,
+                                             wv, lane);
+        const int s = kb + (lane & 31);
+        if (lane < 32 && s <= qpos && s < c1) srow[s] = sc + 0.0f;
+      }
+    }
+  }
+}
+
+template <int DI, int MB, bool FP8>
+hipError_t launch_tile(const IndexerLaunch& p, hipStream_t stream) {
+  // chunks of 2048 keys: enough workgroups for 256 CUs at prefill sizes
+  const int kpw = 2048;
+  dim3 grid((p.row_len + kpw - 1) / kpw, (p.T + kTileQ - 1) / kTileQ, p.B);
+  hipLaunchKernelGGL((indexer_tile_kernel<DI, MB, FP8>), grid,
+                     dim3(kTileQ * kWave), 0, stream, p, kpw);
+  return hipGetLastError();
+}
+
 template <int DI, int MB, bool FP8>
 hipError_t launch_stream(const IndexerLaunch& p, hipStream_t stream) {
   // about 8 resident waves per CU on 256 CUs
@@ -226,22 +370,29 @@ hipError_t launch_stream(const IndexerLaunch& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
+template <int DI, int MB, bool FP8>
+hipError_t launch_any(const IndexerLaunch& p, hipStream_t stream) {
+  // several queries per sequence share every key read: tile them
+  return p.T >= kTileQ ? launch_tile<DI, MB, FP8>(p, stream)
+                       : launch_stream<DI, MB, FP8>(p, stream);
+}
+
 }  // namespace
 
 hipError_t launch_indexer(const IndexerLaunch& p, hipStream_t stream) {
   const bool mb1 = p.H_I <= 32;
   if (p.d_I == 128) {
     if (p.keys.fp8)
-      return mb1 ? launch_stream<128, 1, true>(p, stream)
-                 : launch_stream<128, 2, true>(p, stream);
-    return mb1 ? launch_stream<128, 1, false>(p, stream)
-               : launch_stream<128, 2, false>(p, stream);
+      return mb1 ? launch_any<128, 1, true>(p, stream)
+                 : launch_any<128, 2, true>(p, stream);
+    return mb1 ? launch_any<128, 1, false>(p, stream)
+               : launch_any<128, 2, false>(p, stream);
   }
   if (p.keys.fp8)
-    return mb1 ? launch_stream<64, 1, true>(p, stream)
-               : launch_stream<64, 2, true>(p, stream);
-  return mb1 ? launch_stream<64, 1, false>(p, stream)
-             : launch_stream<64, 2, false>(p, stream);
+    return mb1 ? launch_any<64, 1, true>(p, stream)
+               : launch_any<64, 2, true>(p, stream);
+  return mb1 ? launch_any<64, 1, false>(p, stream)
+             : launch_any<64, 2, false>(p, stream);
 }
 
 }  // namespace dsa

@@ -40,6 +40,15 @@ SMALL = {
                                    top_k=128, H=40, H_I=20, d_I=64, seed=105),
     "odd_heads_bf16": wk.scaled(W["decode"], B=2, L=1024, top_k=96, H=100,
                                 H_I=48, seed=106),
+    # query-tiled indexer: a ragged last query tile, unaligned L, FP8 keys
+    "prefill_ragged_fp8": wk.scaled(W["prefill"], T=37, L=1000, first_pos=900,
+                                    top_k=300, H=32, quantized=True, seed=107),
+    "prefill_small_dims": wk.scaled(W["prefill"], T=19, L=700, first_pos=600,
+                                    top_k=128, H=16, H_I=20, d_I=64,
+                                    quantized=True, seed=108),
+    # causal skipping of whole stages, rows shorter than K
+    "prefill_from_start": wk.scaled(W["prefill"], T=130, L=640, first_pos=0,
+                                    top_k=64, H=16, seed=109),
 }
 
 
@@ -144,10 +153,16 @@ def test_full_ragged_paged():
     check_workload(W["ragged"])
 
 
-def test_contiguous_api_unaligned_length():
+@pytest.mark.parametrize("T,first_pos", [(1, None), (21, 950)])
+def test_contiguous_api_unaligned_length(T, first_pos):
     """Separate entry points over a contiguous cache whose length is not a
-    multiple of the 32-key stage (the last stage is clamped in-bounds)."""
-    wl = wk.scaled(W["decode"], B=2, L=1000, top_k=200, H=64, seed=11)
+    multiple of the key stage (the last stage is clamped in-bounds); T=1 runs
+    the streaming indexer, T=21 the query-tiled one with a ragged tile."""
+    if T == 1:
+        wl = wk.scaled(W["decode"], B=2, L=1000, top_k=200, H=64, seed=11)
+    else:
+        wl = wk.scaled(W["prefill"], B=2, T=T, L=1000, first_pos=first_pos,
+                       top_k=200, H=64, seed=12)
     inp = wk.generate(wl)
     d = to_device(inp)
     B, L = 2, 1000
@@ -158,9 +173,12 @@ def test_contiguous_api_unaligned_length():
     idx = dsa.topk(scores, d["q_pos"], wl.top_k)
     out, lse = dsa.sparse_mla_attn(d["q"], kv_c, idx, wl.softmax_scale)
     torch.cuda.synchronize()
-    rows = [(0, 0), (1, 0)]
+    rows = [(b, t) for b in range(B) for t in range(T)]
     sc = scores.cpu().numpy()
     for b, t in rows:
-        assert np.array_equal(sc[b, t].astype(np.float64), ref["scores"][(b, t)])
+        qp = int(inp.q_pos[b, t])
+        want = np.full(L, -np.inf)
+        want[:qp + 1] = ref["scores"][(b, t)]
+        assert np.array_equal(sc[b, t].astype(np.float64), want), (b, t)
     assert_idx_equal(idx.cpu().numpy(), ref["idx"], rows)
     assert_attn_close(out.cpu().numpy(), lse.cpu().numpy(), ref, rows)
