@@ -36,12 +36,20 @@ constexpr int kDigitBits = 13;
 constexpr int kMaxBins = 1 << kDigitBits;
 constexpr int kBinsPerThread = kMaxBins / kThreads;   // 8
 
+constexpr int kSlab = 512;                  // candidates a wave may keep
+constexpr int kMaxWords = 131072 / 32;      // bitmap words of the longest row
+
 struct alignas(16) TopkShared {
-  uint32_t hist[2][kMaxBins];   // stored in descending digit order
+  uint32_t hist[kMaxBins + 4];   // hist[d]: keys with digit d; the slot past
+                                 // the last digit is a sink
+  uint2 slab[kWaves][kSlab];     // per wave: (position, key) of candidates
+  uint32_t gtw[kMaxWords];       // bitmap: selected keys above thr
+  uint32_t eqw[kMaxWords];       // bitmap: keys equal to thr
   uint32_t wmin[kWaves], wmax[kWaves];
   uint32_t wsum[kWaves];
-  uint32_t gcnt[kWaves], ecnt[kWaves];
-  uint32_t pick[4][2];          // per pass: digit, keys in larger digits
+  uint32_t scnt[kWaves];         // candidates per wave
+  uint32_t pick[4][3];           // per pass: digit, keys above, keys in it
+  uint32_t overflow;
 };
 
 template <int CTRL>
@@ -52,6 +60,13 @@ __device__ __forceinline__ uint32_t dpp(uint32_t x) {
 
 __device__ __forceinline__ uint32_t readlane(uint32_t x, int l) {
   return (uint32_t)__builtin_amdgcn_readlane((int)x, l);
+}
+
+// Lane l of `reg` takes the wave-uniform value v (v_writelane_b32).
+__device__ __forceinline__ uint32_t writelane(uint32_t reg, uint32_t v,
+                                              int l) {
+  asm("s_nop 4\n\tv_writelane_b32 %0, %1, %2" : "+v"(reg) : "s"(v), "i"(l));
+  return reg;
 }
 
 // Inclusive prefix sum over the 64 lanes: row_shr steps inside each 16-lane
@@ -80,69 +95,119 @@ __device__ __forceinline__ void wave_minmax(uint32_t& mn, uint32_t& mx) {
            max(readlane(mx, 32), readlane(mx, 48)));
 }
 
+// Keeps the scheduler from hoisting work of later key steps over earlier
+// ones (register pressure: one live temporary per step otherwise).
+#define TOPK_STEP_FENCE(j) \
+  if (((j) & 7) == 7) __builtin_amdgcn_sched_barrier(0)
+
+// Exclusive prefix of v over the block in thread order, and the block
+// total.  Two barriers (the second frees wsum for the next use).
+__device__ __forceinline__ uint32_t block_excl_scan(uint32_t v,
+                                                   struct TopkShared& sm,
+                                                   int tid, int lane,
+                                                   uint32_t& total);
+
+// Per-wave values arr[0..kWaves): the sum over waves before `wave` and the
+// total, with one LDS read per lane (not one register per wave).
+__device__ __forceinline__ void waves_prefix(const uint32_t* arr, int lane,
+                                             int wave, uint32_t& before,
+                                             uint32_t& total) {
+  const uint32_t incl = wave_incl_scan(lane < kWaves ? arr[lane] : 0u, lane);
+  total = readlane(incl, kWaves - 1);
+  before = wave ? readlane(incl, wave - 1) : 0u;
+}
+
 __device__ __forceinline__ uint32_t lanes_below(uint64_t m) {
   return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
                                    __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
 }
 
-// The digit holding the `rem`-th largest key of a histogram of `nb` bins kept
-// in descending digit order (hist[0] = largest digit): thread t owns slots
-// 8t..8t+7.  Returns the digit and the count of keys in larger digits, to
-// every thread.  Two barriers.
+// The digit holding the `rem`-th largest key of a histogram of `nb` bins
+// (hist[d] counts digit d): thread t owns the digits nb-1-8t .. nb-8-8t, in
+// descending order.  Returns the digit, the count of keys in larger digits
+// and the count in the digit itself, to every thread.  Two barriers.
 __device__ __forceinline__ void pick_digit(const uint32_t* hist, int nb,
                                            uint32_t rem, TopkShared& sm,
                                            int pass, int tid, int lane,
                                            int wave, uint32_t& digit,
-                                           uint32_t& above) {
+                                           uint32_t& above, uint32_t& count) {
   uint32_t c[kBinsPerThread];
-  uint32_t s = 0;
-  if (kBinsPerThread * tid < nb) {
-    const uint4 a = reinterpret_cast<const uint4*>(hist)[2 * tid];
-    const uint4 b = reinterpret_cast<const uint4*>(hist)[2 * tid + 1];
-    c[0] = a.x; c[1] = a.y; c[2] = a.z; c[3] = a.w;
-    c[4] = b.x; c[5] = b.y; c[6] = b.z; c[7] = b.w;
+  const int top = nb - kBinsPerThread * tid;   // one past this thread's digits
+  if (top >= kBinsPerThread) {
+    const uint4 a = reinterpret_cast<const uint4*>(hist)[top / 4 - 2];
+    const uint4 b = reinterpret_cast<const uint4*>(hist)[top / 4 - 1];
+    c[0] = b.w; c[1] = b.z; c[2] = b.y; c[3] = b.x;
+    c[4] = a.w; c[5] = a.z; c[6] = a.y; c[7] = a.x;
   } else {
 #pragma unroll
-    for (int u = 0; u < kBinsPerThread; ++u) c[u] = 0;
+    for (int u = 0; u < kBinsPerThread; ++u)
+      c[u] = top - 1 - u >= 0 ? hist[top - 1 - u] : 0u;
   }
+  uint32_t s = 0;
 #pragma unroll
   for (int u = 0; u < kBinsPerThread; ++u) s += c[u];
   const uint32_t incl = wave_incl_scan(s, lane);
   if (lane == kWave - 1) sm.wsum[wave] = incl;
   __syncthreads();
-  uint32_t base = 0;
-#pragma unroll
-  for (int w = 0; w < kWaves; ++w) base += w < wave ? sm.wsum[w] : 0u;
+  uint32_t base, total;
+  waves_prefix(sm.wsum, lane, wave, base, total);
   uint32_t run = base + incl - s;
 #pragma unroll
   for (int u = 0; u < kBinsPerThread; ++u) {
     if (c[u] && run < rem && rem <= run + c[u]) {
-      sm.pick[pass][0] = (uint32_t)(nb - 1 - (kBinsPerThread * tid + u));
+      sm.pick[pass][0] = (uint32_t)(top - 1 - u);
       sm.pick[pass][1] = run;
+      sm.pick[pass][2] = c[u];
     }
     run += c[u];
   }
   __syncthreads();
   digit = sm.pick[pass][0];
   above = sm.pick[pass][1];
+  count = sm.pick[pass][2];
 }
 
-// Keys of one wave step: resident rows hold them in registers, longer rows
-// read them again from the score row.  Positions past the row's candidates
-// get key 0, which no score maps to: it is below every window and every
-// threshold, so no pass needs a separate validity test.
+__device__ __forceinline__ uint32_t block_excl_scan(uint32_t v,
+                                                   TopkShared& sm, int tid,
+                                                   int lane, uint32_t& total) {
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const uint32_t incl = wave_incl_scan(v, lane);
+  if (lane == kWave - 1) sm.wsum[wave] = incl;
+  __syncthreads();
+  uint32_t base;
+  waves_prefix(sm.wsum, lane, wave, base, total);
+  __syncthreads();
+  return base + incl - v;
+}
+
+// Keys of one wave step.  Once the row's smallest key kmin is known they
+// are kept relative to it (r = key - kmin, so a pass's digit is a shift of
+// r); resident rows hold them in registers, longer rows read them again
+// from the score row.  Lanes past the row's n candidates get r = 0: they
+// tie with the smallest key and sit after every candidate, so the
+// selection (largest keys, then lowest positions) never reaches them
+// (K <= n) and no pass needs a validity test.
 template <int KPT, bool RES>
 struct RowKeys {
   uint32_t k[RES ? KPT : 1];
   const float* row;
-  int n, base;   // candidate count, this lane's position at step 0
+  int n;            // candidate count
+  int wbase;        // first position of the wave (uniform)
+  int lane;
+  uint32_t kmin;
 
-  __device__ __forceinline__ uint32_t at(int j) const {
+  // compares the lane against a uniform bound: no per-step registers
+  __device__ __forceinline__ bool valid(int j) const {
+    return lane < n - wbase - j * kWave;
+  }
+  __device__ __forceinline__ int pos(int j) const {
+    return wbase + j * kWave + lane;
+  }
+  __device__ __forceinline__ uint32_t rel(int j) const {
     if constexpr (RES) {
       return k[j];
     } else {
-      const int p = base + j * kWave;
-      return p < n ? score_key(row[p]) : 0u;
+      return valid(j) ? score_key(row[pos(j)]) - kmin : 0u;
     }
   }
 };
@@ -168,45 +233,48 @@ __global__ __launch_bounds__(kThreads, 1) void topk_kernel(TopkLaunch p) {
   RowKeys<KPT, RES> keys;
   keys.row = p.scores + (int64_t)r * p.L;
   keys.n = n;
-  keys.base = wave * KPT * kWave + lane;
+  keys.wbase = wave * KPT * kWave;
+  keys.lane = lane;
+  keys.kmin = 0;
   // steps of this wave that hold any candidate (wave-uniform)
   const int nsteps =
       min(KPT, max(0, (n - wave * KPT * kWave + kWave - 1) / kWave));
 
-  // ---- load; min / max over the candidates; clear both histograms
+  // ---- load; min / max over the candidates; clear histogram and bitmap
   uint32_t mn = 0xffffffffu, mx = 0u;   // min taken over key - 1
   if constexpr (RES) {
-    if (wave * KPT * kWave + KPT * kWave <= n) {   // all candidates
-      float v[KPT];
+    // buffer loads bounded by the candidate count: positions past n read 0
+    // without branches, and all loads share one offset register
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float*>(keys.row), 0, n * 4, 0x00020000);
 #pragma unroll
-      for (int j = 0; j < KPT; ++j) v[j] = keys.row[keys.base + j * kWave];
-#pragma unroll
-      for (int j = 0; j < KPT; ++j) keys.k[j] = score_key(v[j]);
-    } else {
-#pragma unroll
-      for (int j = 0; j < KPT; ++j) {
-        const int pp = keys.base + j * kWave;
-        keys.k[j] = pp < n ? score_key(keys.row[pp]) : 0u;
-      }
-    }
+    for (int j = 0; j < KPT; ++j)
+      keys.k[j] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(
+          rs, (keys.wbase + lane) * 4, j * kWave * 4, 0);
+    // keys of candidates are >= 1 (NaN maps to 1): 0 marks a lane past n
 #pragma unroll
     for (int j = 0; j < KPT; ++j) {
+      keys.k[j] = keys.valid(j)
+                      ? score_key(__builtin_bit_cast(float, keys.k[j])) : 0u;
       mn = min(mn, keys.k[j] - 1u);
       mx = max(mx, keys.k[j]);
     }
   } else {
 #pragma unroll 8
     for (int j = 0; j < nsteps; ++j) {
-      const uint32_t k = keys.at(j);
+      const uint32_t k = keys.rel(j);   // kmin is still 0: absolute, 0 past n
       mn = min(mn, k - 1u);
       mx = max(mx, k);
     }
   }
   {
-    uint4* h = reinterpret_cast<uint4*>(&sm.hist[0][0]);
-#pragma unroll
-    for (int u = 0; u < 2 * kMaxBins / 4 / kThreads; ++u)
-      h[u * kThreads + tid] = make_uint4(0, 0, 0, 0);
+    uint4* h = reinterpret_cast<uint4*>(sm.hist);
+    for (int i = tid; i < (kMaxBins + 4) / 4; i += kThreads)
+      h[i] = make_uint4(0, 0, 0, 0);
+    uint4* e = reinterpret_cast<uint4*>(sm.eqw);
+    for (int i = tid; i < kMaxWords / 4; i += kThreads)
+      e[i] = make_uint4(0, 0, 0, 0);
+    if (tid == 0) sm.overflow = 0u;
   }
   wave_minmax(mn, mx);
   if (lane == 0) {
@@ -214,102 +282,249 @@ __global__ __launch_bounds__(kThreads, 1) void topk_kernel(TopkLaunch p) {
     sm.wmax[wave] = mx;
   }
   __syncthreads();
-  uint32_t kmin = 0xffffffffu, kmax = 0u;
+  uint32_t kmin = lane < kWaves ? sm.wmin[lane] : 0xffffffffu;
+  uint32_t kmax = lane < kWaves ? sm.wmax[lane] : 0u;
+  wave_minmax(kmin, kmax);
+  kmin += 1u;   // n >= 2 here, so some lane holds a candidate
+  keys.kmin = kmin;
+  if constexpr (RES) {
 #pragma unroll
-  for (int w = 0; w < kWaves; ++w) {
-    kmin = min(kmin, sm.wmin[w]);
-    kmax = max(kmax, sm.wmax[w]);
+    for (int j = 0; j < KPT; ++j)
+      keys.k[j] = keys.k[j] ? keys.k[j] - kmin : 0u;
   }
-  kmin += 1u;   // n >= 2 here, so some key is a candidate (>= 1)
 
-  // ---- digit passes over the window [lo, lo + 2^sh) holding the K-th key
-  uint32_t lo = kmin;
+  // ---- first digit over all keys: digit(r) = r >> nsh, r <= range
   const uint32_t range = kmax - kmin;
-  int sh = range ? 32 - __builtin_clz(range) : 0;   // range < 2^sh
+  const int sh0 = range ? 32 - __builtin_clz(range) : 0;   // range < 2^sh0
   uint32_t rem = (uint32_t)kk;
-  for (int pass = 0; sh > 0; ++pass) {
-    const int np = (sh + kDigitBits - 1) / kDigitBits;
-    const int nbits = (sh + np - 1) / np;
-    const int nsh = sh - nbits;
+  uint32_t d0 = 0, cnt0 = (uint32_t)n;   // all keys equal: one digit
+  int nsh = 0;
+  if (sh0 > 0) {
+    const int np = (sh0 + kDigitBits - 1) / kDigitBits;
+    const int nbits = (sh0 + np - 1) / np;
+    nsh = sh0 - nbits;
     const int nb = 1 << nbits;
-    uint32_t* hist = sm.hist[pass & 1];
-    if (pass >= 1) {   // the other buffer feeds the pass after this one
-      uint4* h = reinterpret_cast<uint4*>(sm.hist[(pass + 1) & 1]);
-#pragma unroll
-      for (int u = 0; u < kMaxBins / 4 / kThreads; ++u)
-        h[u * kThreads + tid] = make_uint4(0, 0, 0, 0);
-    }
-    // key 0 (no position) is below every window: lo >= kmin >= 1
-    const uint64_t win = 1ull << sh;
-    const auto count = [&](uint32_t k) {
-      const uint32_t off = k - lo;
-      if ((uint64_t)off < win && k >= lo)
-        atomicAdd(&hist[nb - 1 - (int)(off >> nsh)], 1u);
+    const auto count = [&](int j, uint32_t rk) {
+      (void)j;
+      atomicAdd(&sm.hist[rk >> nsh], 1u);   // rk <= range < 2^sh0
     };
     if constexpr (RES) {
 #pragma unroll
-      for (int j = 0; j < KPT; ++j) count(keys.k[j]);
+      for (int j = 0; j < KPT; ++j) {
+        count(j, keys.k[j]);
+        TOPK_STEP_FENCE(j);
+      }
     } else {
 #pragma unroll 8
-      for (int j = 0; j < nsteps; ++j) count(keys.at(j));
+      for (int j = 0; j < nsteps; ++j) count(j, keys.rel(j));
     }
     __syncthreads();
-    uint32_t d, above;
-    pick_digit(hist, nb, rem, sm, pass, tid, lane, wave, d, above);
-    lo += d << nsh;
+    uint32_t above;
+    pick_digit(sm.hist, nb, rem, sm, 0, tid, lane, wave, d0, above, cnt0);
     rem -= above;
-    sh = nsh;
   }
-  const uint32_t thr = lo;     // >= 1, so key 0 never counts below
-  const uint32_t need = rem;   // keys equal to thr that are taken
+  // digit d0 spans relative keys [blo, bhi]
+  const uint32_t blo = d0 << nsh;
+  const uint32_t bhi = blo | ((1u << nsh) - 1u);
 
-  // ---- per-wave counts of keys > thr and == thr
-  uint32_t gc = 0, ec = 0;
-  if constexpr (RES) {
+  // ---- sweep: bitmap of keys in larger digits; keys in digit d0 are
+  // final (nsh == 0: they all equal the threshold) or go to the wave's
+  // candidate list, in position order
+  uint32_t ns = 0;
+  // resident rows gather the wave's 2*KPT mask words in registers (word i
+  // in lane i % 64 of register i / 64) and store them once
+  constexpr int kMaskRegs = RES ? (2 * KPT + kWave - 1) / kWave : 1;
+  uint32_t gwr[kMaskRegs], ewr[kMaskRegs];
 #pragma unroll
-    for (int j = 0; j < KPT; ++j) {
-      gc += __builtin_popcountll(__ballot(keys.k[j] > thr));
-      ec += __builtin_popcountll(__ballot(keys.k[j] == thr));
+  for (int i = 0; i < kMaskRegs; ++i) gwr[i] = ewr[i] = 0u;
+  const auto sweep = [&](int j, uint32_t rk) {
+    const bool in = rk >= blo && rk <= bhi;
+    const uint64_t g = __ballot(rk > bhi);
+    const uint64_t c = __ballot(in);
+    if constexpr (RES) {
+      const int i0 = (2 * j) / kWave, l0 = (2 * j) % kWave;
+      gwr[i0] = writelane(gwr[i0], (uint32_t)g, l0);
+      gwr[i0] = writelane(gwr[i0], (uint32_t)(g >> 32), l0 + 1);
+      if (nsh == 0) {
+        ewr[i0] = writelane(ewr[i0], (uint32_t)c, l0);
+        ewr[i0] = writelane(ewr[i0], (uint32_t)(c >> 32), l0 + 1);
+      }
+    } else {
+      const int wd = 2 * (wave * KPT + j);
+      if (lane == 0) {
+        sm.gtw[wd] = (uint32_t)g;
+        sm.gtw[wd + 1] = (uint32_t)(g >> 32);
+        if (nsh == 0) {
+          sm.eqw[wd] = (uint32_t)c;
+          sm.eqw[wd + 1] = (uint32_t)(c >> 32);
+        }
+      }
     }
-  } else {
-    for (int j = 0; j < nsteps; ++j) {
-      const uint32_t k = keys.at(j);
-      gc += __builtin_popcountll(__ballot(k > thr));
-      ec += __builtin_popcountll(__ballot(k == thr));
+    if (nsh != 0 && c != 0ull) {
+      const uint32_t at = ns + lanes_below(c);
+      if (in && at < (uint32_t)kSlab)
+        sm.slab[wave][at] = make_uint2((uint32_t)keys.pos(j), rk);
+      ns += __builtin_popcountll(c);
     }
-  }
-  if (lane == 0) {
-    sm.gcnt[wave] = gc;
-    sm.ecnt[wave] = ec;
-  }
-  __syncthreads();
-  // equal keys before this wave, and its first output slot
-  uint32_t erun = 0, slot = 0;
-#pragma unroll
-  for (int w = 0; w < kWaves; ++w) {
-    if (w < wave) {
-      const uint32_t e = sm.ecnt[w];
-      const uint32_t take = erun >= need ? 0u : min(e, need - erun);
-      slot += sm.gcnt[w] + take;
-      erun += e;
-    }
-  }
-
-  // ---- emit: keys > thr, and equal keys while fewer than `need` precede
-  const auto emit = [&](int j, uint32_t k) {
-    const uint64_t e = __ballot(k == thr);
-    const bool sel = k > thr || (k == thr && erun + lanes_below(e) < need);
-    const uint64_t sm_ = __ballot(sel);
-    const uint32_t o = slot + lanes_below(sm_);
-    if (sel && o < (uint32_t)kk) out[o] = keys.base + j * kWave;
-    slot += __builtin_popcountll(sm_);
-    erun += __builtin_popcountll(e);
   };
   if constexpr (RES) {
 #pragma unroll
-    for (int j = 0; j < KPT; ++j) emit(j, keys.k[j]);
+    for (int j = 0; j < KPT; ++j) {
+      sweep(j, keys.k[j]);
+      TOPK_STEP_FENCE(j);
+    }
   } else {
-    for (int j = 0; j < nsteps; ++j) emit(j, keys.at(j));
+    for (int j = 0; j < nsteps; ++j) sweep(j, keys.rel(j));
+  }
+  if constexpr (RES) {
+#pragma unroll
+    for (int i = 0; i < kMaskRegs; ++i) {
+      const int wd = i * kWave + lane;
+      if (wd < 2 * KPT) {
+        sm.gtw[2 * wave * KPT + wd] = gwr[i];
+        if (nsh == 0) sm.eqw[2 * wave * KPT + wd] = ewr[i];
+      }
+    }
+  }
+  if (lane == 0) {
+    sm.scnt[wave] = min(ns, (uint32_t)kSlab);
+    if (ns > (uint32_t)kSlab) sm.overflow = 1u;
+  }
+  __syncthreads();
+
+  uint32_t thr = blo;            // relative threshold
+  uint32_t eq_total = cnt0;
+  if (nsh > 0) {
+    // ---- the remaining digits, on the candidates only (or, if a wave's
+    // list overflowed, on all keys again)
+    const bool ovf = sm.overflow != 0u;
+    uint32_t lo = blo;
+    int sh = nsh;
+    for (int pass = 1; sh > 0; ++pass) {
+      const int np = (sh + kDigitBits - 1) / kDigitBits;
+      const int nbits = (sh + np - 1) / np;
+      const int psh = sh - nbits;
+      const int nb = 1 << nbits;
+      {
+        uint4* h = reinterpret_cast<uint4*>(sm.hist);
+        for (int i = tid; i < kMaxBins / 4; i += kThreads)
+          h[i] = make_uint4(0, 0, 0, 0);
+      }
+      __syncthreads();
+      const uint32_t win = 1u << sh;   // window [lo, lo + 2^sh)
+      if (!ovf) {   // each wave counts its own candidates
+        const int nc = (int)sm.scnt[wave];
+        for (int e = lane; e < nc; e += kWave) {
+          const uint32_t rk = sm.slab[wave][e].y;
+          if (rk >= lo && rk - lo < win)
+            atomicAdd(&sm.hist[(rk - lo) >> psh], 1u);
+        }
+      } else {
+        const auto count = [&](int j, uint32_t rk) {
+          (void)j;
+          const bool in = rk >= lo && rk - lo < win;
+          if (__ballot(in) != 0ull && in)
+            atomicAdd(&sm.hist[(rk - lo) >> psh], 1u);
+        };
+        if constexpr (RES) {
+#pragma unroll
+          for (int j = 0; j < KPT; ++j) {
+            count(j, keys.k[j]);
+            TOPK_STEP_FENCE(j);
+          }
+        } else {
+          for (int j = 0; j < nsteps; ++j) count(j, keys.rel(j));
+        }
+      }
+      __syncthreads();
+      uint32_t d, above, cnt;
+      pick_digit(sm.hist, nb, rem, sm, pass, tid, lane, wave, d, above, cnt);
+      lo += d << psh;
+      rem -= above;
+      sh = psh;
+      eq_total = cnt;
+    }
+    thr = lo;
+    // ---- keys of digit d0 above thr join the bitmap; those equal to thr
+    // form the equal-key bitmap
+    if (!ovf) {
+      const int nc = (int)sm.scnt[wave];
+      for (int e = lane; e < nc; e += kWave) {
+        const uint2 c = sm.slab[wave][e];
+        if (c.y > thr) atomicOr(&sm.gtw[c.x >> 5], 1u << (c.x & 31));
+        else if (c.y == thr) atomicOr(&sm.eqw[c.x >> 5], 1u << (c.x & 31));
+      }
+    } else {
+      const auto marks = [&](int j, uint32_t rk) {
+        const uint64_t g = __ballot(rk > thr);
+        const uint64_t e = __ballot(rk == thr);
+        const int wd = 2 * (wave * KPT + j);
+        if (lane == 0) {
+          sm.gtw[wd] = (uint32_t)g;
+          sm.gtw[wd + 1] = (uint32_t)(g >> 32);
+          sm.eqw[wd] = (uint32_t)e;
+          sm.eqw[wd + 1] = (uint32_t)(e >> 32);
+        }
+      };
+      if constexpr (RES) {
+#pragma unroll
+        for (int j = 0; j < KPT; ++j) {
+          marks(j, keys.k[j]);
+          TOPK_STEP_FENCE(j);
+        }
+      } else {
+        for (int j = 0; j < nsteps; ++j) marks(j, keys.rel(j));
+      }
+    }
+    __syncthreads();
+  }
+  const uint32_t need = rem;   // keys equal to thr that are taken
+
+  // ---- thread t owns bitmap words [t*q, t*q + q): keep the first `need`
+  // equal keys in position order, then emit in ascending order
+  const int nw = (n + 31) / 32;
+  const int q = (nw + kThreads - 1) / kThreads;
+  const int w0 = tid * q, w1 = min(nw, w0 + q);
+  const bool ties = need < eq_total;   // keep only the lowest equal keys
+  uint32_t ebefore = 0;
+  if (ties) {
+    uint32_t ecount = 0;
+    for (int w = w0; w < w1; ++w) ecount += __builtin_popcount(sm.eqw[w]);
+    uint32_t total;
+    ebefore = block_excl_scan(ecount, sm, tid, lane, total);
+  }
+  uint32_t scount = 0;
+  for (int w = w0; w < w1; ++w) {
+    uint32_t e = sm.eqw[w];
+    if (ties) {
+      const uint32_t ce = __builtin_popcount(e);
+      if (ebefore >= need) {
+        e = 0u;
+      } else if (ebefore + ce > need) {
+        uint32_t keep = need - ebefore, m = e;   // the lowest `keep` bits
+        e = 0u;
+        while (keep--) {
+          const uint32_t lowbit = m & (0u - m);
+          e |= lowbit;
+          m ^= lowbit;
+        }
+      }
+      ebefore += ce;
+    }
+    const uint32_t sel = sm.gtw[w] | e;
+    sm.eqw[w] = sel;
+    scount += __builtin_popcount(sel);
+  }
+  uint32_t stotal;
+  uint32_t slot = block_excl_scan(scount, sm, tid, lane, stotal);
+  for (int w = w0; w < w1; ++w) {
+    uint32_t m = sm.eqw[w];
+    while (m) {
+      const int bit = __builtin_ctz(m);
+      m &= m - 1;
+      if (slot < (uint32_t)kk) out[slot] = w * 32 + bit;
+      ++slot;
+    }
   }
 }
 
