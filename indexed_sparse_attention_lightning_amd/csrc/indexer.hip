@@ -190,21 +190,24 @@ __global__ __launch_bounds__(256, 2) void indexer_stream_kernel(
                      lane, a, wv);
 
   uint4* tile = lds[wave];
+  // Every iteration issues the same loads and stores (the tail re-reads the
+  // last stage, an L2 hit, and its scores are masked), so the compiler can
+  // count them and wait only for the stage it consumes.
+  const int last = nsub - 1;
   Stage<DI, FP8> s0, s1;
   stage_load<DI, FP8>(s0, p.keys, b, k0, lane);
-  if (nsub > 1) stage_load<DI, FP8>(s1, p.keys, b, k0 + kSub, lane);
+  stage_load<DI, FP8>(s1, p.keys, b, k0 + min(1, last) * kSub, lane);
   for (int i = 0; i < nsub; i += 2) {
     stage_store<DI, FP8>(s0, tile, lane);
-    if (i + 2 < nsub) stage_load<DI, FP8>(s0, p.keys, b, k0 + (i + 2) * kSub, lane);
+    stage_load<DI, FP8>(s0, p.keys, b, k0 + min(i + 2, last) * kSub, lane);
     {
       const float sc = tile_scores<DI, MB>(tile, a, wv, lane);
       const int s = k0 + i * kSub + (lane & 31);
       if (lane < 32 && s < kend) srow[s] = sc + 0.0f;
     }
-    if (i + 1 < nsub) {
-      stage_store<DI, FP8>(s1, tile, lane);
-      if (i + 3 < nsub)
-        stage_load<DI, FP8>(s1, p.keys, b, k0 + (i + 3) * kSub, lane);
+    stage_store<DI, FP8>(s1, tile, lane);
+    stage_load<DI, FP8>(s1, p.keys, b, k0 + min(i + 3, last) * kSub, lane);
+    {
       const float sc = tile_scores<DI, MB>(tile, a, wv, lane);
       const int s = k0 + (i + 1) * kSub + (lane & 31);
       if (lane < 32 && s < kend) srow[s] = sc + 0.0f;
