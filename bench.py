@@ -27,6 +27,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBPS = 8000.0
+PEAK_BF16_TFLOPS = 2500.0   # dense bf16 matrix-core peak of one MI355X
 METRIC = ("DSA decode tokens/sec at B=32,L=32K,k=2048; achieved HBM GB/s vs "
           "peak")
 REPLICAS = 3
@@ -50,7 +51,10 @@ def indexer_bytes(wl, L):
     return wl.B * wl.T * (L * wl.d_I * 2 + wl.H_I * wl.d_I * 2 + wl.H_I * 4)
 
 
-def time_loop(fn, steps, warmup, stream):
+def time_loop(fn, steps, warmup, stream, per_call=False):
+    """Mean ms per call over `steps` back-to-back calls on `stream` (events
+    around the whole loop); with per_call also the 10th/50th/90th percentile
+    of the calls, each bracketed by its own event pair."""
     import torch
     for i in range(warmup):
         fn(i)
@@ -62,7 +66,20 @@ def time_loop(fn, steps, warmup, stream):
         fn(i)
     end.record(stream)
     torch.cuda.synchronize()
-    return start.elapsed_time(end) / steps   # ms per call
+    mean = start.elapsed_time(end) / steps
+    if not per_call:
+        return mean
+    ev = [(torch.cuda.Event(enable_timing=True),
+           torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for i in range(steps):
+        ev[i][0].record(stream)
+        fn(i)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    t = np.array([a.elapsed_time(b) for a, b in ev])
+    return mean, {"p10": round(float(np.percentile(t, 10)), 5),
+                  "p50": round(float(np.percentile(t, 50)), 5),
+                  "p90": round(float(np.percentile(t, 90)), 5)}
 
 
 def traffic_record(kernel_src):
@@ -80,25 +97,79 @@ def traffic_record(kernel_src):
 
 def cpu_baseline(inp, budget_s=12.0):
     """The CPU oracle, as it stands, on whole decode rows of the same
-    workload until about `budget_s` seconds of work (at least one row)."""
+    workload (every row of the batch, in passes over it) until about
+    `budget_s` seconds of work."""
     import oracle
     try:
         from threadpoolctl import threadpool_info
         cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     except Exception:  # pragma: no cover
         cores = 1
-    rows, t0 = [], time.perf_counter()
-    for b in range(inp.wl.B):
-        oracle.decode_path(inp, rows=[(b, 0)])
-        rows.append(b)
+    rows, t0 = 0, time.perf_counter()
+    while True:
+        for b in range(inp.wl.B):
+            oracle.decode_path(inp, rows=[(b, 0)])
+            rows += 1
+            if time.perf_counter() - t0 > budget_s:
+                break
         if time.perf_counter() - t0 > budget_s:
             break
     dt = time.perf_counter() - t0
-    return {"value": len(rows) / dt, "unit": "tokens/s", "cores": cores,
+    return {"value": rows / dt, "unit": "tokens/s", "cores": cores,
             "kind": "oracle",
-            "sample": f"{len(rows)} of {inp.wl.B} decode tokens (full "
-                      f"indexer over {inp.L} keys, top-k, attention), "
-                      f"{dt:.1f} s"}
+            "sample": f"{rows} decode tokens ({rows / inp.wl.B:.1f} passes "
+                      f"over the batch of {inp.wl.B}; full indexer over "
+                      f"{inp.L} keys, top-k, attention), {dt:.1f} s"}
+
+
+def prefill_kernels(stream, steps=5, warmup=2):
+    """The prefill chunk (4096 queries at positions 61440..65535 of a
+    65536-token bf16 context, 64 indexer heads x 128, top_k 2048, 128 MLA
+    heads) through the three separate entry points, each timed on its own.
+    The indexer is the dense contraction here: its rate is reported against
+    the bf16 matrix-core peak, with the causal (query, key) pairs as work."""
+    import torch
+    import indexed_sparse_attention_lightning_amd as dsa
+    import workloads as wk
+    from workloads.device import to_device
+
+    wl = wk.WORKLOADS["prefill"]
+    inp = wk.generate(wl)
+    d = to_device(inp)
+    L = inp.L
+    scores = torch.empty((1, wl.T, L), device="cuda")
+    idx = torch.empty((1, wl.T, wl.top_k), dtype=torch.int32, device="cuda")
+    out = torch.empty((1, wl.T, wl.H, 512), device="cuda")
+    lse = torch.empty((1, wl.T, wl.H), device="cuda")
+    ws = torch.empty(max(1, dsa.workspace_size(dsa.OP_SPARSE_MLA, 1, wl.T, L,
+                                               wl.H, wl.top_k)),
+                     dtype=torch.uint8, device="cuda")
+    ms_i = time_loop(lambda i: dsa.indexer_scores(
+        d["q_idx"], d["w"], d["kidx_c"], d["q_pos"], out=scores),
+        steps, warmup, stream)
+    ms_t = time_loop(lambda i: dsa.topk(scores, d["q_pos"], wl.top_k,
+                                        out=idx), steps, warmup, stream)
+    ms_a = time_loop(lambda i: dsa.sparse_mla_attn(
+        d["q"], d["kv_c"], idx, wl.softmax_scale, out=out, lse=lse,
+        workspace=ws), steps, warmup, stream)
+    pairs = int(np.sum(inp.q_pos.astype(np.int64) + 1))
+    idx_flop = pairs * 2 * wl.H_I * wl.d_I
+    attn_flop = wl.T * wl.H * wl.top_k * 2 * (576 + 512)
+    idx_tf = idx_flop / (ms_i * 1e-3) / 1e12
+    attn_tf = attn_flop / (ms_a * 1e-3) / 1e12
+    return {
+        "workload": "prefill chunk: 4096 queries at 61440..65535 of a 65536 "
+                    "bf16 context, top_k 2048",
+        "indexer_ms": round(ms_i, 4), "topk_ms": round(ms_t, 4),
+        "sparse_mla_attn_ms": round(ms_a, 4),
+        "indexer_roofline": {"bound": "mfma", "achieved": round(idx_tf, 1),
+                             "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                             "frac": round(idx_tf / PEAK_BF16_TFLOPS, 4),
+                             "algorithmic_flop": idx_flop},
+        "attn_tflops": round(attn_tf, 1),
+        "attn_frac_of_bf16_peak": round(attn_tf / PEAK_BF16_TFLOPS, 4),
+        "tokens_per_s": round(wl.T / ((ms_i + ms_t + ms_a) * 1e-3), 1),
+    }
 
 
 def main(argv=None):
@@ -107,6 +178,8 @@ def main(argv=None):
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true",
+                    help="skip the prefill-chunk kernel timings")
     ap.add_argument("--kernels-only", action="store_true",
                     help="run one 256 MiB device copy (counter calibration) "
                          "and one decode step, then exit (for rocprofv3 "
@@ -165,7 +238,8 @@ def main(argv=None):
         print(json.dumps({"kernels_only": True, "copy_bytes": 1 << 28}))
         return 0
 
-    ms = time_loop(step, args.steps, args.warmup, stream)
+    ms, ms_pct = time_loop(step, args.steps, args.warmup, stream,
+                           per_call=True)
 
     # per-kernel timing of the three stages through the separate entry points
     scores = [torch.empty((wl.B, 1, L), device="cuda") for _ in range(REPLICAS)]
@@ -216,6 +290,7 @@ def main(argv=None):
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms, 5),
+        "ms_per_step_percentiles": ms_pct,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -242,6 +317,9 @@ def main(argv=None):
             "traffic": traffic_record(src),
             "algorithmic_bytes_per_launch": ib},
     }
+    del reps, caches, outs, scores
+    if not args.no_prefill:
+        line["prefill"] = prefill_kernels(stream)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(inp)
     print(json.dumps(line), flush=True)
