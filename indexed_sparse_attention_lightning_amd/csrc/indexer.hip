@@ -33,6 +33,7 @@ namespace {
 
 constexpr int kSub = 32;      // keys per stage == MFMA N
 constexpr int kWavesPerWG = 4;
+constexpr int kFlush = 512;   // scores a wave buffers in LDS between writes
 
 template <int DI>
 struct KeyLayout {
@@ -167,6 +168,9 @@ __global__ __launch_bounds__(256, 2) void indexer_stream_kernel(
     IndexerLaunch p, int kpw) {
   using KL = KeyLayout<DI>;
   __shared__ uint4 lds[kWavesPerWG][KL::kTileBytes / 16];
+  // scores leave in bursts of up to kFlush: a steady trickle of small
+  // writes into the key stream costs read bandwidth
+  __shared__ float sbuf[kWavesPerWG][kFlush];
   const int lane = lane_id();
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int b = blockIdx.z, t = blockIdx.y;
@@ -197,22 +201,28 @@ __global__ __launch_bounds__(256, 2) void indexer_stream_kernel(
   Stage<DI, FP8> s0, s1;
   stage_load<DI, FP8>(s0, p.keys, b, k0, lane);
   stage_load<DI, FP8>(s1, p.keys, b, k0 + min(1, last) * kSub, lane);
+  float* sb = sbuf[wave];
+  const auto flush = [&](int from, int to) {   // positions [from, to)
+    for (int s = from + lane; s < to; s += kWave) srow[s] = sb[(s - k0) % kFlush];
+  };
   for (int i = 0; i < nsub; i += 2) {
     stage_store<DI, FP8>(s0, tile, lane);
     stage_load<DI, FP8>(s0, p.keys, b, k0 + min(i + 2, last) * kSub, lane);
     {
       const float sc = tile_scores<DI, MB>(tile, a, wv, lane);
-      const int s = k0 + i * kSub + (lane & 31);
-      if (lane < 32 && s < kend) srow[s] = sc + 0.0f;
+      if (lane < 32) sb[(i * kSub + lane) % kFlush] = sc + 0.0f;
     }
     stage_store<DI, FP8>(s1, tile, lane);
     stage_load<DI, FP8>(s1, p.keys, b, k0 + min(i + 3, last) * kSub, lane);
     {
       const float sc = tile_scores<DI, MB>(tile, a, wv, lane);
-      const int s = k0 + (i + 1) * kSub + (lane & 31);
-      if (lane < 32 && s < kend) srow[s] = sc + 0.0f;
+      if (lane < 32) sb[((i + 1) * kSub + lane) % kFlush] = sc + 0.0f;
     }
+    if ((i + 2) * kSub % kFlush == 0 && i + 2 < nsub)   // a full buffer
+      flush(k0 + (i + 2) * kSub - kFlush, k0 + (i + 2) * kSub);
   }
+  const int done = (nsub - 1) / (kFlush / kSub) * kFlush;   // flushed so far
+  flush(k0 + done, kend);
 }
 
 // ---------------------------------------------------------------- prefill

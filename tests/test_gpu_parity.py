@@ -182,3 +182,30 @@ def test_contiguous_api_unaligned_length(T, first_pos):
         assert np.array_equal(sc[b, t].astype(np.float64), want), (b, t)
     assert_idx_equal(idx.cpu().numpy(), ref["idx"], rows)
     assert_attn_close(out.cpu().numpy(), lse.cpu().numpy(), ref, rows)
+
+
+def test_indexer_long_wave_ranges():
+    """Many long rows: each wave scores more than one LDS score buffer
+    (several flushes per wave) and a tail shorter than a stage; queries at
+    varied positions mask part of some waves' ranges.  Scores compared
+    exactly with the oracle on sampled rows."""
+    rng = np.random.default_rng(21)
+    B, L, H_I, d_I = 40, 40001, 64, 128
+    q_i = rng.integers(-4, 5, (B, 1, H_I, d_I)).astype(np.float32)
+    k_i = rng.integers(-4, 5, (B, L, d_I)).astype(np.float32)
+    w = np.ldexp(1.0, -rng.integers(0, 4, (B, 1, H_I))).astype(np.float32)
+    q_pos = np.full((B, 1), L - 1, dtype=np.int32)
+    q_pos[1, 0], q_pos[2, 0], q_pos[3, 0] = 12345, 0, 33000
+    to_bf16 = lambda x: torch.from_numpy(
+        wk.f32_to_bf16_bits(x).view(np.int16)).view(torch.bfloat16)
+    scores = dsa.indexer_scores(to_bf16(q_i).cuda(), torch.from_numpy(w).cuda(),
+                                to_bf16(k_i).cuda(),
+                                torch.from_numpy(q_pos).cuda())
+    torch.cuda.synchronize()
+    sc = scores.cpu().numpy()
+    for b in (0, 1, 2, 3, 39):
+        qp = int(q_pos[b, 0])
+        want = np.full(L, -np.inf)
+        want[:qp + 1] = oracle.indexer_scores_row(q_i[b, 0], w[b, 0],
+                                                  k_i[b, :qp + 1])
+        assert np.array_equal(sc[b, 0].astype(np.float64), want), b
