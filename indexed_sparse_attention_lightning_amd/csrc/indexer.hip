@@ -162,10 +162,13 @@ __device__ __forceinline__ void load_query(const uint16_t* q_idx,
 }
 
 // Streaming indexer: grid (chunks, T, B); each wave scores `kpw`
-// consecutive positions of one query.
+// consecutive positions of one query.  With `xcd_rows` (a row count that is
+// a multiple of 8) the linear workgroup id, which the dispatcher deals to the
+// 8 XCDs round-robin, is remapped so that every chunk of query row r runs on
+// XCD r % 8: the row's query, weights and score lines stay in one L2.
 template <int DI, int MB, bool FP8>
 __global__ __launch_bounds__(256, 2) void indexer_stream_kernel(
-    IndexerLaunch p, int kpw) {
+    IndexerLaunch p, int kpw, int xcd_rows) {
   using KL = KeyLayout<DI>;
   __shared__ uint4 lds[kWavesPerWG][KL::kTileBytes / 16];
   // scores leave in bursts of up to kFlush: a steady trickle of small
@@ -173,8 +176,16 @@ __global__ __launch_bounds__(256, 2) void indexer_stream_kernel(
   __shared__ float sbuf[kWavesPerWG][kFlush];
   const int lane = lane_id();
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-  const int b = blockIdx.z, t = blockIdx.y;
-  const int k0 = (blockIdx.x * kWavesPerWG + wave) * kpw;
+  int b = blockIdx.z, t = blockIdx.y, chunk = blockIdx.x;
+  if (xcd_rows) {
+    const int lin = (blockIdx.z * gridDim.y + blockIdx.y) * gridDim.x + blockIdx.x;
+    const int slot = lin >> 3;
+    const int row = (slot / gridDim.x) * 8 + (lin & 7);
+    chunk = slot % gridDim.x;
+    b = row / p.T;
+    t = row % p.T;
+  }
+  const int k0 = (chunk * kWavesPerWG + wave) * kpw;
   if (k0 >= p.row_len) return;
   const int k1 = min(k0 + kpw, p.row_len);
   const int qpos = __builtin_amdgcn_readfirstlane(query_pos(p.qp, b, t));
@@ -378,8 +389,9 @@ hipError_t launch_stream(const IndexerLaunch& p, hipStream_t stream) {
   kpw = kpw < 64 ? 64 : (kpw > 4096 ? 4096 : kpw);
   const int per_wg = (int)kpw * kWavesPerWG;
   dim3 grid((p.row_len + per_wg - 1) / per_wg, p.T, p.B);
+  const int xcd_rows = ((p.B * p.T) & 7) == 0 ? 1 : 0;
   hipLaunchKernelGGL((indexer_stream_kernel<DI, MB, FP8>), grid, dim3(256), 0,
-                     stream, p, (int)kpw);
+                     stream, p, (int)kpw, xcd_rows);
   return hipGetLastError();
 }
 
