@@ -41,6 +41,7 @@ constexpr int kCodeTileSlots = kRowsT * kCodeSlotsRow;  // 1152
 constexpr int kCodeSegs = 20;                   // 18 real 64-lane segments + 2
 constexpr int kStageSlots = kCodeSegs * kWave;  // 1280
 constexpr int kMaxSplitRows = 2048;
+constexpr int kStageRow = kValue + 16;   // staged half partial row (bytes)
 constexpr int kQRegSteps = 27;                  // Q k-steps kept in registers
 constexpr int kQLdsSteps = kLatent / 16 - kQRegSteps;   // 9 in LDS
 constexpr int kQLdsStride = 2 * kQLdsSteps + 1; // uint4 per head (padded)
@@ -49,13 +50,17 @@ constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kRef = 64.0f;     // log2 headroom of the fixed softmax reference
 constexpr float kRange = 96.0f;   // largest logit excess (log2) handled exactly
 
-// chunk c of tile row R sits at slot R*72 + (c ^ swz(R)); swz < 8 keeps a
-// chunk inside its aligned group of 8, and 72 = 9 * 8.
+// A tile is 36 blocks of 64 slots (1 KB), block (g, rg) holding chunks
+// 8g..8g+7 of rows 8rg..8rg+7: chunk c of row R sits at slot
+// ((c/8)*4 + R/8)*64 + (R%8)*8 + ((c%8) ^ swz(R)).  One direct-to-LDS load
+// of 64 lanes fills one block, so a lane loads the same row at 16-byte
+// offsets 128g + const for every g; swz spreads the rows of a block over the
+// 64 banks for both read patterns of compute_tile.
 __device__ __forceinline__ int kv_swz(int R) {
   return (((R >> 1) & 1) << 2) | ((R >> 2) & 3);
 }
 __device__ __forceinline__ int kv_slot(int R, int c) {
-  return R * kSlotsRow + (c ^ kv_swz(R));
+  return ((c >> 3) * 4 + (R >> 3)) * 64 + (R & 7) * 8 + ((c & 7) ^ kv_swz(R));
 }
 
 __device__ __forceinline__ void wait_vm(int n) {
@@ -108,22 +113,44 @@ __device__ __forceinline__ void dma16(const uint8_t* base,
     __builtin_amdgcn_global_load_lds(base + off, dst, 16, 0, 0);
 }
 
-// Issue the direct-to-LDS loads of tile j (bf16 rows straight into a tile).
+// Direct-to-LDS loads of blocks G.. of one wave's block row: block g lands 4
+// blocks (4 KB) after block g-1 and reads 128 bytes further along the row.
+// The step goes into the per-lane offset: the instruction's immediate offset
+// would move the LDS destination as well.
+template <int G>
+__device__ __forceinline__ void block_loads(__amdgpu_buffer_rsrc_t rsrc,
+                                            uint32_t voff, uint4* dst) {
+  if constexpr (G < kSlotsRow / 8) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rsrc, (__attribute__((address_space(3))) void*)(dst + G * 4 * kWave),
+        16, voff + G * 128, 0, 0, 0);
+    block_loads<G + 1>(rsrc, voff, dst);
+  }
+}
+
+// Issue the direct-to-LDS loads of tile j (bf16 rows straight into a tile):
+// wave w fills blocks (g, w), g = 0..8, so lane l always loads row
+// 8w + l/8 and its 16-byte chunk 8g + ((l%8) ^ swz(row)): one row lookup and
+// one offset per tile, the block index g goes into the instruction offset.
 template <bool BUF>
 __device__ __forceinline__ void issue_bf16(const AttnLaunch& p, const Split& s,
                                            __amdgpu_buffer_rsrc_t rsrc, int j,
                                            uint4* dst, int wave) {
-  const int lane = opaque(lane_id());
+  const int lane = lane_id();
+  const int R = wave * 8 + (lane >> 3);
+  int ent = s.rows[j * kRowsT + R];
+  ent ^= ent >> 31;   // ~row for masked entries
+  const int cpart = ((lane & 7) ^ kv_swz(R)) * 16;
+  if constexpr (BUF) {
+    // pools under 4 GiB hold fewer than 2^24 rows of 1152 bytes
+    const uint32_t voff = __umul24((uint32_t)ent, kLatent * 2) + cpart;
+    block_loads<0>(rsrc, voff, dst + wave * kWave);
+  } else {
+    const uint8_t* src = p.kv.data + (uint64_t)(uint32_t)ent * (kLatent * 2) + cpart;
 #pragma unroll
-  for (int k = 0; k < kTileSlots / kThreads; ++k) {
-    const int seg = k * 4 + wave;
-    const int q = seg * kWave + lane;
-    const int R = q / kSlotsRow, pch = q % kSlotsRow;
-    const int c = pch ^ kv_swz(R);
-    int ent = s.rows[j * kRowsT + R];
-    ent = ent >= 0 ? ent : ~ent;
-    dma16<BUF>(p.kv.data, rsrc, (uint64_t)(uint32_t)ent * (kLatent * 2) + c * 16,
-               dst + seg * kWave);
+    for (int g = 0; g < kSlotsRow / 8; ++g)
+      __builtin_amdgcn_global_load_lds(src + g * 128,
+                                       dst + (g * 4 + wave) * kWave, 16, 0, 0);
   }
 }
 
@@ -221,16 +248,14 @@ __device__ __forceinline__ void compute_tile(const uint4* tile,
   const int n = lane & 31, h = lane >> 5;
   const char* tb = reinterpret_cast<const char*>(tile);
   // ---- S^T = KV . Q^T.  Chunk 2ks+h of row n; for ks = 4u + v the slot is
-  // 8u + ((2v + h) ^ swz(n)), so four base addresses plus 128-byte steps.
+  // that of chunk 2v+h plus u blocks of 4 (4 KB), so four base addresses.
   f32x16 acc;
   {
-    const int sw = kv_swz(n);
     int aoff[4];
 #pragma unroll
-    for (int v = 0; v < 4; ++v)
-      aoff[v] = (n * kSlotsRow + ((2 * v + h) ^ sw)) * 16;
+    for (int v = 0; v < 4; ++v) aoff[v] = kv_slot(n, 2 * v + h) * 16;
     auto a_at = [&](int ks) {
-      return *reinterpret_cast<const uint4*>(tb + aoff[ks & 3] + 128 * (ks >> 2));
+      return *reinterpret_cast<const uint4*>(tb + aoff[ks & 3] + 4096 * (ks >> 2));
     };
     auto b_at = [&](int ks) {
       return ks < kQRegSteps ? st.qb[ks < kQRegSteps ? ks : 0]
@@ -266,13 +291,19 @@ __device__ __forceinline__ void compute_tile(const uint4* tile,
     for (int r = 0; r < 16; ++r) acc[r] += acc1[r];
   }
   // ---- online softmax (lane: head n, rows 8(r/4) + 4h + r%4 of the tile)
+  if (vmask == 0xffffffffu) {   // every row of the tile is selected (uniform)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[r] *= sl2;
+  } else {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int R = 8 * (r >> 2) + 4 * h + (r & 3);
+      acc[r] = ((vmask >> R) & 1u) ? acc[r] * sl2 : -__builtin_inff();
+    }
+  }
   float tmax = -__builtin_inff();
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int R = 8 * (r >> 2) + 4 * h + (r & 3);
-    acc[r] = ((vmask >> R) & 1u) ? acc[r] * sl2 : -__builtin_inff();
-    tmax = fmaxf(tmax, acc[r]);
-  }
+  for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, acc[r]);
   tmax = fmaxf(tmax, swap_halves(tmax));
   // The reference max is fixed once per head, at the first tile with a valid
   // row, 2^64 above that tile's max: later rows stay representable (p <= 2^32
@@ -280,14 +311,17 @@ __device__ __forceinline__ void compute_tile(const uint4* tile,
   // beyond that range marks the head as out of range (its LSE becomes NaN).
   if (st.m == -__builtin_inff() && tmax != -__builtin_inff()) st.m = tmax + kRef;
   if (tmax > st.m + kRange) st.bad = true;
-  const bool live = st.m != -__builtin_inff();
+  // no reference yet (no valid row so far): subtracting +inf gives p = 0.
+  // The hardware exp2 flushes results below 2^-126, i.e. more than 2^-62
+  // below the largest p of the first valid tile.
+  const float mref = st.m != -__builtin_inff() ? st.m : __builtin_inff();
   uint4 pb[2];
 #pragma unroll
   for (int kk = 0; kk < 2; ++kk) {
     float p[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      p[e] = live ? exp2f(acc[8 * kk + e] - st.m) : 0.f;
+      p[e] = __builtin_amdgcn_exp2f(acc[8 * kk + e] - mref);
       st.l += p[e];
     }
     pb[kk] = make_uint4(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
@@ -296,8 +330,9 @@ __device__ __forceinline__ void compute_tile(const uint4* tile,
   // ---- O^T += V^T . P^T with transposing LDS reads.  Lane (G = lane/16,
   // i = lane%16) supplies the address of row Ra = 16kk + 4h + i/4 (Rb = Ra+8
   // for k-slots 4..7) at features 32t + f0, f0 = 16(G&1) + 4(i&3).  Chunk
-  // 4t + c0 of a row sits at slot 4(t ^ s2) + (c0 ^ s01) with s2, s01 the
-  // row's swizzle bits, which gives two bases (even/odd t) per row parity.
+  // 4t + c0 of a row sits in block t/2 at in-block chunk 4((t&1) ^ s2) +
+  // (c0 ^ s01) with s2, s01 the row's swizzle bits, which gives two bases
+  // (even/odd t) per row; rows 16kk + R are 2kk blocks further.
   {
     const int G = lane >> 4, i = lane & 15;
     const int f0 = 16 * (G & 1) + 4 * (i & 3);
@@ -305,12 +340,12 @@ __device__ __forceinline__ void compute_tile(const uint4* tile,
     const int Ra = 4 * h + (i >> 2), Rb = Ra + 8;
     const int swa = kv_swz(Ra), swb = kv_swz(Rb);
     const int s2 = (swa >> 2) * 64;          // same for Ra and Rb
-    const int pa = Ra * (kSlotsRow * 16) + (c0 ^ (swa & 3)) * 16 + e0;
-    const int pbo = Rb * (kSlotsRow * 16) + (c0 ^ (swb & 3)) * 16 + e0;
-    const int pa_e = pa + s2, pa_o = pa - s2;
-    const int pb_e = pbo + s2, pb_o = pbo - s2;
+    const int pa = (Ra & 7) * 128 + (c0 ^ (swa & 3)) * 16 + e0;
+    const int pbo = 1024 + (Rb & 7) * 128 + (c0 ^ (swb & 3)) * 16 + e0;
+    const int pa_e = pa + s2, pa_o = pa + 64 - s2;
+    const int pb_e = pbo + s2, pb_o = pbo + 64 - s2;
     auto rd = [&](int kk, int t) {
-      const int off = kk * 16 * kSlotsRow * 16 + 64 * t;
+      const int off = kk * 2048 + (t >> 1) * 4096;
       const uint2 ua = __builtin_bit_cast(uint2, lds_tr16(tb + ((t & 1) ? pa_o : pa_e) + off));
       const uint2 ub = __builtin_bit_cast(uint2, lds_tr16(tb + ((t & 1) ? pb_o : pb_e) + off));
       return make_uint4(ua.x, ua.y, ub.x, ub.y);
@@ -336,12 +371,18 @@ template <bool FP8, bool BUF>
 __global__ __launch_bounds__(kThreads, 1) void sparse_mla_kernel(
     AttnLaunch p, int rows_per_split) {
   constexpr int kBufSlots = FP8 ? kStageSlots : kTileSlots;
+  // Separate arrays: the compiler then knows that reads of one tile buffer
+  // cannot touch the direct-to-LDS loads in flight into another, and waits
+  // only for the loads of the tile it reads.
   __shared__ uint4 buf0[kBufSlots];
   __shared__ uint4 buf1[kBufSlots];
   __shared__ uint4 buf2[kBufSlots];
   __shared__ uint4 ftile[FP8 ? kTileSlots : 1];
   __shared__ int32_t rows[kMaxSplitRows];
   __shared__ uint4 qlds[128 * kQLdsStride];
+  static_assert(32 * kStageRow <= kBufSlots * 16 &&
+                    32 * kStageRow <= (FP8 ? kTileSlots : 128 * kQLdsStride) * 16,
+                "epilogue staging regions");
 
   const int tid = threadIdx.x, lane = lane_id();
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
@@ -484,11 +525,12 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_kernel(
     }
     wait_vm(0);
   }
-  if (!active || head >= p.H) return;
+  if (!active) return;   // wave-uniform; ended waves leave the barriers
 
   const float ltot = st.l + swap_halves(st.l);
   const int dvb = 4 * h;   // first of this lane's 4 consecutive dv per group
   if (gridDim.x == 1) {
+    if (head >= p.H) return;
     const float inv = ltot > 0.f ? 1.0f / ltot : 0.f;
     float* o = p.out + ((int64_t)s.token * p.H + head) * kValue;
 #pragma unroll
@@ -506,18 +548,47 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_kernel(
   } else {
     // partial of this split: O / l in bf16 (relative rounding 2^-9, well
     // inside the output tolerance) plus (m, l) in fp32
-    const int64_t slot = ((int64_t)s.token * gridDim.x + split) * p.H + head;
+    // The wave's 32 rows go through LDS, half a row (256 values) at a time,
+    // so that each store writes whole 512-byte row halves.  Staged rows are
+    // kStageRow bytes apart; rows 16..31 swap the 8-byte halves of every 16
+    // bytes, so the 32 lanes of a write cycle (one column of rows 0..31) hit
+    // distinct banks.  Each wave stages in a buffer of its own.
+    barrier(true);   // every wave is done reading the tiles and Q
+    char* const stg = reinterpret_cast<char*>(
+        wave == 0 ? buf0 : wave == 1 ? buf1 : wave == 2 ? buf2 : (FP8 ? ftile : qlds));
     const float inv = ltot > 0.f ? 1.0f / ltot : 0.f;
-    uint16_t* o = reinterpret_cast<uint16_t*>(p.partial) + slot * kValue;
+    const int64_t slot0 = ((int64_t)s.token * gridDim.x + split) * p.H + wave * 32;
+    uint16_t* const o0 = reinterpret_cast<uint16_t*>(p.partial) + slot0 * kValue;
+    const int rr = lane >> 5;   // row of the pair a read instruction covers
 #pragma unroll
-    for (int t = 0; t < kValue / 32; ++t)
+    for (int half = 0; half < 2; ++half) {
+      {
+        char* const wr = stg + n * kStageRow;
+        const int sx = (n >> 4) << 3;
 #pragma unroll
-      for (int g = 0; g < 4; ++g)
-        *reinterpret_cast<uint2*>(o + 32 * t + 8 * g + dvb) =
-            make_uint2(pack_bf16x2(st.o[t][4 * g] * inv, st.o[t][4 * g + 1] * inv),
-                       pack_bf16x2(st.o[t][4 * g + 2] * inv,
-                                   st.o[t][4 * g + 3] * inv));
-    if (h == 0) {
+        for (int t = 0; t < kValue / 64; ++t)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const f32x16& ot = st.o[half * (kValue / 64) + t];
+            *reinterpret_cast<uint2*>(wr + (((32 * t + 8 * g + dvb) * 2) ^ sx)) =
+                make_uint2(pack_bf16x2(ot[4 * g] * inv, ot[4 * g + 1] * inv),
+                           pack_bf16x2(ot[4 * g + 2] * inv, ot[4 * g + 3] * inv));
+          }
+      }
+#pragma unroll 4
+      for (int r0 = 0; r0 < 32; r0 += 2) {
+        const int r = r0 + rr;
+        uint4 v = *reinterpret_cast<const uint4*>(stg + r * kStageRow + (lane & 31) * 16);
+        if (r >= 16) v = make_uint4(v.z, v.w, v.x, v.y);
+        if (wave * 32 + r < p.H)
+          *reinterpret_cast<uint4*>(o0 + (int64_t)r * kValue + half * (kValue / 2) +
+                                    (lane & 31) * 8) = v;
+      }
+      // a wave's LDS accesses run in order: the second half may overwrite
+      // the first once its reads are issued
+    }
+    const int64_t slot = slot0 + n;
+    if (h == 0 && head < p.H) {
       const int64_t nslots = (int64_t)gridDim.y * gridDim.x * p.H;
       float* ml = reinterpret_cast<float*>(
                       reinterpret_cast<uint16_t*>(p.partial) + nslots * kValue) +
