@@ -46,6 +46,70 @@ def algorithmic_bytes(wl, L):
     return wl.B * wl.T * per_tok
 
 
+def step_bytes_general(wl, lens):
+    """Algorithmic bytes of one decode step over sequences of lengths `lens`
+    (one query each): every indexer key (bf16, or e4m3 codes + e8m0 block
+    scales) once, every selected latent row (bf16, or MXFP8 codes + scales)
+    once, plus queries, weights, indices and outputs."""
+    key_b = wl.d_I + wl.d_I // 32 if wl.quantized else 2 * wl.d_I
+    row_b = 576 + 18 if wl.quantized else 2 * 576
+    tot = 0
+    for L in lens:
+        L = int(L)
+        tot += (L * key_b + min(wl.top_k, L) * row_b
+                + wl.H_I * wl.d_I * 2 + wl.H_I * 4 + wl.H * 576 * 2
+                + wl.H * 512 * 4 + wl.H * 4 + wl.top_k * 4)
+    return tot
+
+
+def decode_config(name, stream, steps=20, warmup=5):
+    """ms per dsa_decode_step call for another decode configuration, with
+    enough input replicas rotating that a step's operands (over 1 GB in
+    total) are not served from the 256 MB Infinity Cache."""
+    import torch
+    import indexed_sparse_attention_lightning_amd as dsa
+    import workloads as wk
+    from workloads.device import to_device
+    wl = wk.WORKLOADS[name]
+    inp = wk.generate(wl)
+    lens = [int(x) for x in inp.seq_lens]
+    sb = step_bytes_general(wl, lens)
+    nrep = max(3, -(-(1 << 30) // sb))
+    base = to_device(inp)
+    reps = [base] + [{k: (None if v is None else v.clone())
+                      for k, v in base.items() if not k.endswith("_c")}
+                     for _ in range(nrep - 1)]
+    caches = [dsa.PagedCache(kidx=d["kidx"], kv=d["kv"],
+                             page_table=d["page_table"], seq_lens=d["seq_lens"],
+                             kidx_scale=d["kidx_scale"], kv_scale=d["kv_scale"])
+              for d in reps]
+    max_len = max(lens)
+    ws = torch.empty(dsa.workspace_size(dsa.OP_DECODE_STEP, wl.B, 1, max_len,
+                                        wl.H, wl.top_k), dtype=torch.uint8,
+                     device="cuda")
+    o = torch.empty((wl.B, 1, wl.H, 512), device="cuda")
+    l = torch.empty((wl.B, 1, wl.H), device="cuda")
+
+    def step(i):
+        r = i % nrep
+        d = reps[r]
+        dsa.decode_step(caches[r], d["q_idx"], d["w"], d["q"], wl.top_k,
+                        wl.softmax_scale, max_seq_len=max_len, out=o, lse=l,
+                        workspace=ws)
+
+    ms = time_loop(step, steps, warmup, stream)
+    gbps = sb / (ms * 1e-3) / 1e9
+    res = {"ms_per_step": round(ms, 5),
+           "tokens_per_s": round(wl.B / (ms * 1e-3), 1),
+           "step_algorithmic_bytes": sb,
+           "step_hbm_gbps": round(gbps, 1),
+           "step_frac_of_peak": round(gbps / PEAK_HBM_GBPS, 4),
+           "input_replicas": nrep}
+    del reps, caches, base, ws
+    torch.cuda.empty_cache()
+    return res
+
+
 def indexer_bytes(wl, L):
     """Algorithmic bytes of one indexer launch: keys + queries + weights."""
     return wl.B * wl.T * (L * wl.d_I * 2 + wl.H_I * wl.d_I * 2 + wl.H_I * 4)
@@ -180,6 +244,8 @@ def main(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true",
                     help="skip the prefill-chunk kernel timings")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the FP8 and ragged decode configurations")
     ap.add_argument("--kernels-only", action="store_true",
                     help="run one 256 MiB device copy (counter calibration) "
                          "and one decode step, then exit (for rocprofv3 "
@@ -320,6 +386,16 @@ def main(argv=None):
     del reps, caches, outs, scores
     if not args.no_prefill:
         line["prefill"] = prefill_kernels(stream)
+    if not args.no_configs:
+        line["other_configs"] = {
+            "decode_fp8": dict(workload="batch 32 x 32768, e4m3 indexer keys "
+                               "and MXFP8 latent KV (block 32, e8m0 scales), "
+                               "top_k 2048", **decode_config("decode_fp8", stream)),
+            "ragged": dict(workload="batch 4, lengths uniform in [16384, "
+                           "131072], 64-token pages scattered by a seeded "
+                           "page table, FP8 keys and MXFP8 KV, top_k 2048",
+                           **decode_config("ragged", stream)),
+        }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(inp)
     print(json.dumps(line), flush=True)

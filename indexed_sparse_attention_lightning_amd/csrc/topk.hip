@@ -210,6 +210,38 @@ struct RowKeys {
       return valid(j) ? score_key(row[pos(j)]) - kmin : 0u;
     }
   }
+
+  // Rows read again from memory: f(j, key) for steps 0..nsteps-1 in chunks
+  // of kChunk steps, every load of a chunk issued together and the next
+  // chunk's loads in flight while this one is processed.  Buffer loads
+  // bounded by the candidate count read 0 past n.
+  static constexpr int kChunk = 16;
+  template <class F>
+  __device__ __forceinline__ void stream(int nsteps, F&& f) const {
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float*>(row), 0, n * 4, 0x00020000);
+    const uint32_t voff = (uint32_t)(wbase + lane) * 4;
+    uint32_t cur[kChunk], nxt[kChunk];
+#pragma unroll
+    for (int u = 0; u < kChunk; ++u)
+      cur[u] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(
+          rs, voff + u * kWave * 4, 0, 0);
+    for (int j0 = 0; j0 < nsteps; j0 += kChunk) {
+#pragma unroll
+      for (int u = 0; u < kChunk; ++u)
+        nxt[u] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(
+            rs, voff + (j0 + kChunk + u) * kWave * 4, 0, 0);
+#pragma unroll
+      for (int u = 0; u < kChunk; ++u) {
+        const int j = j0 + u;
+        if (j < nsteps)   // wave-uniform
+          f(j, valid(j) ? score_key(__builtin_bit_cast(float, cur[u])) - kmin
+                        : 0u);
+      }
+#pragma unroll
+      for (int u = 0; u < kChunk; ++u) cur[u] = nxt[u];
+    }
+  }
 };
 
 template <int KPT, bool RES>
@@ -260,12 +292,11 @@ __global__ __launch_bounds__(kThreads, 1) void topk_kernel(TopkLaunch p) {
       mx = max(mx, keys.k[j]);
     }
   } else {
-#pragma unroll 8
-    for (int j = 0; j < nsteps; ++j) {
-      const uint32_t k = keys.rel(j);   // kmin is still 0: absolute, 0 past n
+    // kmin is still 0: absolute keys, 0 past n
+    keys.stream(nsteps, [&](int, uint32_t k) {
       mn = min(mn, k - 1u);
       mx = max(mx, k);
-    }
+    });
   }
   {
     uint4* h = reinterpret_cast<uint4*>(sm.hist);
@@ -315,8 +346,7 @@ __global__ __launch_bounds__(kThreads, 1) void topk_kernel(TopkLaunch p) {
         TOPK_STEP_FENCE(j);
       }
     } else {
-#pragma unroll 8
-      for (int j = 0; j < nsteps; ++j) count(j, keys.rel(j));
+      keys.stream(nsteps, count);
     }
     __syncthreads();
     uint32_t above;
@@ -374,7 +404,7 @@ __global__ __launch_bounds__(kThreads, 1) void topk_kernel(TopkLaunch p) {
       TOPK_STEP_FENCE(j);
     }
   } else {
-    for (int j = 0; j < nsteps; ++j) sweep(j, keys.rel(j));
+    keys.stream(nsteps, sweep);
   }
   if constexpr (RES) {
 #pragma unroll
@@ -433,7 +463,7 @@ __global__ __launch_bounds__(kThreads, 1) void topk_kernel(TopkLaunch p) {
             TOPK_STEP_FENCE(j);
           }
         } else {
-          for (int j = 0; j < nsteps; ++j) count(j, keys.rel(j));
+          keys.stream(nsteps, count);
         }
       }
       __syncthreads();
@@ -473,7 +503,7 @@ __global__ __launch_bounds__(kThreads, 1) void topk_kernel(TopkLaunch p) {
           TOPK_STEP_FENCE(j);
         }
       } else {
-        for (int j = 0; j < nsteps; ++j) marks(j, keys.rel(j));
+        keys.stream(nsteps, marks);
       }
     }
     __syncthreads();
