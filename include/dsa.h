@@ -129,7 +129,12 @@ dsa_status dsa_indexer_scores(int B, int T, int L, int H_I, int d_I,
  *   idx    [B, T, K] int32 out: the min(K, q_pos+1) positions with the
  *          largest scores (equal scores: lower position first), in ascending
  *          order, then -1 padding
- *   workspace: dsa_workspace_size(DSA_OP_TOPK, ...) bytes (may be 0 / NULL)
+ *   workspace: dsa_workspace_size(DSA_OP_TOPK, ...) bytes: candidate lists
+ *          for rows longer than 65536 positions (each 16384-position chunk
+ *          selects its own Top-K, then each row selects from its chunks'
+ *          candidates).  It is 0 for shorter rows and may be NULL / too
+ *          small: long rows then run on one workgroup each (same result,
+ *          slower).
  */
 dsa_status dsa_topk(int B, int T, int L, int K, const float* scores,
                     const int32_t* q_pos, int32_t* idx, void* workspace,

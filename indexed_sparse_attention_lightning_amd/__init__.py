@@ -166,17 +166,28 @@ def indexer_scores(q_idx: torch.Tensor, w: torch.Tensor, k_idx: torch.Tensor,
 
 
 def topk(scores: torch.Tensor, q_pos: torch.Tensor, k: int,
-         out: Optional[torch.Tensor] = None) -> torch.Tensor:
+         out: Optional[torch.Tensor] = None,
+         workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
     """idx [B, T, k] int32: the min(k, q_pos+1) best positions of each row
-    (ties to the lower position), ascending, then -1."""
+    (ties to the lower position), ascending, then -1.  Rows longer than
+    65536 use a workspace of workspace_size(OP_TOPK, ...) bytes (allocated
+    here when not given; an empty tensor selects the one-workgroup path)."""
     B, T, L = scores.shape
     _need(scores, "scores", torch.float32)
     _need(q_pos, "q_pos", torch.int32, (B, T))
     if out is None:
         out = torch.empty((B, T, k), dtype=torch.int32, device=scores.device)
     _need(out, "idx", torch.int32, (B, T, k))
+    if workspace is None:
+        ws_bytes = workspace_size(OP_TOPK, B, T, L, 1, k)
+        if ws_bytes:
+            workspace = torch.empty(ws_bytes, dtype=torch.uint8,
+                                    device=scores.device)
     _check(_lib.dsa_topk(B, T, L, k, _ptr(scores), _ptr(q_pos), _ptr(out),
-                         None, 0, _stream()), "dsa_topk")
+                         _ptr(workspace) if workspace is not None and
+                         workspace.numel() else None,
+                         0 if workspace is None else workspace.numel(),
+                         _stream()), "dsa_topk")
     return out
 
 

@@ -63,6 +63,7 @@ size_t decode_ws(int B, int T, int L, int H, int K) {
   const size_t tokens = (size_t)B * T;
   return align_up(tokens * (size_t)L * sizeof(float)) +
          align_up(tokens * (size_t)K * sizeof(int32_t)) +
+         align_up(dsa::topk_workspace_bytes((int)tokens, L, K)) +
          align_up(dsa::attn_workspace_bytes((int)tokens, H, K));
 }
 
@@ -93,7 +94,7 @@ size_t dsa_workspace_size(int op, int B, int T, int L, int H, int K) {
   if (B < 1 || T < 1 || L < 1 || H < 1 || K < 1) return 0;
   switch (op) {
     case DSA_OP_INDEXER_SCORES: return 0;
-    case DSA_OP_TOPK: return 0;
+    case DSA_OP_TOPK: return dsa::topk_workspace_bytes(B * T, L, K);
     case DSA_OP_SPARSE_MLA: return dsa::attn_workspace_bytes(B * T, H, K);
     case DSA_OP_DECODE_STEP: return decode_ws(B, T, L, H, K);
     default: return 0;
@@ -132,8 +133,6 @@ dsa_status dsa_indexer_scores(int B, int T, int L, int H_I, int d_I,
 dsa_status dsa_topk(int B, int T, int L, int K, const float* scores,
                     const int32_t* q_pos, int32_t* idx, void* workspace,
                     size_t workspace_bytes, void* stream) {
-  (void)workspace;
-  (void)workspace_bytes;
   if (!scores || !q_pos || !idx)
     return fail(DSA_ERR_NULL, "dsa_topk: NULL tensor pointer");
   if (B < 1 || T < 1 || L < 1) return fail(DSA_ERR_SHAPE, "B, T, L must be >= 1");
@@ -149,7 +148,8 @@ dsa_status dsa_topk(int B, int T, int L, int K, const float* scores,
   a.scores = scores;
   a.qp = dsa::QueryPos{q_pos, nullptr, T};
   a.idx = idx;
-  return hip_status(dsa::launch_topk(a, (hipStream_t)stream), "dsa_topk");
+  return hip_status(dsa::launch_topk(a, workspace, workspace_bytes,
+                                     (hipStream_t)stream), "dsa_topk");
 }
 
 dsa_status dsa_sparse_mla_attn(int B, int T, int L, int H, int K,
@@ -235,6 +235,9 @@ dsa_status dsa_decode_step(int B, int T, int H_I, int d_I, int H, int K,
   ws += align_up(tokens * (size_t)max_seq_len * sizeof(float));
   int32_t* idx = reinterpret_cast<int32_t*>(ws);
   ws += align_up(tokens * (size_t)K * sizeof(int32_t));
+  void* topk_ws = ws;
+  const size_t topk_bytes = dsa::topk_workspace_bytes((int)tokens, max_seq_len, K);
+  ws += align_up(topk_bytes);
   float* partial = reinterpret_cast<float*>(ws);
   if (idx_out) idx = idx_out;
 
@@ -261,7 +264,7 @@ dsa_status dsa_decode_step(int B, int T, int H_I, int d_I, int H, int K,
   ta.scores = scores;
   ta.qp = qp;
   ta.idx = idx;
-  if (hipError_t e = dsa::launch_topk(ta, st))
+  if (hipError_t e = dsa::launch_topk(ta, topk_ws, topk_bytes, st))
     return hip_status(e, "dsa_decode_step: topk");
 
   dsa::AttnLaunch aa{};

@@ -50,8 +50,17 @@ struct TopkLaunch {
   const float* scores;
   QueryPos qp;
   int32_t* idx;            // [rows, K]
+  int nchunks, chunk;      // long rows: chunks per row, positions per chunk
+  int32_t* cand;           // long rows: [rows, nchunks, K] candidate lists
 };
+// One workgroup per row.
 hipError_t launch_topk(const TopkLaunch& a, hipStream_t stream);
+// Rows longer than 64K positions go through per-chunk candidate lists when
+// the workspace holds topk_workspace_bytes(); otherwise as above.
+hipError_t launch_topk(const TopkLaunch& a, void* workspace,
+                       size_t workspace_bytes, hipStream_t stream);
+int topk_chunks(int L);
+size_t topk_workspace_bytes(int rows, int L, int K);
 
 struct AttnLaunch {
   int B, T, H, K;

@@ -128,6 +128,46 @@ __device__ __forceinline__ void block_loads(__amdgpu_buffer_rsrc_t rsrc,
   }
 }
 
+// The loads of one bf16 tile as nine separate blocks, so that they can be
+// spread over the matrix-core work of the tile being computed: prepare()
+// looks up this lane's row, block(g) issues block (g, wave).
+template <bool BUF>
+struct TileLoads {
+  const uint8_t* data;
+  __amdgpu_buffer_rsrc_t rsrc;
+  const int32_t* rows;   // the tile's 32 physical rows (~row if masked)
+  uint4* dst;
+  int wave;
+  uint32_t voff;
+  __device__ __forceinline__ void prepare() {
+    const int lane = lane_id();
+    const int R = wave * 8 + (lane >> 3);
+    int ent = rows[R];
+    ent ^= ent >> 31;
+    const int cpart = ((lane & 7) ^ kv_swz(R)) * 16;
+    if constexpr (BUF)
+      voff = __umul24((uint32_t)ent, kLatent * 2) + cpart;
+    else
+      voff = (uint32_t)ent;   // 64-bit offset formed per block
+    if constexpr (!BUF) cp = cpart;
+  }
+  int cp = 0;
+  __device__ __forceinline__ void block(int g) const {
+    uint4* d = dst + (g * 4 + wave) * kWave;
+    if constexpr (BUF)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rsrc, (__attribute__((address_space(3))) void*)d, 16, voff + g * 128,
+          0, 0, 0);
+    else
+      __builtin_amdgcn_global_load_lds(
+          data + (uint64_t)voff * (kLatent * 2) + cp + g * 128, d, 16, 0, 0);
+  }
+};
+struct NoLoads {
+  __device__ __forceinline__ void prepare() {}
+  __device__ __forceinline__ void block(int) const {}
+};
+
 // Issue the direct-to-LDS loads of tile j (bf16 rows straight into a tile):
 // wave w fills blocks (g, w), g = 0..8, so lane l always loads row
 // 8w + l/8 and its 16-byte chunk 8g + ((l%8) ^ swz(row)): one row lookup and
@@ -241,12 +281,14 @@ __device__ __forceinline__ void mfma32_vgpr_last(f32x16& c, const uint4& a,
 
 // One 32-row tile for this wave's 32 heads.  `vmask` bit R says whether tile
 // row R is a real selected row.
+template <class Loads>
 __device__ __forceinline__ void compute_tile(const uint4* tile,
                                              const uint4* qrow, uint32_t vmask,
                                              HeadState& st, float sl2,
-                                             int lane) {
+                                             int lane, Loads& loads) {
   const int n = lane & 31, h = lane >> 5;
   const char* tb = reinterpret_cast<const char*>(tile);
+  loads.prepare();
   // ---- S^T = KV . Q^T.  Chunk 2ks+h of row n; for ks = 4u + v the slot is
   // that of chunk 2v+h plus u blocks of 4 (4 KB), so four base addresses.
   f32x16 acc;
@@ -278,6 +320,9 @@ __device__ __forceinline__ void compute_tile(const uint4* tile,
         aq[(ks + kAhead) % (kAhead + 1)] = a_at(ks + kAhead);
         bq[(ks + kAhead) % (kAhead + 1)] = b_at(ks + kAhead);
       }
+      // one block of the next tile's loads every fourth k-step (k-steps 2,
+      // 6, ..., 34), so the address unit drains while the matrix core works
+      if ((ks & 3) == 2) loads.block(ks >> 2);
       const uint4 a = aq[ks % (kAhead + 1)], b = bq[ks % (kAhead + 1)];
       f32x16& c = (ks & 1) ? acc1 : acc;
       if (ks < 2)
@@ -413,7 +458,8 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_kernel(
   const int dummy = nvalid > 0 ? (int)cache_row(p.kv.page_table,
                                                 p.kv.max_pages, p.kv.L, s.b, 0)
                                  : 0;
-  // all index loads of a thread first, then the page-table lookups
+  // all index loads of a thread first, then the query loads (in flight
+  // while the page-table lookups run), then the row table
   constexpr int kRowIter = kMaxSplitRows / kThreads;   // 8
   int pos[kRowIter];
 #pragma unroll
@@ -421,8 +467,33 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_kernel(
     const int i = tid + u * kThreads;
     const int r = s.r0 + i;
     pos[u] = (i < s.ntiles * kRowsT && r < s.r1) ? idx[r] : -1;
-    if (!(pos[u] >= 0 && pos[u] < nvalid)) pos[u] = -1;
   }
+  const int n = lane & 31, h = lane >> 5;
+  const int head = wave * 32 + n;
+  const bool active = wave * 32 < p.H;   // wave-uniform
+  HeadState st;
+  st.m = -__builtin_inff();
+  st.l = 0.f;
+  st.bad = false;
+#pragma unroll
+  for (int t = 0; t < kValue / 32; ++t) st.o[t] = f32x16{};
+  constexpr int kQL = 128 * 2 * kQLdsSteps / kThreads;   // 9 per thread
+  uint4 qv[kQL];
+  {
+    const uint16_t* qh = p.q + ((int64_t)s.token * p.H + min(head, p.H - 1)) * kLatent;
+#pragma unroll
+    for (int ks = 0; ks < kQRegSteps; ++ks) st.qb[ks] = ld16(qh + ks * 16 + h * 8);
+#pragma unroll
+    for (int u = 0; u < kQL; ++u) {
+      const int i = tid + u * kThreads;
+      const int hd = i / (2 * kQLdsSteps), r = i % (2 * kQLdsSteps);
+      qv[u] = ld16(p.q + ((int64_t)s.token * p.H + min(hd, p.H - 1)) * kLatent +
+                   (kQRegSteps + (r >> 1)) * 16 + (r & 1) * 8);
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < kRowIter; ++u)
+    if (!(pos[u] >= 0 && pos[u] < nvalid)) pos[u] = -1;
 #pragma unroll
   for (int u = 0; u < kRowIter; ++u) {
     const int i = tid + u * kThreads;
@@ -436,7 +507,7 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_kernel(
   const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
       (void*)p.kv.data, (short)0,
       (int)(BUF ? (uint32_t)p.kv.bytes : 0u), 0x00020000);
-  // the first two tiles are in flight while the queries load
+  // the first two tiles go out while the queries are still arriving
   uint32_t sc0[5], sc1[5], sc2[5];
   constexpr int per_tile = FP8 ? 10 : 9;
   auto issue = [&](int j, uint4* dst, uint32_t (&sc)[5]) {
@@ -446,40 +517,16 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_kernel(
   issue(0, buf0, sc0);
   issue(min(1, s.ntiles - 1), buf1, sc1);
 
-  const int n = lane & 31, h = lane >> 5;
-  const int head = wave * 32 + n;
-  const bool active = wave * 32 < p.H;   // wave-uniform
-  HeadState st;
-  st.m = -__builtin_inff();
-  st.l = 0.f;
-  st.bad = false;
+  // the last k-steps of every head of this token go to LDS
 #pragma unroll
-  for (int t = 0; t < kValue / 32; ++t) st.o[t] = f32x16{};
-  {
-    const uint16_t* qh = p.q + ((int64_t)s.token * p.H + min(head, p.H - 1)) * kLatent;
-    const uint32_t keep = head < p.H ? 0xffffffffu : 0u;
+  for (int u = 0; u < kQL; ++u) {
+    const int i = tid + u * kThreads;
+    const int hd = i / (2 * kQLdsSteps), r = i % (2 * kQLdsSteps);
+    qlds[hd * kQLdsStride + r] = hd < p.H ? qv[u] : make_uint4(0, 0, 0, 0);
+  }
+  if (head >= p.H) {
 #pragma unroll
-    for (int ks = 0; ks < kQRegSteps; ++ks) {
-      const uint4 v = ld16(qh + ks * 16 + h * 8);
-      st.qb[ks] = make_uint4(v.x & keep, v.y & keep, v.z & keep, v.w & keep);
-    }
-    // the last k-steps of every head of this token into LDS (all loads of
-    // a thread issued before any store)
-    constexpr int kQL = 128 * 2 * kQLdsSteps / kThreads;   // 9 per thread
-    uint4 qv[kQL];
-#pragma unroll
-    for (int u = 0; u < kQL; ++u) {
-      const int i = tid + u * kThreads;
-      const int hd = i / (2 * kQLdsSteps), r = i % (2 * kQLdsSteps);
-      qv[u] = ld16(p.q + ((int64_t)s.token * p.H + min(hd, p.H - 1)) * kLatent +
-                   (kQRegSteps + (r >> 1)) * 16 + (r & 1) * 8);
-    }
-#pragma unroll
-    for (int u = 0; u < kQL; ++u) {
-      const int i = tid + u * kThreads;
-      const int hd = i / (2 * kQLdsSteps), r = i % (2 * kQLdsSteps);
-      qlds[hd * kQLdsStride + r] = hd < p.H ? qv[u] : make_uint4(0, 0, 0, 0);
-    }
+    for (int ks = 0; ks < kQRegSteps; ++ks) st.qb[ks] = make_uint4(0, 0, 0, 0);
   }
   barrier(true);
   const uint4* qrow = qlds + (wave * 32 + n) * kQLdsStride + h;
@@ -501,7 +548,11 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_kernel(
                     uint32_t (&scn)[5]) {
       wait_vm(per_tile);
       barrier(false);
-      issue(min(j + 2, s.ntiles - 1), nxt, scn);
+      const int jn = min(j + 2, s.ntiles - 1);
+      // bf16: a wave that computes this step spreads the loads of tile j+2
+      // over its S^T products; otherwise they all go out here
+      const bool spread = !FP8 && active && j < s.ntiles;   // wave-uniform
+      if (!spread) issue(jn, nxt, scn);
       if (j < s.ntiles) {
         const uint4* tile = cur;
         if constexpr (FP8) {
@@ -512,7 +563,13 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_kernel(
         if (active) {
           const uint32_t vmask = (uint32_t)__builtin_amdgcn_ballot_w64(
               s.rows[j * kRowsT + (lane & 31)] >= 0);
-          compute_tile(tile, qrow, vmask, st, sl2, lane);
+          if constexpr (FP8) {
+            NoLoads none;
+            compute_tile(tile, qrow, vmask, st, sl2, lane, none);
+          } else {
+            TileLoads<BUF> tl{p.kv.data, rsrc, s.rows + jn * kRowsT, nxt, wave, 0u};
+            compute_tile(tile, qrow, vmask, st, sl2, lane, tl);
+          }
         }
         if constexpr (FP8) barrier(false);   // ftile is rewritten next step
       }

@@ -180,13 +180,12 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v,
   return base + incl - v;
 }
 
-// Keys of one wave step.  Once the row's smallest key kmin is known they
-// are kept relative to it (r = key - kmin, so a pass's digit is a shift of
-// r); resident rows hold them in registers, longer rows read them again
-// from the score row.  Lanes past the row's n candidates get r = 0: they
-// tie with the smallest key and sit after every candidate, so the
-// selection (largest keys, then lowest positions) never reaches them
-// (K <= n) and no pass needs a validity test.
+// Keys of one wave step.  Once the row's smallest key is known they are kept
+// relative to it minus one (r = key - kmin >= 1, so a pass's digit is a
+// shift of r); resident rows hold them in registers, longer rows read them
+// again from the score row.  Lanes past the row's n candidates get r = 0,
+// which the histograms and candidate lists skip (one compare; no position
+// test).
 template <int KPT, bool RES>
 struct RowKeys {
   uint32_t k[RES ? KPT : 1];
@@ -244,26 +243,59 @@ struct RowKeys {
   }
 };
 
-template <int KPT, bool RES>
+// What one workgroup selects from:
+//   kRow     a whole score row (positions 0..n-1, n from the query position);
+//   kChunk   chunk c of a row (its positions c*chunk ..), writing the chunk's
+//            own Top-K as row positions (-1 padded) to the candidate lists;
+//   kGather  a row's candidate lists (nchunks * K slots of positions in
+//            ascending order, -1 holes), each slot's key read from the row
+//            at its position.  A row's Top-K lies in the union of its chunks'
+//            Top-Ks (an entry of the row's Top-K has fewer than K entries
+//            above it in its own chunk), and slot order is position order,
+//            so ties still go to the lower position.
+enum TopkMode { kRow = 0, kChunk = 1, kGather = 2 };
+
+template <int KPT, bool RES, int MODE = kRow>
 __global__ __launch_bounds__(kThreads, 1) void topk_kernel(TopkLaunch p) {
   __shared__ TopkShared sm;
   const int tid = threadIdx.x, lane = lane_id();
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
-  const int r = blockIdx.x;
+  const int r = MODE == kChunk ? blockIdx.x / p.nchunks : blockIdx.x;
   const int b = r / p.T, t = r % p.T;
   const int qpos = query_pos(p.qp, b, t);
-  const int n = max(0, min(qpos + 1, p.L));
-  const int kk = min(p.K, n);
-  int32_t* out = p.idx + (int64_t)r * p.K;
+  const int nrow = max(0, min(qpos + 1, p.L));   // causal candidates of the row
+  int n, kk, pbase = 0;
+  const float* rowp = p.scores + (int64_t)r * p.L;
+  const int32_t* cand = nullptr;
+  int32_t* out;
+  if constexpr (MODE == kRow) {
+    n = nrow;
+    kk = min(p.K, n);
+    out = p.idx + (int64_t)r * p.K;
+  } else if constexpr (MODE == kChunk) {
+    const int c = blockIdx.x % p.nchunks;
+    pbase = c * p.chunk;
+    n = max(0, min(nrow - pbase, p.chunk));
+    kk = min(p.K, n);
+    rowp += pbase;
+    out = p.cand + (int64_t)blockIdx.x * p.K;
+  } else {
+    n = p.nchunks * p.K;   // candidate slots
+    kk = min(p.K, nrow);
+    cand = p.cand + (int64_t)r * n;
+    out = p.idx + (int64_t)r * p.K;
+  }
 
   for (int i = kk + tid; i < p.K; i += kThreads) out[i] = -1;
   if (kk == n) {  // every candidate is selected
-    for (int i = tid; i < n; i += kThreads) out[i] = i;
+    for (int i = tid; i < n; i += kThreads)
+      out[i] = MODE == kGather ? cand[i] : pbase + i;
     return;
   }
+  if (MODE == kGather && kk == 0) return;
 
   RowKeys<KPT, RES> keys;
-  keys.row = p.scores + (int64_t)r * p.L;
+  keys.row = rowp;
   keys.n = n;
   keys.wbase = wave * KPT * kWave;
   keys.lane = lane;
@@ -277,19 +309,47 @@ __global__ __launch_bounds__(kThreads, 1) void topk_kernel(TopkLaunch p) {
   if constexpr (RES) {
     // buffer loads bounded by the candidate count: positions past n read 0
     // without branches, and all loads share one offset register
-    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<float*>(keys.row), 0, n * 4, 0x00020000);
+    if constexpr (MODE == kGather) {
+      // slot positions first (slots past n are holes), then the scores at
+      // those positions (a hole's offset is out of the row's range: the
+      // bounded load reads 0 without touching memory); a hole gets key 0
+      const __amdgpu_buffer_rsrc_t cs = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<int32_t*>(cand), 0, n * 4, 0x00020000);
+      int32_t ps[KPT];
 #pragma unroll
-    for (int j = 0; j < KPT; ++j)
-      keys.k[j] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(
-          rs, (keys.wbase + lane) * 4, j * kWave * 4, 0);
-    // keys of candidates are >= 1 (NaN maps to 1): 0 marks a lane past n
+      for (int j = 0; j < KPT; ++j) {
+        const int32_t v = __builtin_amdgcn_raw_buffer_load_b32(
+            cs, (keys.wbase + lane) * 4, j * kWave * 4, 0);
+        ps[j] = keys.valid(j) ? v : -1;
+      }
+      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<float*>(keys.row), 0, nrow * 4, 0x00020000);
 #pragma unroll
-    for (int j = 0; j < KPT; ++j) {
-      keys.k[j] = keys.valid(j)
-                      ? score_key(__builtin_bit_cast(float, keys.k[j])) : 0u;
-      mn = min(mn, keys.k[j] - 1u);
-      mx = max(mx, keys.k[j]);
+      for (int j = 0; j < KPT; ++j)
+        keys.k[j] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(
+            rs, (uint32_t)ps[j] * 4u, 0, 0);
+#pragma unroll
+      for (int j = 0; j < KPT; ++j) {
+        keys.k[j] = ps[j] >= 0
+                        ? score_key(__builtin_bit_cast(float, keys.k[j])) : 0u;
+        mn = min(mn, keys.k[j] - 1u);
+        mx = max(mx, keys.k[j]);
+      }
+    } else {
+      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<float*>(keys.row), 0, n * 4, 0x00020000);
+#pragma unroll
+      for (int j = 0; j < KPT; ++j)
+        keys.k[j] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(
+            rs, (keys.wbase + lane) * 4, j * kWave * 4, 0);
+      // keys of candidates are >= 1 (NaN maps to 1): 0 marks a lane past n
+#pragma unroll
+      for (int j = 0; j < KPT; ++j) {
+        keys.k[j] = keys.valid(j)
+                        ? score_key(__builtin_bit_cast(float, keys.k[j])) : 0u;
+        mn = min(mn, keys.k[j] - 1u);
+        mx = max(mx, keys.k[j]);
+      }
     }
   } else {
     // kmin is still 0: absolute keys, 0 past n
@@ -316,7 +376,10 @@ __global__ __launch_bounds__(kThreads, 1) void topk_kernel(TopkLaunch p) {
   uint32_t kmin = lane < kWaves ? sm.wmin[lane] : 0xffffffffu;
   uint32_t kmax = lane < kWaves ? sm.wmax[lane] : 0u;
   wave_minmax(kmin, kmax);
-  kmin += 1u;   // n >= 2 here, so some lane holds a candidate
+  // some lane holds a candidate (n >= 2 here).  kmin is the smallest
+  // candidate key minus one: candidates have relative keys >= 1 and lanes
+  // past n (or holes between candidate slots) the relative key 0, which no
+  // histogram, candidate list or bitmap takes.
   keys.kmin = kmin;
   if constexpr (RES) {
 #pragma unroll
@@ -326,9 +389,9 @@ __global__ __launch_bounds__(kThreads, 1) void topk_kernel(TopkLaunch p) {
 
   // ---- first digit over all keys: digit(r) = r >> nsh, r <= range
   const uint32_t range = kmax - kmin;
-  const int sh0 = range ? 32 - __builtin_clz(range) : 0;   // range < 2^sh0
+  const int sh0 = 32 - __builtin_clz(range);   // range >= 1, < 2^sh0
   uint32_t rem = (uint32_t)kk;
-  uint32_t d0 = 0, cnt0 = (uint32_t)n;   // all keys equal: one digit
+  uint32_t d0 = 0, cnt0 = 0;
   int nsh = 0;
   if (sh0 > 0) {
     const int np = (sh0 + kDigitBits - 1) / kDigitBits;
@@ -337,7 +400,7 @@ __global__ __launch_bounds__(kThreads, 1) void topk_kernel(TopkLaunch p) {
     const int nb = 1 << nbits;
     const auto count = [&](int j, uint32_t rk) {
       (void)j;
-      atomicAdd(&sm.hist[rk >> nsh], 1u);   // rk <= range < 2^sh0
+      if (rk != 0u) atomicAdd(&sm.hist[rk >> nsh], 1u);   // rk <= range < 2^sh0
     };
     if constexpr (RES) {
 #pragma unroll
@@ -368,7 +431,7 @@ __global__ __launch_bounds__(kThreads, 1) void topk_kernel(TopkLaunch p) {
 #pragma unroll
   for (int i = 0; i < kMaskRegs; ++i) gwr[i] = ewr[i] = 0u;
   const auto sweep = [&](int j, uint32_t rk) {
-    const bool in = rk >= blo && rk <= bhi;
+    const bool in = rk != 0u && rk >= blo && rk <= bhi;
     const uint64_t g = __ballot(rk > bhi);
     const uint64_t c = __ballot(in);
     if constexpr (RES) {
@@ -452,7 +515,7 @@ __global__ __launch_bounds__(kThreads, 1) void topk_kernel(TopkLaunch p) {
       } else {
         const auto count = [&](int j, uint32_t rk) {
           (void)j;
-          const bool in = rk >= lo && rk - lo < win;
+          const bool in = rk != 0u && rk >= lo && rk - lo < win;
           if (__ballot(in) != 0ull && in)
             atomicAdd(&sm.hist[(rk - lo) >> psh], 1u);
         };
@@ -552,7 +615,8 @@ __global__ __launch_bounds__(kThreads, 1) void topk_kernel(TopkLaunch p) {
     while (m) {
       const int bit = __builtin_ctz(m);
       m &= m - 1;
-      if (slot < (uint32_t)kk) out[slot] = w * 32 + bit;
+      if (slot < (uint32_t)kk)
+        out[slot] = MODE == kGather ? cand[w * 32 + bit] : pbase + w * 32 + bit;
       ++slot;
     }
   }
@@ -564,7 +628,44 @@ void launch_kpt(const TopkLaunch& p, hipStream_t stream) {
                      stream, p);
 }
 
+constexpr int kChunkLen = 16 * kThreads;   // positions per chunk workgroup
+
 }  // namespace
+
+int topk_chunks(int L) {
+  return L > 64 * kThreads ? (L + kChunkLen - 1) / kChunkLen : 0;
+}
+
+size_t topk_workspace_bytes(int rows, int L, int K) {
+  return (size_t)rows * topk_chunks(L) * K * sizeof(int32_t);
+}
+
+hipError_t launch_topk(const TopkLaunch& p0, void* workspace,
+                       size_t workspace_bytes, hipStream_t stream) {
+  // Rows past 64K positions: one workgroup per 16K-position chunk selects
+  // the chunk's Top-K (keys in registers), then one workgroup per row
+  // selects from the chunks' candidates.  Without the workspace for the
+  // candidate lists, one workgroup streams the whole row.
+  const int nch = topk_chunks(p0.L);
+  const size_t need = topk_workspace_bytes(p0.rows, p0.L, p0.K);
+  if (nch > 0 && workspace && workspace_bytes >= need) {
+    TopkLaunch p = p0;
+    p.nchunks = nch;
+    p.chunk = kChunkLen;
+    p.cand = static_cast<int32_t*>(workspace);
+    hipLaunchKernelGGL((topk_kernel<16, true, kChunk>), dim3(p.rows * nch),
+                       dim3(kThreads), 0, stream, p);
+    const int slots = nch * p.K;   // <= 8 * 2048
+    if (slots <= 4 * kThreads)
+      hipLaunchKernelGGL((topk_kernel<4, true, kGather>), dim3(p.rows),
+                         dim3(kThreads), 0, stream, p);
+    else
+      hipLaunchKernelGGL((topk_kernel<16, true, kGather>), dim3(p.rows),
+                         dim3(kThreads), 0, stream, p);
+    return hipGetLastError();
+  }
+  return launch_topk(p0, stream);
+}
 
 hipError_t launch_topk(const TopkLaunch& p, hipStream_t stream) {
   // positions per row a workgroup covers: 1024 * KPT

@@ -60,6 +60,51 @@ def test_topk_lengths_and_distributions(L):
                 f"{kind} L={L} row {r} q_pos={q_pos[r, 0]}"
 
 
+@pytest.mark.parametrize("L", [65537, 100000, 131072])
+def test_topk_long_rows_one_workgroup_path(L):
+    """Rows past 64K positions without a workspace: one workgroup streams the
+    whole row (the chunk-candidate path is covered above)."""
+    rng = np.random.default_rng(2000 + L)
+    K = 2048
+    for kind in ("indexer_like", "few_values", "specials"):
+        x = _rows(kind, rng, 2, L)
+        q_pos = np.array([[L - 1], [int(rng.integers(K, L))]], dtype=np.int32)
+        scores = torch.from_numpy(x).view(2, 1, L).cuda()
+        idx = dsa.topk(scores, torch.from_numpy(q_pos).cuda(), K,
+                       workspace=torch.empty(0, dtype=torch.uint8,
+                                             device="cuda"))
+        torch.cuda.synchronize()
+        got = idx.cpu().numpy()
+        for r in range(2):
+            want = oracle.topk_row(x[r], int(q_pos[r, 0]), K)
+            assert np.array_equal(got[r, 0], want), f"{kind} L={L} row {r}"
+
+
+def test_topk_long_rows_chunk_boundaries():
+    """Candidate lists of 16K-position chunks: equal scores straddling chunk
+    boundaries, selections concentrated in one chunk, causal extents ending
+    inside a chunk, and K = 1."""
+    rng = np.random.default_rng(31)
+    L = 70000
+    x = np.zeros((4, L), dtype=np.float32)
+    x[0] = 1.0
+    x[0, 16384 - 1000:16384 + 1000] = 2.0        # 2000 equal keys across a boundary
+    x[1] = rng.standard_normal(L).astype(np.float32)
+    x[1, 49152:49152 + 3000] += 100.0           # the whole Top-K in one chunk
+    x[2] = rng.integers(0, 3, L).astype(np.float32)
+    x[3] = rng.standard_normal(L).astype(np.float32)
+    q_pos = np.array([[L - 1], [L - 1], [40000], [16383 + 5]], dtype=np.int32)
+    scores = torch.from_numpy(x).view(4, 1, L).cuda()
+    qp = torch.from_numpy(q_pos).cuda()
+    for K in (2048, 1, 777):
+        idx = dsa.topk(scores, qp, K)
+        torch.cuda.synchronize()
+        got = idx.cpu().numpy()
+        for r in range(4):
+            want = oracle.topk_row(x[r], int(q_pos[r, 0]), K)
+            assert np.array_equal(got[r, 0], want), f"K={K} row {r}"
+
+
 def test_topk_many_rows_prefill_shape():
     """Many rows with staggered causal extents in one launch (the prefill
     chunk's row structure), unaligned row length."""
