@@ -50,6 +50,107 @@ struct KeyLayout {
   }
 };
 
+// FP8 keys (stream path): the e4m3 codes go to LDS as they are (16-byte
+// chunk c of key n at chunk slot c ^ swz(n) of the key's DI-byte row) and
+// are dequantised when read as MFMA operands.  The features are taken in
+// the order that lets a lane read one whole chunk per two k-steps: k-step
+// 2j+s, operand half h covers features (2j+h)*16 + 8s .. +8, for the queries
+// (A operands) and the keys (B operands) alike.  The chunk of a lane then
+// lies in MX block j, whose scale is byte j of the key's scale word.
+template <int DI>
+struct CodeLayout {
+  static constexpr int kChunks = DI / 16;           // 16-B code chunks per key
+  static constexpr int kLoads = kSub * DI / (16 * kWave);
+  __device__ static __forceinline__ int slot(int n, int c) {
+    return c ^ (kChunks == 8 ? ((n >> 1) & 7) : ((n >> 2) & 3));
+  }
+};
+
+template <int DI>
+struct StageF8 {
+  uint4 v[CodeLayout<DI>::kLoads];
+  uint32_t sc;   // scale codes of key (lane % 32) of the stage, block j in byte j
+};
+
+template <int DI>
+__device__ __forceinline__ void stage_load_f8(StageF8<DI>& st,
+                                              const CacheView& kc, int b,
+                                              int kbase, int lane) {
+  using CL = CodeLayout<DI>;
+  int64_t row0;
+  bool clamp = false;
+  if (kc.page_table != nullptr) {
+    row0 = cache_row(kc.page_table, kc.max_pages, kc.L, b, kbase);
+  } else {
+    row0 = (int64_t)b * kc.L + kbase;
+    clamp = kbase + kSub > kc.L;
+  }
+#pragma unroll
+  for (int i = 0; i < CL::kLoads; ++i) {
+    const int id = i * kWave + lane;
+    const int n = id / CL::kChunks, c = id % CL::kChunks;
+    int64_t row = row0 + n;
+    if (clamp) row = (int64_t)b * kc.L + min(kbase + n, kc.L - 1);
+    st.v[i] = ld16(kc.data + row * DI + c * 16);
+  }
+  {
+    const int n = lane & 31;
+    int64_t row = row0 + n;
+    if (clamp) row = (int64_t)b * kc.L + min(kbase + n, kc.L - 1);
+    if constexpr (DI == 128)
+      st.sc = *reinterpret_cast<const uint32_t*>(kc.scale + row * 4);
+    else
+      st.sc = *reinterpret_cast<const uint16_t*>(kc.scale + row * 2);
+  }
+}
+
+template <int DI>
+__device__ __forceinline__ void stage_store_f8(const StageF8<DI>& st,
+                                               uint4* tile, int lane) {
+  using CL = CodeLayout<DI>;
+#pragma unroll
+  for (int i = 0; i < CL::kLoads; ++i) {
+    const int id = i * kWave + lane;
+    const int n = id / CL::kChunks, c = id % CL::kChunks;
+    tile[n * CL::kChunks + CL::slot(n, c)] = st.v[i];
+  }
+}
+
+// tile_scores for a code tile; `sc` holds the scale codes of key lane % 32.
+template <int DI, int MB>
+__device__ __forceinline__ float tile_scores_f8(const uint4* tile,
+                                                const uint4 (&a)[MB][DI / 16],
+                                                const float (&wv)[MB][16],
+                                                uint32_t sc, int lane) {
+  using CL = CodeLayout<DI>;
+  const int n = lane & 31, h = lane >> 5;
+  f32x16 acc[MB];
+#pragma unroll
+  for (int m = 0; m < MB; ++m) acc[m] = f32x16{};
+  // all of the lane's code chunks first: one LDS wait per tile
+  uint4 cvs[DI / 32];
+#pragma unroll
+  for (int j = 0; j < DI / 32; ++j)
+    cvs[j] = tile[n * CL::kChunks + CL::slot(n, 2 * j + h)];
+#pragma unroll
+  for (int j = 0; j < DI / 32; ++j) {
+    const uint4 cv = cvs[j];
+    const uint32_t e = (sc >> (8 * j)) & 0xffu;
+    const uint4 b0 = dequant8_e4m3(make_uint2(cv.x, cv.y), e);
+    const uint4 b1 = dequant8_e4m3(make_uint2(cv.z, cv.w), e);
+#pragma unroll
+    for (int m = 0; m < MB; ++m) acc[m] = mfma32(a[m][2 * j], b0, acc[m]);
+#pragma unroll
+    for (int m = 0; m < MB; ++m) acc[m] = mfma32(a[m][2 * j + 1], b1, acc[m]);
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int m = 0; m < MB; ++m)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s += wv[m][r] * fmaxf(acc[m][r], 0.f);
+  return s + swap_halves(s);
+}
+
 // Registers holding one 32-key stage on its way from HBM to LDS.
 template <int DI, bool FP8>
 struct Stage {
@@ -140,7 +241,9 @@ __device__ __forceinline__ float tile_scores(const uint4* tile,
 
 // Loads one query's indexer vectors as MFMA A operands and its head weights
 // in accumulator-row layout (heads >= H_I contribute zero).
-template <int DI, int MB>
+// CHUNKED: the feature order of the FP8 code tiles (k-step 2j+s, half h =
+// features (2j+h)*16 + 8s); otherwise k-step ks, half h = ks*16 + 8h.
+template <int DI, int MB, bool CHUNKED = false>
 __device__ __forceinline__ void load_query(const uint16_t* q_idx,
                                            const float* w, int H_I, int lane,
                                            uint4 (&a)[MB][DI / 16],
@@ -150,9 +253,11 @@ __device__ __forceinline__ void load_query(const uint16_t* q_idx,
   for (int m = 0; m < MB; ++m) {
     const int head = m * 32 + m32;
 #pragma unroll
-    for (int ks = 0; ks < DI / 16; ++ks)
-      a[m][ks] = head < H_I ? ld16(q_idx + head * DI + ks * 16 + h * 8)
+    for (int ks = 0; ks < DI / 16; ++ks) {
+      const int f = CHUNKED ? ((ks & ~1) + h) * 16 + (ks & 1) * 8 : ks * 16 + h * 8;
+      a[m][ks] = head < H_I ? ld16(q_idx + head * DI + f)
                             : make_uint4(0, 0, 0, 0);
+    }
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int hr = m * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
@@ -201,36 +306,59 @@ __global__ __launch_bounds__(256, 2) void indexer_stream_kernel(
   uint4 a[MB][DI / 16];
   float wv[MB][16];
   const int64_t qrow = (int64_t)b * p.T + t;
-  load_query<DI, MB>(p.q_idx + qrow * p.H_I * DI, p.w + qrow * p.H_I, p.H_I,
-                     lane, a, wv);
+  load_query<DI, MB, FP8>(p.q_idx + qrow * p.H_I * DI, p.w + qrow * p.H_I,
+                          p.H_I, lane, a, wv);
 
   uint4* tile = lds[wave];
   // Every iteration issues the same loads and stores (the tail re-reads the
   // last stage, an L2 hit, and its scores are masked), so the compiler can
   // count them and wait only for the stage it consumes.
   const int last = nsub - 1;
-  Stage<DI, FP8> s0, s1;
-  stage_load<DI, FP8>(s0, p.keys, b, k0, lane);
-  stage_load<DI, FP8>(s1, p.keys, b, k0 + min(1, last) * kSub, lane);
   float* sb = sbuf[wave];
   const auto flush = [&](int from, int to) {   // positions [from, to)
     for (int s = from + lane; s < to; s += kWave) srow[s] = sb[(s - k0) % kFlush];
   };
-  for (int i = 0; i < nsub; i += 2) {
-    stage_store<DI, FP8>(s0, tile, lane);
-    stage_load<DI, FP8>(s0, p.keys, b, k0 + min(i + 2, last) * kSub, lane);
-    {
-      const float sc = tile_scores<DI, MB>(tile, a, wv, lane);
-      if (lane < 32) sb[(i * kSub + lane) % kFlush] = sc + 0.0f;
+  if constexpr (FP8) {
+    // stages are half the bytes of bf16 ones: four in flight
+    StageF8<DI> st[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      stage_load_f8<DI>(st[u], p.keys, b, k0 + min(u, last) * kSub, lane);
+    for (int i = 0; i < nsub; i += 4) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        stage_store_f8<DI>(st[u], tile, lane);
+        const uint32_t scs = st[u].sc;
+        stage_load_f8<DI>(st[u], p.keys, b, k0 + min(i + u + 4, last) * kSub,
+                          lane);
+        const float sc = tile_scores_f8<DI, MB>(tile, a, wv, scs, lane);
+        // stages past the end (re-read tail) are not buffered
+        if (lane < 32 && i + u < nsub)
+          sb[((i + u) * kSub + lane) % kFlush] = sc + 0.0f;
+      }
+      if ((i + 4) * kSub % kFlush == 0 && i + 4 < nsub)   // a full buffer
+        flush(k0 + (i + 4) * kSub - kFlush, k0 + (i + 4) * kSub);
     }
-    stage_store<DI, FP8>(s1, tile, lane);
-    stage_load<DI, FP8>(s1, p.keys, b, k0 + min(i + 3, last) * kSub, lane);
-    {
-      const float sc = tile_scores<DI, MB>(tile, a, wv, lane);
-      if (lane < 32) sb[((i + 1) * kSub + lane) % kFlush] = sc + 0.0f;
+  } else {
+    Stage<DI, FP8> s0, s1;
+    stage_load<DI, FP8>(s0, p.keys, b, k0, lane);
+    stage_load<DI, FP8>(s1, p.keys, b, k0 + min(1, last) * kSub, lane);
+    for (int i = 0; i < nsub; i += 2) {
+      stage_store<DI, FP8>(s0, tile, lane);
+      stage_load<DI, FP8>(s0, p.keys, b, k0 + min(i + 2, last) * kSub, lane);
+      {
+        const float sc = tile_scores<DI, MB>(tile, a, wv, lane);
+        if (lane < 32) sb[(i * kSub + lane) % kFlush] = sc + 0.0f;
+      }
+      stage_store<DI, FP8>(s1, tile, lane);
+      stage_load<DI, FP8>(s1, p.keys, b, k0 + min(i + 3, last) * kSub, lane);
+      {
+        const float sc = tile_scores<DI, MB>(tile, a, wv, lane);
+        if (lane < 32) sb[((i + 1) * kSub + lane) % kFlush] = sc + 0.0f;
+      }
+      if ((i + 2) * kSub % kFlush == 0 && i + 2 < nsub)   // a full buffer
+        flush(k0 + (i + 2) * kSub - kFlush, k0 + (i + 2) * kSub);
     }
-    if ((i + 2) * kSub % kFlush == 0 && i + 2 < nsub)   // a full buffer
-      flush(k0 + (i + 2) * kSub - kFlush, k0 + (i + 2) * kSub);
   }
   const int done = (nsub - 1) / (kFlush / kSub) * kFlush;   // flushed so far
   flush(k0 + done, kend);

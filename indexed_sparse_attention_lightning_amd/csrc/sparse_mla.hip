@@ -658,6 +658,9 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_kernel(
 
 // Merge split partials: out = sum_s w_s * (O_s / l_s) / sum_s w_s with
 // w_s = l_s * 2^(m_s - M), M the largest m_s; lse = ln(2^M * sum_s w_s).
+// Every load of a thread (all splits' (m, l), then all splits' partial
+// values) is issued before any is used: the splits' latencies overlap.
+constexpr int kMaxSplits = 16;
 __global__ __launch_bounds__(128) void combine_kernel(AttnLaunch p,
                                                       int splits) {
   const int token = blockIdx.x, head = blockIdx.y;
@@ -666,25 +669,40 @@ __global__ __launch_bounds__(128) void combine_kernel(AttnLaunch p,
   const uint16_t* po = reinterpret_cast<const uint16_t*>(p.partial);
   const float* ml = reinterpret_cast<const float*>(po + nslots * kValue);
   const int64_t slot0 = (int64_t)token * splits * p.H + head;
+  float2 mls[kMaxSplits];
+#pragma unroll
+  for (int sp = 0; sp < kMaxSplits; ++sp)
+    mls[sp] = sp < splits
+                  ? *reinterpret_cast<const float2*>(ml + 2 * (slot0 + (int64_t)sp * p.H))
+                  : make_float2(-__builtin_inff(), 0.f);
+  uint2 v[kMaxSplits];
+#pragma unroll
+  for (int sp = 0; sp < kMaxSplits; ++sp)
+    v[sp] = sp < splits
+                ? *reinterpret_cast<const uint2*>(po + (slot0 + (int64_t)sp * p.H) * kValue + dv)
+                : make_uint2(0u, 0u);
   float M = -__builtin_inff();
-  for (int sp = 0; sp < splits; ++sp) {
-    const float m = ml[2 * (slot0 + (int64_t)sp * p.H)];
+#pragma unroll
+  for (int sp = 0; sp < kMaxSplits; ++sp) {
+    const float m = mls[sp].x;
     M = (m != m || M != M) ? __builtin_nanf("") : fmaxf(M, m);
   }
   float wsum = 0.f;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   if (M != -__builtin_inff() && M == M) {
-    for (int sp = 0; sp < splits; ++sp) {
-      const int64_t slot = slot0 + (int64_t)sp * p.H;
-      const float m = ml[2 * slot], l = ml[2 * slot + 1];
-      if (m == -__builtin_inff() || !(l > 0.f)) continue;
-      const float f = l * exp2f(m - M);
+#pragma unroll
+    for (int sp = 0; sp < kMaxSplits; ++sp) {
+      const float m = mls[sp].x, l = mls[sp].y;
+      // splits without rows (m = -inf) or beyond `splits` weigh nothing
+      const float f = (m == -__builtin_inff() || !(l > 0.f)) ? 0.f
+                                                             : l * exp2f(m - M);
       wsum += f;
-      const uint2 v = *reinterpret_cast<const uint2*>(po + slot * kValue + dv);
-      acc.x += f * __builtin_bit_cast(float, v.x << 16);
-      acc.y += f * __builtin_bit_cast(float, v.x & 0xffff0000u);
-      acc.z += f * __builtin_bit_cast(float, v.y << 16);
-      acc.w += f * __builtin_bit_cast(float, v.y & 0xffff0000u);
+      if (f > 0.f) {   // a skipped split's values are never read
+        acc.x += f * __builtin_bit_cast(float, v[sp].x << 16);
+        acc.y += f * __builtin_bit_cast(float, v[sp].x & 0xffff0000u);
+        acc.z += f * __builtin_bit_cast(float, v[sp].y << 16);
+        acc.w += f * __builtin_bit_cast(float, v[sp].y & 0xffff0000u);
+      }
     }
   }
   const float inv = wsum > 0.f ? 1.0f / wsum : 0.f;
@@ -704,7 +722,7 @@ int attn_splits(int tokens, int K) {
   const int tiles = (K + kRowsT - 1) / kRowsT;
   int s = (256 + tokens - 1) / tokens;
   s = s < 1 ? 1 : s;
-  s = s > 16 ? 16 : s;
+  s = s > kMaxSplits ? kMaxSplits : s;   // the combine holds up to kMaxSplits
   s = s > tiles ? tiles : s;
   return s;
 }

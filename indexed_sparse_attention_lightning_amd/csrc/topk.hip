@@ -402,11 +402,22 @@ __global__ __launch_bounds__(kThreads, 1) void topk_kernel(TopkLaunch p) {
       (void)j;
       if (rk != 0u) atomicAdd(&sm.hist[rk >> nsh], 1u);   // rk <= range < 2^sh0
     };
+    // only waves that reach past n (or hold candidate-slot holes) have
+    // keys to skip; the others count without the test
+    const bool padded = MODE == kGather || keys.wbase + KPT * kWave > n;
     if constexpr (RES) {
+      if (padded) {
 #pragma unroll
-      for (int j = 0; j < KPT; ++j) {
-        count(j, keys.k[j]);
-        TOPK_STEP_FENCE(j);
+        for (int j = 0; j < KPT; ++j) {
+          count(j, keys.k[j]);
+          TOPK_STEP_FENCE(j);
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < KPT; ++j) {
+          atomicAdd(&sm.hist[keys.k[j] >> nsh], 1u);
+          TOPK_STEP_FENCE(j);
+        }
       }
     } else {
       keys.stream(nsteps, count);
@@ -416,9 +427,11 @@ __global__ __launch_bounds__(kThreads, 1) void topk_kernel(TopkLaunch p) {
     pick_digit(sm.hist, nb, rem, sm, 0, tid, lane, wave, d0, above, cnt0);
     rem -= above;
   }
-  // digit d0 spans relative keys [blo, bhi]
+  // digit d0 spans relative keys [blo, bhi]; blo1 leaves out the key 0 of
+  // lanes past n
   const uint32_t blo = d0 << nsh;
   const uint32_t bhi = blo | ((1u << nsh) - 1u);
+  const uint32_t blo1 = blo > 1u ? blo : 1u;
 
   // ---- sweep: bitmap of keys in larger digits; keys in digit d0 are
   // final (nsh == 0: they all equal the threshold) or go to the wave's
@@ -431,7 +444,7 @@ __global__ __launch_bounds__(kThreads, 1) void topk_kernel(TopkLaunch p) {
 #pragma unroll
   for (int i = 0; i < kMaskRegs; ++i) gwr[i] = ewr[i] = 0u;
   const auto sweep = [&](int j, uint32_t rk) {
-    const bool in = rk != 0u && rk >= blo && rk <= bhi;
+    const bool in = rk >= blo1 && rk <= bhi;
     const uint64_t g = __ballot(rk > bhi);
     const uint64_t c = __ballot(in);
     if constexpr (RES) {
@@ -515,7 +528,7 @@ __global__ __launch_bounds__(kThreads, 1) void topk_kernel(TopkLaunch p) {
       } else {
         const auto count = [&](int j, uint32_t rk) {
           (void)j;
-          const bool in = rk != 0u && rk >= lo && rk - lo < win;
+          const bool in = rk >= (lo > 1u ? lo : 1u) && rk - lo < win;
           if (__ballot(in) != 0ull && in)
             atomicAdd(&sm.hist[(rk - lo) >> psh], 1u);
         };
