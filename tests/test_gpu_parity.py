@@ -46,6 +46,11 @@ SMALL = {
     "prefill_small_dims": wk.scaled(W["prefill"], T=19, L=700, first_pos=600,
                                     top_k=128, H=16, H_I=20, d_I=64,
                                     quantized=True, seed=108),
+    # few tokens, long selections: the most attention splits per token
+    "few_tokens_long_k": wk.scaled(W["decode"], B=2, L=4096, top_k=2048,
+                                   H=64, seed=110),
+    "paged_fp8_long_k": wk.scaled(W["ragged"], B=1, L_min=3000, L_max=5000,
+                                  top_k=1536, seed=111),
     # causal skipping of whole stages, rows shorter than K
     "prefill_from_start": wk.scaled(W["prefill"], T=130, L=640, first_pos=0,
                                     top_k=64, H=16, seed=109),
