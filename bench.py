@@ -246,6 +246,10 @@ def main(argv=None):
                     help="skip the prefill-chunk kernel timings")
     ap.add_argument("--no-configs", action="store_true",
                     help="skip the FP8 and ragged decode configurations")
+    ap.add_argument("--only-config", choices=["decode_fp8", "ragged"],
+                    help="time only this decode configuration (10 steps after "
+                         "3 warm-up steps) and print its JSON object; for "
+                         "kernel traces")
     ap.add_argument("--kernels-only", action="store_true",
                     help="run one 256 MiB device copy (counter calibration) "
                          "and one decode step, then exit (for rocprofv3 "
@@ -261,6 +265,12 @@ def main(argv=None):
     import indexed_sparse_attention_lightning_amd as dsa
     import workloads as wk
     from workloads.device import to_device
+
+    if args.only_config:
+        res = decode_config(args.only_config, torch.cuda.current_stream(),
+                            steps=10, warmup=3)
+        print(json.dumps({"config": args.only_config, **res}), flush=True)
+        return 0
 
     wl = wk.WORKLOADS["decode"]
     inp = wk.generate(wl)

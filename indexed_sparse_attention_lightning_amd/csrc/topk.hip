@@ -13,6 +13,11 @@
 // [w*KPT*64, (w+1)*KPT*64), lane l position w*KPT*64 + j*64 + l of step j,
 // so one compare-and-ballot covers 64 consecutive positions.  Rows of up to
 // 64K positions keep their keys in registers for the whole selection.
+// Longer rows, given a workspace, go in two launches: one workgroup per
+// 16K-position chunk selects the chunk's own Top-K into a candidate list,
+// then one workgroup per row selects from its chunks' lists (the row's Top-K
+// lies in their union, and list order is position order); without the
+// workspace one workgroup streams the whole row through each pass.
 //
 // The exact K-th largest key `thr` is found digit by digit, with the digits
 // cut from the row's own key range [min, max] rather than from fixed bit
