@@ -36,9 +36,7 @@ constexpr int kThreads = 256;
 constexpr int kRowsT = 32;                      // rows per tile
 constexpr int kSlotsRow = kLatent * 2 / 16;     // 72 bf16 chunks per row
 constexpr int kTileSlots = kRowsT * kSlotsRow;  // 2304
-constexpr int kCodeSlotsRow = kLatent / 16;     // 36 fp8 chunks per row
-constexpr int kCodeTileSlots = kRowsT * kCodeSlotsRow;  // 1152
-constexpr int kCodeSegs = 20;                   // 18 real 64-lane segments + 2
+constexpr int kCodeSegs = 20;                   // 18 code blocks + 2 dummies
 constexpr int kStageSlots = kCodeSegs * kWave;  // 1280
 constexpr int kMaxSplitRows = 2048;
 constexpr int kStageRow = kValue + 16;   // staged half partial row (bytes)
@@ -82,13 +80,6 @@ __device__ __forceinline__ void barrier(bool lds) {
   if (lds) __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
-}
-
-// The lane id behind an empty asm: values derived from it are recomputed
-// where used instead of being hoisted into long-lived registers.
-__device__ __forceinline__ int opaque(int x) {
-  asm volatile("" : "+v"(x));
-  return x;
 }
 
 struct Split {
@@ -194,44 +185,63 @@ __device__ __forceinline__ void issue_bf16(const AttnLaunch& p, const Split& s,
   }
 }
 
-// FP8: codes (linear, 36 chunks per row) by DMA, the scale code each of this
-// thread's conversion slots needs into registers.
+// FP8 code staging: block (cb, hb) of 64 slots holds code chunks
+// 4cb..4cb+3 of rows 16hb..16hb+15, chunk c of row R at in-block slot
+// (R%16)*4 + ((c%4) ^ ((R/4)%4)), so that one chunk of 16 rows is read
+// without bank conflicts.  36 chunks x 32 rows = 18 blocks; wave w loads
+// blocks w, w+4, .. (hb = w%2 for all of them: one row per lane), blocks 18
+// and 19 are dummies (a copy of 16 and 17 into spare slots) so that every
+// wave issues five loads per tile.
+__device__ __forceinline__ int code_slot(int R, int c) {
+  return ((c >> 2) * 2 + (R >> 4)) * 64 + (R & 15) * 4 + ((c & 3) ^ ((R >> 2) & 3));
+}
+
+// FP8: code blocks by DMA; the scale codes of this lane's conversion slots
+// (row lane%32, MX blocks 4k + wave) into registers.
 template <bool BUF>
 __device__ __forceinline__ void issue_fp8(const AttnLaunch& p, const Split& s,
                                           __amdgpu_buffer_rsrc_t rsrc, int j,
                                           uint4* dst, uint32_t (&sc)[5],
                                           int wave) {
-  const int lane = opaque(lane_id());
-  const int tid = wave * kWave + lane;
-#pragma unroll
-  for (int k = 0; k < kCodeSegs / 4; ++k) {
-    const int seg = k * 4 + wave;
-    const int q = min(seg * kWave + lane, kCodeTileSlots - 1);
-    const int R = q / kCodeSlotsRow, c = q % kCodeSlotsRow;
+  const int lane = lane_id();
+  {
+    const int R = 16 * (wave & 1) + (lane >> 2);
     int ent = s.rows[j * kRowsT + R];
-    ent = ent >= 0 ? ent : ~ent;
-    dma16<BUF>(p.kv.data, rsrc, (uint64_t)(uint32_t)ent * kLatent + c * 16,
-               dst + seg * kWave);
+    ent ^= ent >> 31;   // ~row for masked entries
+    const uint64_t off = (uint64_t)(uint32_t)ent * kLatent +
+                         ((lane & 3) ^ ((R >> 2) & 3)) * 16;
+#pragma unroll
+    for (int k = 0; k < 5; ++k) {
+      const int b = wave + 4 * k;                    // 18, 19: dummies
+      const int cb = (b < 18 ? b : b - 2) >> 1;
+      dma16<BUF>(p.kv.data, rsrc, off + cb * 64, dst + b * kWave);
+    }
   }
+  {
+    int ent = s.rows[j * kRowsT + (lane & 31)];
+    ent ^= ent >> 31;
+    const uint8_t* srow = p.kv.scale + (int64_t)ent * (kLatent / 32);
 #pragma unroll
-  for (int k = 0; k < 5; ++k) {
-    const int q = min(tid + k * kThreads, kCodeTileSlots - 1);
-    const int R = q / kCodeSlotsRow, c = q % kCodeSlotsRow;
-    int ent = s.rows[j * kRowsT + R];
-    ent = ent >= 0 ? ent : ~ent;
-    sc[k] = p.kv.scale[(int64_t)ent * (kLatent / 32) + (c >> 1)];
+    for (int k = 0; k < 5; ++k) {
+      const int blk = 4 * k + wave;
+      sc[k] = srow[blk < kLatent / 32 ? blk : blk - 4];
+    }
   }
 }
 
-// FP8 staging -> bf16 swizzled tile (exact: e4m3 * 2^k fits bf16).
+// FP8 staging -> bf16 swizzled tile (exact: e4m3 * 2^k fits bf16).  Lane l
+// of wave w converts row l%32, code chunks c = 8k + 2w + l/32 (k = 0..4,
+// c < 36): 16 lanes read one chunk of 16 rows and write two chunks of the
+// same rows, conflict-free both ways.
 __device__ __forceinline__ void convert_fp8(const uint4* stg, uint4* tile,
-                                            const uint32_t (&sc)[5], int tid) {
+                                            const uint32_t (&sc)[5], int wave,
+                                            int lane) {
+  const int R = lane & 31;
 #pragma unroll
   for (int k = 0; k < 5; ++k) {
-    const int q = tid + k * kThreads;
-    if (q < kCodeTileSlots) {
-      const int R = q / kCodeSlotsRow, c = q % kCodeSlotsRow;
-      const uint4 v = stg[q];
+    const int c = 8 * k + 2 * wave + (lane >> 5);
+    if (k < 4 || wave < 2) {   // c < 36 (wave-uniform)
+      const uint4 v = stg[code_slot(R, c)];
       tile[kv_slot(R, 2 * c)] = dequant8_e4m3(make_uint2(v.x, v.y), sc[k]);
       tile[kv_slot(R, 2 * c + 1)] = dequant8_e4m3(make_uint2(v.z, v.w), sc[k]);
     }
@@ -556,7 +566,7 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_kernel(
       if (j < s.ntiles) {
         const uint4* tile = cur;
         if constexpr (FP8) {
-          convert_fp8(cur, ftile, scc, tid);
+          convert_fp8(cur, ftile, scc, wave, lane);
           barrier(true);
           tile = ftile;
         }
