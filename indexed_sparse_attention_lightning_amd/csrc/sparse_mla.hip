@@ -581,7 +581,8 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_kernel(
             compute_tile(tile, qrow, vmask, st, sl2, lane, tl);
           }
         }
-        if constexpr (FP8) barrier(false);   // ftile is rewritten next step
+        // FP8: the barrier at the start of the next step also keeps its
+        // conversion from overwriting ftile while a wave still reads it
       }
     };
     const int nsteps = (s.ntiles + 2) / 3 * 3;
