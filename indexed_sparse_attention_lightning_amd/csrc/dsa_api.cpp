@@ -256,6 +256,7 @@ dsa_status dsa_decode_step(int B, int T, int H_I, int d_I, int H, int K,
   ia.qp = qp;
   ia.scores = scores;
   ia.row_len = max_seq_len;
+  ia.keys_out = 1;   // the Top-K below reads keys: no conversion there
   if (hipError_t e = dsa::launch_indexer(ia, st))
     return hip_status(e, "dsa_decode_step: indexer");
 
@@ -263,6 +264,7 @@ dsa_status dsa_decode_step(int B, int T, int H_I, int d_I, int H, int K,
   ta.rows = (int)tokens; ta.T = T; ta.L = max_seq_len; ta.K = K;
   ta.scores = scores;
   ta.qp = qp;
+  ta.keys_in = 1;
   ta.idx = idx;
   if (hipError_t e = dsa::launch_topk(ta, topk_ws, topk_bytes, st))
     return hip_status(e, "dsa_decode_step: topk");

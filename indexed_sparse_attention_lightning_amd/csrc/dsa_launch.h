@@ -42,6 +42,7 @@ struct IndexerLaunch {
   QueryPos qp;
   float* scores;           // [B*T, row_len]
   int row_len;             // positions written per row (L or max_seq_len)
+  int keys_out;            // store score_key(score) bit patterns, not scores
 };
 hipError_t launch_indexer(const IndexerLaunch& a, hipStream_t stream);
 
@@ -52,6 +53,7 @@ struct TopkLaunch {
   int32_t* idx;            // [rows, K]
   int nchunks, chunk;      // long rows: chunks per row, positions per chunk
   int32_t* cand;           // long rows: [rows, nchunks, K] candidate lists
+  int keys_in;             // scores holds score_key bit patterns already
 };
 // One workgroup per row.
 hipError_t launch_topk(const TopkLaunch& a, hipStream_t stream);

@@ -151,6 +151,12 @@ __device__ __forceinline__ float tile_scores_f8(const uint4* tile,
   return s + swap_halves(s);
 }
 
+// The value stored for a score: the score (+0 folds -0), or, for the fused
+// path whose Top-K reads keys, its order-preserving key bit pattern.
+__device__ __forceinline__ float out_val(const IndexerLaunch& p, float sc) {
+  return p.keys_out ? __builtin_bit_cast(float, score_key(sc)) : sc + 0.0f;
+}
+
 // Registers holding one 32-key stage on its way from HBM to LDS.
 template <int DI, bool FP8>
 struct Stage {
@@ -298,7 +304,7 @@ __global__ __launch_bounds__(256, 2) void indexer_stream_kernel(
 
   // positions past the query are masked
   for (int s = max(k0, qpos + 1) + lane; s < k1; s += kWave)
-    srow[s] = -__builtin_inff();
+    srow[s] = out_val(p, -__builtin_inff());
   const int kend = min(k1, qpos + 1);
   if (kend <= k0) return;
   const int nsub = (kend - k0 + kSub - 1) / kSub;
@@ -334,7 +340,7 @@ __global__ __launch_bounds__(256, 2) void indexer_stream_kernel(
         const float sc = tile_scores_f8<DI, MB>(tile, a, wv, scs, lane);
         // stages past the end (re-read tail) are not buffered
         if (lane < 32 && i + u < nsub)
-          sb[((i + u) * kSub + lane) % kFlush] = sc + 0.0f;
+          sb[((i + u) * kSub + lane) % kFlush] = out_val(p, sc);
       }
       if ((i + 4) * kSub % kFlush == 0 && i + 4 < nsub)   // a full buffer
         flush(k0 + (i + 4) * kSub - kFlush, k0 + (i + 4) * kSub);
@@ -348,13 +354,13 @@ __global__ __launch_bounds__(256, 2) void indexer_stream_kernel(
       stage_load<DI, FP8>(s0, p.keys, b, k0 + min(i + 2, last) * kSub, lane);
       {
         const float sc = tile_scores<DI, MB>(tile, a, wv, lane);
-        if (lane < 32) sb[(i * kSub + lane) % kFlush] = sc + 0.0f;
+        if (lane < 32) sb[(i * kSub + lane) % kFlush] = out_val(p, sc);
       }
       stage_store<DI, FP8>(s1, tile, lane);
       stage_load<DI, FP8>(s1, p.keys, b, k0 + min(i + 3, last) * kSub, lane);
       {
         const float sc = tile_scores<DI, MB>(tile, a, wv, lane);
-        if (lane < 32) sb[((i + 1) * kSub + lane) % kFlush] = sc + 0.0f;
+        if (lane < 32) sb[((i + 1) * kSub + lane) % kFlush] = out_val(p, sc);
       }
       if ((i + 2) * kSub % kFlush == 0 && i + 2 < nsub)   // a full buffer
         flush(k0 + (i + 2) * kSub - kFlush, k0 + (i + 2) * kSub);
@@ -466,7 +472,7 @@ __global__ __launch_bounds__(kTileQ * kWave, 2) void indexer_tile_kernel(
   float* srow = has_q ? p.scores + ((int64_t)b * p.T + t) * p.row_len : nullptr;
   if (has_q)
     for (int s = max(c0, qpos + 1) + lane; s < c1; s += kWave)
-      srow[s] = -__builtin_inff();
+      srow[s] = out_val(p, -__builtin_inff());
   const int kend = min(c1, qmax + 1);
   if (kend <= c0) return;   // workgroup-uniform
   const int nst = (kend - c0 + kStageKeys - 1) / kStageKeys;
@@ -492,7 +498,7 @@ __global__ __launch_bounds__(kTileQ * kWave, 2) void indexer_tile_kernel(
         const float sc = tile_scores<DI, MB>(tile + u * kSub * KL::kChunks, a,
                                              wv, lane);
         const int s = kb + (lane & 31);
-        if (lane < 32 && s <= qpos && s < c1) srow[s] = sc + 0.0f;
+        if (lane < 32 && s <= qpos && s < c1) srow[s] = out_val(p, sc);
       }
     }
   }

@@ -191,6 +191,12 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v,
 // again from the score row.  Lanes past the row's n candidates get r = 0,
 // which the histograms and candidate lists skip (one compare; no position
 // test).
+// A loaded row value as a key: the scores' keys, or the value itself when
+// the row already holds keys (the fused path's indexer writes them).
+__device__ __forceinline__ uint32_t as_key(uint32_t raw, bool keys_in) {
+  return keys_in ? raw : score_key(__builtin_bit_cast(float, raw));
+}
+
 template <int KPT, bool RES>
 struct RowKeys {
   uint32_t k[RES ? KPT : 1];
@@ -199,6 +205,7 @@ struct RowKeys {
   int wbase;        // first position of the wave (uniform)
   int lane;
   uint32_t kmin;
+  bool keys_in;
 
   // compares the lane against a uniform bound: no per-step registers
   __device__ __forceinline__ bool valid(int j) const {
@@ -211,7 +218,7 @@ struct RowKeys {
     if constexpr (RES) {
       return k[j];
     } else {
-      return valid(j) ? score_key(row[pos(j)]) - kmin : 0u;
+      return valid(j) ? as_key(__builtin_bit_cast(uint32_t, row[pos(j)]), keys_in) - kmin : 0u;
     }
   }
 
@@ -239,8 +246,7 @@ struct RowKeys {
       for (int u = 0; u < kChunk; ++u) {
         const int j = j0 + u;
         if (j < nsteps)   // wave-uniform
-          f(j, valid(j) ? score_key(__builtin_bit_cast(float, cur[u])) - kmin
-                        : 0u);
+          f(j, valid(j) ? as_key(cur[u], keys_in) - kmin : 0u);
       }
 #pragma unroll
       for (int u = 0; u < kChunk; ++u) cur[u] = nxt[u];
@@ -301,6 +307,7 @@ __global__ __launch_bounds__(kThreads, 1) void topk_kernel(TopkLaunch p) {
 
   RowKeys<KPT, RES> keys;
   keys.row = rowp;
+  keys.keys_in = p.keys_in != 0;
   keys.n = n;
   keys.wbase = wave * KPT * kWave;
   keys.lane = lane;
@@ -335,8 +342,7 @@ __global__ __launch_bounds__(kThreads, 1) void topk_kernel(TopkLaunch p) {
             rs, (uint32_t)ps[j] * 4u, 0, 0);
 #pragma unroll
       for (int j = 0; j < KPT; ++j) {
-        keys.k[j] = ps[j] >= 0
-                        ? score_key(__builtin_bit_cast(float, keys.k[j])) : 0u;
+        keys.k[j] = ps[j] >= 0 ? as_key(keys.k[j], keys.keys_in) : 0u;
         mn = min(mn, keys.k[j] - 1u);
         mx = max(mx, keys.k[j]);
       }
@@ -348,10 +354,21 @@ __global__ __launch_bounds__(kThreads, 1) void topk_kernel(TopkLaunch p) {
         keys.k[j] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(
             rs, (keys.wbase + lane) * 4, j * kWave * 4, 0);
       // keys of candidates are >= 1 (NaN maps to 1): 0 marks a lane past n
+      // (only waves that reach past n test positions; the conversion is
+      // skipped when the row holds keys)
+      const bool padded = keys.wbase + KPT * kWave > n;   // wave-uniform
+      const bool kin = keys.keys_in;
+      if (padded) {
+#pragma unroll
+        for (int j = 0; j < KPT; ++j)
+          keys.k[j] = keys.valid(j) ? as_key(keys.k[j], kin) : 0u;
+      } else if (!kin) {
+#pragma unroll
+        for (int j = 0; j < KPT; ++j)
+          keys.k[j] = score_key(__builtin_bit_cast(float, keys.k[j]));
+      }
 #pragma unroll
       for (int j = 0; j < KPT; ++j) {
-        keys.k[j] = keys.valid(j)
-                        ? score_key(__builtin_bit_cast(float, keys.k[j])) : 0u;
         mn = min(mn, keys.k[j] - 1u);
         mx = max(mx, keys.k[j]);
       }
