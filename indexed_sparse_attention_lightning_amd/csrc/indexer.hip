@@ -484,12 +484,15 @@ __global__ __launch_bounds__(kTileQ * kWave, 2) void indexer_tile_kernel(
     load_query<DI, MB>(p.q_idx + qrow * p.H_I * DI, p.w + qrow * p.H_I, p.H_I,
                        lane, a, wv);
   }
-  TileStage<DI, FP8> st;
-  tile_load<DI, FP8>(st, p.keys, b, c0, tid);
-  for (int i = 0; i < nst; ++i) {
+  // two stages in flight in registers: stage i+2 loads while stage i is
+  // computed (the tail re-loads the last stage, whose loads are never stored)
+  TileStage<DI, FP8> st[2];
+  tile_load<DI, FP8>(st[0], p.keys, b, c0, tid);
+  tile_load<DI, FP8>(st[1], p.keys, b, c0 + min(1, nst - 1) * kStageKeys, tid);
+  const auto stage = [&](int i, TileStage<DI, FP8>& sr) {
     uint4* tile = lds[i & 1];
-    tile_store<DI, FP8>(st, tile, tid);
-    if (i + 1 < nst) tile_load<DI, FP8>(st, p.keys, b, c0 + (i + 1) * kStageKeys, tid);
+    tile_store<DI, FP8>(sr, tile, tid);
+    tile_load<DI, FP8>(sr, p.keys, b, c0 + min(i + 2, nst - 1) * kStageKeys, tid);
     __syncthreads();
 #pragma unroll
     for (int u = 0; u < kStageKeys / kSub; ++u) {
@@ -501,7 +504,13 @@ __global__ __launch_bounds__(kTileQ * kWave, 2) void indexer_tile_kernel(
         if (lane < 32 && s <= qpos && s < c1) srow[s] = out_val(p, sc);
       }
     }
+  };
+  int i = 0;
+  for (; i + 1 < nst; i += 2) {
+    stage(i, st[0]);
+    stage(i + 1, st[1]);
   }
+  if (i < nst) stage(i, st[0]);
 }
 
 template <int DI, int MB, bool FP8>
