@@ -317,6 +317,25 @@ def main(argv=None):
     ms, ms_pct = time_loop(step, args.steps, args.warmup, stream,
                            per_call=True)
 
+    # the same steps replayed from HIP graphs (one captured step per replica)
+    graphs = []
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        for r in range(REPLICAS):
+            step(r)
+    stream.wait_stream(side)
+    torch.cuda.synchronize()
+    for r in range(REPLICAS):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step(r)
+        graphs.append(g)
+    torch.cuda.synchronize()
+    ms_graph = time_loop(lambda i: graphs[i % REPLICAS].replay(), args.steps,
+                         args.warmup, stream)
+    del graphs
+
     # per-kernel timing of the three stages through the separate entry points
     scores = [torch.empty((wl.B, 1, L), device="cuda") for _ in range(REPLICAS)]
 
@@ -367,6 +386,7 @@ def main(argv=None):
         "warmup": args.warmup,
         "ms_per_step": round(ms, 5),
         "ms_per_step_percentiles": ms_pct,
+        "ms_per_step_graph_replay": round(ms_graph, 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
