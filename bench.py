@@ -62,7 +62,7 @@ def step_bytes_general(wl, lens):
     return tot
 
 
-def decode_config(name, stream, steps=20, warmup=5):
+def decode_config(name, stream, steps=20, warmup=5, oracle_budget_s=0.0):
     """ms per dsa_decode_step call for another decode configuration, with
     enough input replicas rotating that a step's operands (over 1 GB in
     total) are not served from the 256 MB Infinity Cache."""
@@ -107,6 +107,8 @@ def decode_config(name, stream, steps=20, warmup=5):
            "input_replicas": nrep}
     del reps, caches, base, ws
     torch.cuda.empty_cache()
+    if oracle_budget_s > 0:
+        res["cpu_oracle"] = oracle_rate(inp, oracle_budget_s)
     return res
 
 
@@ -186,7 +188,21 @@ def cpu_baseline(inp, budget_s=12.0):
                       f"{inp.L} keys, top-k, attention), {dt:.1f} s"}
 
 
-def prefill_kernels(stream, steps=5, warmup=2):
+def oracle_rate(inp, budget_s=4.0):
+    """The CPU oracle on whole query rows of `inp` (rows in order, cycling)
+    for about `budget_s` seconds: query rows per second."""
+    import oracle
+    allrows = [(b, t) for b in range(inp.wl.B) for t in range(inp.wl.T)]
+    n, t0 = 0, time.perf_counter()
+    while time.perf_counter() - t0 < budget_s:
+        oracle.decode_path(inp, rows=[allrows[n % len(allrows)]])
+        n += 1
+    dt = time.perf_counter() - t0
+    return {"value": round(n / dt, 2), "unit": "query rows/s",
+            "kind": "oracle", "sample": f"{n} query rows, {dt:.1f} s"}
+
+
+def prefill_kernels(stream, steps=5, warmup=2, oracle_budget_s=0.0):
     """The prefill chunk (4096 queries at positions 61440..65535 of a
     65536-token bf16 context, 64 indexer heads x 128, top_k 2048, 128 MLA
     heads) through the three separate entry points, each timed on its own.
@@ -232,6 +248,8 @@ def prefill_kernels(stream, steps=5, warmup=2):
                              "algorithmic_flop": idx_flop},
         "attn_tflops": round(attn_tf, 1),
         "attn_frac_of_bf16_peak": round(attn_tf / PEAK_BF16_TFLOPS, 4),
+        **({"cpu_oracle": oracle_rate(inp, oracle_budget_s)}
+           if oracle_budget_s > 0 else {}),
         "tokens_per_s": round(wl.T / ((ms_i + ms_t + ms_a) * 1e-3), 1),
     }
 
@@ -415,16 +433,21 @@ def main(argv=None):
     }
     del reps, caches, outs, scores
     if not args.no_prefill:
-        line["prefill"] = prefill_kernels(stream)
+        line["prefill"] = prefill_kernels(
+            stream, oracle_budget_s=0 if args.no_cpu_baseline else 4.0)
     if not args.no_configs:
         line["other_configs"] = {
             "decode_fp8": dict(workload="batch 32 x 32768, e4m3 indexer keys "
                                "and MXFP8 latent KV (block 32, e8m0 scales), "
-                               "top_k 2048", **decode_config("decode_fp8", stream)),
+                               "top_k 2048", **decode_config(
+                                   "decode_fp8", stream,
+                                   oracle_budget_s=0 if args.no_cpu_baseline else 4.0)),
             "ragged": dict(workload="batch 4, lengths uniform in [16384, "
                            "131072], 64-token pages scattered by a seeded "
                            "page table, FP8 keys and MXFP8 KV, top_k 2048",
-                           **decode_config("ragged", stream)),
+                           **decode_config(
+                               "ragged", stream,
+                               oracle_budget_s=0 if args.no_cpu_baseline else 4.0)),
         }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(inp)
