@@ -29,6 +29,14 @@ a sparse-attention architecture; "DSA" is its indexed sparse attention):
   the format MXFP8).  Decoding follows the OCP e4m3fn / e8m0 definitions.
 * Paged key cache read through a page table: "Optimizing Inference ..."
   page, section 3 ("reading the paged key cache directly").
+* Cache quantization on append (the step that writes a new token's indexer
+  key and latent row into the paged pools): per-group dynamic scaling,
+  scale = max|group| / quant_max and q = round(x / scale), groups of 32 for
+  the indexer keys, tiles of 128 per token for the main KV -- page "Day-0
+  Inference Adaptation and Performance Optimization for New-Architecture
+  Large Language Models", section "Tiered Quantization" (its table and
+  pseudocode); page "Inference Adaptation and Performance Optimization for
+  New Large Language Model Architectures", sections 4.2 and 4.3.
 
 Every function here is pinned by tests that do not re-type its formula
 (brute force in pure Python, torch's fp8/bf16 decoders, torch's dense SDPA,
@@ -83,6 +91,22 @@ def dequant_mx32(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
     return v * s
 
 
+# The main-KV "tile" storage: each 576-wide latent row is cut into
+# consecutive 128-element tiles; the last one holds the remaining 64 (rope)
+# features.  One fp32 scale per tile.
+T128_EDGES = (0, 128, 256, 384, 512, 576)
+
+
+def dequant_t128(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """Tile dequantisation of [..., 576] e4m3fn codes with [..., 5] fp32
+    scales: element i of a row is e4m3(code[i]) times its tile's scale."""
+    v = decode_e4m3fn(codes)
+    s = np.asarray(scales).astype(np.float64)
+    assert v.shape[-1] == T128_EDGES[-1] and s.shape[-1] == len(T128_EDGES) - 1
+    widths = np.diff(T128_EDGES)
+    return v * np.repeat(s, widths, axis=-1)
+
+
 # ------------------------------------------------------------ cache reading
 
 def cache_rows(data, scale, quantized, page_table_row, positions,
@@ -90,13 +114,17 @@ def cache_rows(data, scale, quantized, page_table_row, positions,
     """Rows of one sequence's paged cache at logical ``positions``.
 
     The physical slot of logical position s is page page_table_row[s // 64],
-    row s % 64.  ``data`` is [num_pages, page_size, width]; ``scale`` is
-    [num_pages, page_size, width/32] e8m0 codes when ``quantized``.
+    row s % 64.  ``data`` is [num_pages, page_size, width].  ``quantized``
+    names the storage: False (bf16 bits), True or "mx32" (e4m3 codes with
+    ``scale`` [num_pages, page_size, width/32] e8m0 codes) or "t128" (e4m3
+    codes with ``scale`` [num_pages, page_size, 5] fp32 tile scales).
     Returns float64 [len(positions), width].
     """
     pos = np.asarray(positions, dtype=np.int64)
     page = np.asarray(page_table_row, dtype=np.int64)[pos // page_size]
     slot = pos % page_size
+    if quantized == "t128":
+        return dequant_t128(data[page, slot], scale[page, slot])
     if quantized:
         return dequant_mx32(data[page, slot], scale[page, slot])
     return decode_bf16(data[page, slot])
@@ -229,3 +257,121 @@ def decode_path(inp, rows=None, want_scores=False):
     if want_scores:
         res["scores"] = scores
     return res
+
+
+# ------------------------------------------- cache quantization and append
+
+E4M3_MAX = 448.0       # largest finite e4m3fn magnitude (the "quant_max")
+
+
+def round_to_e4m3fn(y) -> np.ndarray:
+    """Codes (uint8) of the e4m3fn values nearest to ``y`` (finite inputs).
+
+    Nearest among the 127 finite non-negative magnitudes, ties to the code
+    whose mantissa is even (round half to even); magnitudes beyond 448 take
+    448 (saturation: the format has no infinity).  The sign bit is the sign
+    of y, also for zero.
+    """
+    y = np.asarray(y, dtype=np.float64)
+    assert np.isfinite(y).all()
+    table = decode_e4m3fn(np.arange(0x7F))          # increasing in the code
+    a = np.abs(y)
+    hi = np.minimum(np.searchsorted(table, a, side="left"), 0x7E)
+    lo = np.maximum(hi - 1, 0)
+    d_hi = table[hi] - a
+    d_lo = a - table[lo]
+    take_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0))
+    mag = np.where(take_hi, hi, lo)
+    return (mag | np.where(np.signbit(y), 0x80, 0)).astype(np.uint8)
+
+
+def quantize_mx32(x):
+    """MX block-32 quantisation of the last axis of ``x`` (float values).
+
+    The pages scale each group by max|group| / quant_max; an e8m0 scale must
+    be a power of two, so the group takes the smallest 2^X (X >= -127) with
+    448 * 2^X >= max|group| -- the power-of-two reading in which no element
+    needs saturating.  An all-zero group takes X = 0.  Elements are rounded
+    to the nearest e4m3fn of x / 2^X.  Returns (codes uint8 [..., n], scale
+    codes uint8 [..., n/32] = X + 127).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    n = x.shape[-1]
+    assert n % 32 == 0
+    blocks = x.reshape(*x.shape[:-1], n // 32, 32)
+    amax = np.abs(blocks).max(axis=-1)
+    cand = np.arange(-127, 128)
+    fits = np.ldexp(E4M3_MAX, cand) >= amax[..., None]
+    assert fits[..., -1].all()
+    X = np.where(amax > 0, cand[np.argmax(fits, axis=-1)], 0)
+    codes = round_to_e4m3fn(blocks / np.ldexp(1.0, X)[..., None])
+    return codes.reshape(x.shape), (X + 127).astype(np.uint8)
+
+
+def quantize_t128(x):
+    """Tile quantisation of [..., 576] rows (values exact in float32).
+
+    Per tile (T128_EDGES): scale = max|tile| / 448 and code = nearest
+    e4m3fn of x / scale, both divisions in IEEE float32 (the precision the
+    codes are decided in), magnitudes saturating at 448.  An all-zero tile
+    stores scale 0 and codes of x itself (signed zeros).  Returns (codes
+    uint8 [..., 576], scales float32 [..., 5]).
+    """
+    x32 = np.asarray(x, dtype=np.float32)
+    assert x32.shape[-1] == T128_EDGES[-1]
+    codes = np.empty(x32.shape, dtype=np.uint8)
+    scales = np.empty(x32.shape[:-1] + (len(T128_EDGES) - 1,),
+                      dtype=np.float32)
+    for i, (lo, hi) in enumerate(zip(T128_EDGES[:-1], T128_EDGES[1:])):
+        tile = x32[..., lo:hi]
+        amax = np.abs(tile).max(axis=-1)
+        scale = amax / np.float32(E4M3_MAX)
+        divisor = np.where(amax > 0, scale, np.float32(1.0))
+        with np.errstate(over="ignore"):
+            y = tile / divisor[..., None]
+        codes[..., lo:hi] = round_to_e4m3fn(
+            np.clip(y.astype(np.float64), -E4M3_MAX, E4M3_MAX))
+        scales[..., i] = scale
+    return codes, scales
+
+
+def quantize_rows(bits, fmt):
+    """Storage of bf16 rows (uint16 bits [..., width]) in format ``fmt``:
+    "bf16" (the bits themselves), "mx32" or "t128".  Returns (data, scale)
+    with scale None for bf16."""
+    if fmt == "bf16":
+        return np.asarray(bits, dtype=np.uint16).copy(), None
+    x = decode_bf16(bits)
+    if fmt == "mx32":
+        return quantize_mx32(x)
+    if fmt == "t128":
+        return quantize_t128(x)
+    raise ValueError(fmt)
+
+
+def cache_append(data, scale, fmt, page_table, pos, rows):
+    """Write new tokens' rows into a paged pool, in place.
+
+    ``rows`` [B, T, width] bf16 bits are quantised per ``fmt`` and stored at
+    the slot of logical position pos[b, t] of sequence b: page
+    page_table[b, pos // 64], row pos % 64.  Tokens with pos < 0, a
+    position past the page table or a page entry outside the pool are
+    skipped.  ``data`` [num_pages, 64, width] and ``scale`` (None for bf16)
+    are modified and returned.
+    """
+    page_table = np.asarray(page_table)
+    B, T = np.asarray(pos).shape
+    q, s = quantize_rows(rows, fmt)
+    num_pages = data.shape[0]
+    for b in range(B):
+        for t in range(T):
+            p = int(pos[b, t])
+            if p < 0 or p // 64 >= page_table.shape[1]:
+                continue
+            page = int(page_table[b, p // 64])
+            if page < 0 or page >= num_pages:
+                continue
+            data[page, p % 64] = q[b, t]
+            if s is not None:
+                scale[page, p % 64] = s[b, t]
+    return data, scale
