@@ -30,6 +30,15 @@
  *   32; the "Technical Deep Dive" page, section 2, names it MXFP8).  The
  *   value of element i of a row is e4m3(code[i]) * 2^(scale[i/32] - 127).
  *   Dequantisation is exact while the product is a normal bf16 number.
+ * - The latent KV may instead use the "tile" layout DSA_E4M3_T128 (page
+ *   "Inference Adaptation and Performance Optimization for New Large
+ *   Language Model Architectures", section 4.3: FP8 per token and head in
+ *   blocks of 128 elements; page "Day-0 Inference Adaptation and Performance
+ *   Optimization for New-Architecture Large Language Models", section
+ *   "Tiered Quantization", whose scale is max|tile| / quant_max): a row's
+ *   576 codes form tiles [0,128) [128,256) [256,384) [384,512) [512,576),
+ *   each with one fp32 scale, and element i is e4m3(code[i]) * scale[tile].
+ *   The attention rounds that fp32 product to bf16.
  * - `stream` is a hipStream_t (NULL = the legacy default stream).  Every call
  *   only enqueues kernels on it and returns.
  * - Errors: argument and shape checks run on the host before any HIP call and
@@ -65,7 +74,9 @@ typedef enum dsa_status {
 
 typedef enum dsa_dtype {
   DSA_BF16 = 0,             /* bfloat16 values                              */
-  DSA_E4M3_MX32 = 1         /* e4m3fn codes + one e8m0 scale per 32 values  */
+  DSA_E4M3_MX32 = 1,        /* e4m3fn codes + one e8m0 scale per 32 values  */
+  DSA_E4M3_T128 = 2         /* e4m3fn codes + one fp32 scale per 128-value
+                               tile of a 576-wide latent row (latent KV only) */
 } dsa_dtype;
 
 /* Operation selector for dsa_workspace_size. */
@@ -99,7 +110,8 @@ typedef struct dsa_paged_cache {
   const void* kidx;           /* [num_pages, 64, d_I] bf16 or e4m3 codes     */
   const uint8_t* kidx_scale;  /* [num_pages, 64, d_I/32] e8m0; NULL if bf16  */
   const void* kv;             /* [num_pages, 64, 576] bf16 or e4m3 codes     */
-  const uint8_t* kv_scale;    /* [num_pages, 64, 18] e8m0; NULL if bf16      */
+  const void* kv_scale;       /* [num_pages, 64, 18] e8m0 (MX32), [num_pages,
+                                 64, 5] fp32 (T128); NULL if bf16           */
   const int32_t* page_table;  /* [B, max_pages_per_seq] int32               */
   const int32_t* seq_lens;    /* [B] tokens in the cache, current ones incl. */
 } dsa_paged_cache;
@@ -144,8 +156,8 @@ dsa_status dsa_topk(int B, int T, int L, int K, const float* scores,
  * Sparse absorbed-MLA attention over selected latent rows of a contiguous
  * KV cache (step 3).
  *   q        [B, T, H, 576] bf16    absorbed queries (512 latent + 64 rope)
- *   kv       [B, L, 576]            bf16, or e4m3 codes if kv_dtype is MX
- *   kv_scale [B, L, 18] e8m0        (NULL unless kv_dtype == DSA_E4M3_MX32)
+ *   kv       [B, L, 576]            bf16, or e4m3 codes (MX32 / T128)
+ *   kv_scale [B, L, 18] e8m0 (MX32), [B, L, 5] fp32 (T128); NULL for bf16
  *   idx      [B, T, K] int32        selected positions; -1 entries skipped;
  *                                   valid entries must lie in [0, L)
  *   out      [B, T, H, 512] fp32    softmax-weighted sum of value rows
@@ -156,7 +168,7 @@ dsa_status dsa_topk(int B, int T, int L, int K, const float* scores,
  */
 dsa_status dsa_sparse_mla_attn(int B, int T, int L, int H, int K,
                                const void* q, const void* kv, int kv_dtype,
-                               const uint8_t* kv_scale, const int32_t* idx,
+                               const void* kv_scale, const int32_t* idx,
                                float softmax_scale, float* out, float* lse,
                                void* workspace, size_t workspace_bytes,
                                void* stream);
@@ -179,6 +191,45 @@ dsa_status dsa_decode_step(int B, int T, int H_I, int d_I, int H, int K,
                            const void* q, const int32_t* q_pos, float* out,
                            float* lse, int32_t* idx_out, void* workspace,
                            size_t workspace_bytes, void* stream);
+
+/*
+ * Store new tokens' indexer keys and latent rows into the paged pools -- the
+ * write that precedes the path for every new token -- quantising each row
+ * into its pool's format (pages: "Day-0 Inference Adaptation and
+ * Performance Optimization for New-Architecture Large Language Models",
+ * section "Tiered Quantization", per-group dynamic scaling with the scale
+ * max|group| / quant_max; "Inference Adaptation and Performance
+ * Optimization for New Large Language Model Architectures", sections 4.2
+ * and 4.3, groups of 32 for the index keys and 128-element tiles for the
+ * KV).
+ *   page_table [B, max_pages_per_seq] int32 (as in dsa_paged_cache)
+ *   pos        [B, T] int32: logical position of each new token; the row
+ *              goes to page page_table[b, pos / 64], row pos % 64.  Tokens
+ *              with pos < 0, pos >= 64 * max_pages_per_seq or a page entry
+ *              outside [0, num_pages) are skipped (nothing is written).
+ *   k_new      [B, T, d_I] bf16 or NULL (keys not appended); d_I in {64, 128}
+ *   kidx       [num_pages, 64, d_I] pool of dtype kidx_dtype (BF16 or MX32)
+ *   kidx_scale [num_pages, 64, d_I/32] e8m0 (MX32) or NULL
+ *   kv_new     [B, T, 576] bf16 or NULL (latent rows not appended)
+ *   kv         [num_pages, 64, 576] pool of dtype kv_dtype (any)
+ *   kv_scale   [num_pages, 64, 18] e8m0 (MX32), [num_pages, 64, 5] fp32
+ *              (T128), or NULL (BF16)
+ * BF16 pools receive the bits unchanged.  MX32 groups of 32 take the scale
+ * 2^X with X the smallest integer >= -127 such that 448 * 2^X >= the
+ * group's largest magnitude (X = 0 for an all-zero group); T128 tiles take
+ * the fp32 scale max|tile| / 448 (0 for an all-zero tile).  Codes are the
+ * nearest e4m3fn (ties to even) of x * 2^-X, resp. of x / scale computed
+ * with correctly rounded fp32 division and saturated at +-448; the sign bit
+ * is x's, also for zero.  Inputs must be finite.  The written bytes are a
+ * deterministic function of the inputs.  Tokens that map to the same slot
+ * race.  seq_lens is not touched: the caller advances it.
+ */
+dsa_status dsa_cache_append(int B, int T, int d_I, int num_pages,
+                            int max_pages_per_seq, const int32_t* page_table,
+                            const int32_t* pos, const void* k_new,
+                            int kidx_dtype, void* kidx, uint8_t* kidx_scale,
+                            const void* kv_new, int kv_dtype, void* kv,
+                            void* kv_scale, void* stream);
 
 /* Bytes of workspace an operation needs for these sizes (L = the context
  * length, or max_seq_len for DSA_OP_DECODE_STEP).  0 for an unknown op. */

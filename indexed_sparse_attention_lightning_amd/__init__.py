@@ -13,6 +13,8 @@ Entry points (same names as the C ABI, without the ``dsa_`` prefix):
 * ``topk``            per-row Top-K (ties to the lower position), ascending
 * ``sparse_mla_attn`` absorbed-MLA attention over selected latent rows
 * ``decode_step``     indexer -> Top-K -> attention over a paged cache
+* ``cache_append``    store new tokens' key / latent rows into the paged
+                      pools, quantised to each pool's format
 """
 from __future__ import annotations
 
@@ -25,13 +27,15 @@ from typing import Optional
 import torch
 
 __all__ = [
-    "DSA_BF16", "DSA_E4M3_MX32", "DsaError", "PagedCache", "decode_step",
-    "indexer_scores", "library_path", "sparse_mla_attn", "topk",
-    "workspace_size",
+    "DSA_BF16", "DSA_E4M3_MX32", "DSA_E4M3_T128", "DsaError", "PagedCache",
+    "cache_append", "decode_step", "indexer_scores", "library_path",
+    "sparse_mla_attn", "topk", "workspace_size",
 ]
 
 DSA_BF16 = 0
 DSA_E4M3_MX32 = 1
+DSA_E4M3_T128 = 2
+T128_TILES = 5
 OP_INDEXER_SCORES, OP_TOPK, OP_SPARSE_MLA, OP_DECODE_STEP = 0, 1, 2, 3
 LATENT, VALUE, PAGE = 576, 512, 64
 
@@ -72,6 +76,7 @@ def _load():
         "dsa_sparse_mla_attn": [I, I, I, I, I, P, P, I, P, P, F, P, P, P, S, P],
         "dsa_decode_step": [I, I, I, I, I, I, F, ctypes.POINTER(_PagedCacheC),
                             I, P, P, P, P, P, P, P, P, S, P],
+        "dsa_cache_append": [I, I, I, I, I, P, P, P, I, P, P, P, I, P, P, P],
         "dsa_workspace_size": [I, I, I, I, I, I],
         "dsa_status_string": [I],
         "dsa_last_error": [],
@@ -80,7 +85,7 @@ def _load():
         fn = getattr(lib, name)
         fn.argtypes = args
     for name in ("dsa_indexer_scores", "dsa_topk", "dsa_sparse_mla_attn",
-                 "dsa_decode_step"):
+                 "dsa_decode_step", "dsa_cache_append"):
         getattr(lib, name).restype = ctypes.c_int
     lib.dsa_workspace_size.restype = ctypes.c_size_t
     lib.dsa_status_string.restype = ctypes.c_char_p
@@ -128,16 +133,30 @@ def workspace_size(op: int, B: int, T: int, L: int, H: int, K: int) -> int:
     return int(_lib.dsa_workspace_size(op, B, T, L, H, K))
 
 
-def _cache_dtype(t: torch.Tensor, scale: Optional[torch.Tensor], name: str):
+def _cache_dtype(t: torch.Tensor, scale: Optional[torch.Tensor], name: str,
+                 tiles_ok: bool = False):
+    """Storage format of a cache tensor: bf16 values; uint8 e4m3 codes with
+    uint8 e8m0 group scales (MX32); or, for latent KV, uint8 codes with
+    float32 tile scales (T128)."""
     if t.dtype == torch.bfloat16:
         if scale is not None:
             raise ValueError(f"{name}: bf16 cache takes no scales")
         return DSA_BF16
     if t.dtype == torch.uint8:
         if scale is None:
-            raise ValueError(f"{name}: e4m3 codes need e8m0 scales")
-        return DSA_E4M3_MX32
+            raise ValueError(f"{name}: e4m3 codes need scales")
+        if scale.dtype == torch.uint8:
+            return DSA_E4M3_MX32
+        if scale.dtype == torch.float32 and tiles_ok:
+            return DSA_E4M3_T128
+        raise TypeError(f"{name}: scales must be uint8 e8m0"
+                        + (" or float32 tile scales" if tiles_ok else ""))
     raise TypeError(f"{name} must be bfloat16 or uint8 (e4m3 codes)")
+
+
+def _scale_shape(dtype: int, lead, width: int):
+    return (*lead, T128_TILES) if dtype == DSA_E4M3_T128 else \
+        (*lead, width // 32)
 
 
 def indexer_scores(q_idx: torch.Tensor, w: torch.Tensor, k_idx: torch.Tensor,
@@ -198,17 +217,18 @@ def sparse_mla_attn(q: torch.Tensor, kv: torch.Tensor, idx: torch.Tensor,
                     lse: Optional[torch.Tensor] = None,
                     workspace: Optional[torch.Tensor] = None):
     """Absorbed-MLA attention of q [B, T, H, 576] bf16 over the rows of
-    kv [B, L, 576] (bf16, or uint8 e4m3 codes with kv_scale [B, L, 18])
-    selected by idx [B, T, K] (-1 skipped).  Returns (out [B, T, H, 512]
-    fp32, lse [B, T, H] fp32)."""
+    kv [B, L, 576] (bf16, or uint8 e4m3 codes with kv_scale [B, L, 18]
+    uint8 e8m0 or [B, L, 5] float32 tile scales) selected by idx [B, T, K]
+    (-1 skipped).  Returns (out [B, T, H, 512] fp32, lse [B, T, H] fp32)."""
     B, T, H, D = q.shape
     L = kv.shape[1]
     K = idx.shape[2]
     _need(q, "q", torch.bfloat16, (B, T, H, LATENT))
-    kd = _cache_dtype(kv, kv_scale, "kv")
+    kd = _cache_dtype(kv, kv_scale, "kv", tiles_ok=True)
     _need(kv, "kv", kv.dtype, (B, L, LATENT))
     if kv_scale is not None:
-        _need(kv_scale, "kv_scale", torch.uint8, (B, L, LATENT // 32))
+        _need(kv_scale, "kv_scale", kv_scale.dtype,
+              _scale_shape(kd, (B, L), LATENT))
     _need(idx, "idx", torch.int32, (B, T, K))
     dev = q.device
     if out is None:
@@ -232,8 +252,9 @@ def sparse_mla_attn(q: torch.Tensor, kv: torch.Tensor, idx: torch.Tensor,
 class PagedCache:
     """One layer's paged cache: indexer keys and latent KV share one page
     table.  kidx [P, 64, d_I] and kv [P, 64, 576] are bf16, or uint8 e4m3
-    codes with kidx_scale [P, 64, d_I/32] / kv_scale [P, 64, 18] uint8 e8m0.
-    page_table [B, max_pages] int32; seq_lens [B] int32."""
+    codes with kidx_scale [P, 64, d_I/32] / kv_scale [P, 64, 18] uint8 e8m0;
+    kv may also take float32 tile scales kv_scale [P, 64, 5].  page_table
+    [B, max_pages] int32; seq_lens [B] int32."""
     kidx: torch.Tensor
     kv: torch.Tensor
     page_table: torch.Tensor
@@ -244,7 +265,7 @@ class PagedCache:
     def as_c(self) -> _PagedCacheC:
         P = self.kidx.shape[0]
         kd = _cache_dtype(self.kidx, self.kidx_scale, "kidx")
-        vd = _cache_dtype(self.kv, self.kv_scale, "kv")
+        vd = _cache_dtype(self.kv, self.kv_scale, "kv", tiles_ok=True)
         _need(self.kidx, "kidx", self.kidx.dtype)
         _need(self.kv, "kv", self.kv.dtype, (P, PAGE, LATENT))
         if self.kidx.dim() != 3 or self.kidx.shape[1] != PAGE:
@@ -253,7 +274,8 @@ class PagedCache:
             _need(self.kidx_scale, "kidx_scale", torch.uint8,
                   (P, PAGE, self.kidx.shape[2] // 32))
         if self.kv_scale is not None:
-            _need(self.kv_scale, "kv_scale", torch.uint8, (P, PAGE, LATENT // 32))
+            _need(self.kv_scale, "kv_scale", self.kv_scale.dtype,
+                  _scale_shape(vd, (P, PAGE), LATENT))
         _need(self.page_table, "page_table", torch.int32)
         _need(self.seq_lens, "seq_lens", torch.int32,
               (self.page_table.shape[0],))
@@ -301,6 +323,34 @@ def decode_step(cache: PagedCache, q_idx: torch.Tensor, w: torch.Tensor,
         _ptr(out), _ptr(lse), _ptr(idx_out), _ptr(workspace),
         workspace.numel(), _stream()), "dsa_decode_step")
     return out, lse, idx_out
+
+
+def cache_append(cache: PagedCache, pos: torch.Tensor,
+                 k_new: Optional[torch.Tensor] = None,
+                 kv_new: Optional[torch.Tensor] = None) -> None:
+    """Store new tokens into ``cache``'s pools, in place: k_new [B, T, d_I]
+    and / or kv_new [B, T, 576] bf16 rows go to the slots of the logical
+    positions pos [B, T] int32 (pos < 0 skipped), quantised to the pools'
+    formats.  seq_lens is left to the caller."""
+    if k_new is None and kv_new is None:
+        raise ValueError("cache_append: nothing to append")
+    c = cache.as_c()
+    _need(pos, "pos", torch.int32)
+    if pos.dim() != 2:
+        raise ValueError("pos must be [B, T]")
+    B, T = pos.shape
+    if cache.page_table.shape[0] != B:
+        raise ValueError("pos and page_table disagree on B")
+    d_I = cache.kidx.shape[2]
+    if k_new is not None:
+        _need(k_new, "k_new", torch.bfloat16, (B, T, d_I))
+    if kv_new is not None:
+        _need(kv_new, "kv_new", torch.bfloat16, (B, T, LATENT))
+    _check(_lib.dsa_cache_append(
+        B, T, d_I, c.num_pages, c.max_pages_per_seq, _ptr(cache.page_table),
+        _ptr(pos), _ptr(k_new), c.kidx_dtype, _ptr(cache.kidx),
+        _ptr(cache.kidx_scale), _ptr(kv_new), c.kv_dtype, _ptr(cache.kv),
+        _ptr(cache.kv_scale), _stream()), "dsa_cache_append")
 
 
 def default_softmax_scale() -> float:

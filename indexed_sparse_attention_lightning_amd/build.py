@@ -16,7 +16,8 @@ CSRC = os.path.join(PKG, "csrc")
 ROOT = os.path.dirname(PKG)
 LIB = os.path.join(PKG, "libdsa.so")
 BUILD = os.path.join(ROOT, "_build")
-SOURCES = ["dsa_api.cpp", "indexer.hip", "topk.hip", "sparse_mla.hip"]
+SOURCES = ["dsa_api.cpp", "indexer.hip", "topk.hip", "sparse_mla.hip",
+           "cache_append.hip"]
 ARCH = "gfx950"
 
 # Packed-fp32 instructions stay off: hipcc would otherwise emit them on its own.

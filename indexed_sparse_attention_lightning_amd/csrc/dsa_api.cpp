@@ -31,7 +31,20 @@ dsa_status ok() {
 constexpr size_t kAlign = 256;
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
-bool valid_dtype(int d) { return d == DSA_BF16 || d == DSA_E4M3_MX32; }
+// Indexer keys: bf16 or MX block-32; latent KV: any of the three formats.
+bool valid_key_dtype(int d) { return d == DSA_BF16 || d == DSA_E4M3_MX32; }
+bool valid_kv_dtype(int d) { return valid_key_dtype(d) || d == DSA_E4M3_T128; }
+
+dsa::CacheView kv_view(const void* data, const void* scale, int dtype,
+                       const int32_t* page_table, int max_pages, int L,
+                       uint64_t rows) {
+  const bool fp8 = dtype != DSA_BF16;
+  return dsa::CacheView{static_cast<const uint8_t*>(data),
+                        static_cast<const uint8_t*>(scale), page_table,
+                        max_pages, L, fp8,
+                        rows * DSA_LATENT_DIM * (fp8 ? 1 : 2),
+                        dtype == DSA_E4M3_T128};
+}
 
 // Grid limits: B*T query tokens index a grid dimension capped at 65535.
 constexpr int kMaxTokens = 65535;
@@ -112,8 +125,8 @@ dsa_status dsa_indexer_scores(int B, int T, int L, int H_I, int d_I,
   if (L < 1) return fail(DSA_ERR_SHAPE, "L must be >= 1");
   if ((long long)B * L > 0x7fffffffLL)
     return fail(DSA_ERR_UNSUPPORTED, "B*L must fit in int32");
-  if (!valid_dtype(k_dtype))
-    return fail(DSA_ERR_UNSUPPORTED, "unknown key dtype %d", k_dtype);
+  if (!valid_key_dtype(k_dtype))
+    return fail(DSA_ERR_UNSUPPORTED, "unsupported key dtype %d", k_dtype);
   const bool fp8 = k_dtype == DSA_E4M3_MX32;
   if (fp8 && !k_scale) return fail(DSA_ERR_NULL, "MX keys need k_scale");
   dsa::IndexerLaunch a{};
@@ -122,7 +135,7 @@ dsa_status dsa_indexer_scores(int B, int T, int L, int H_I, int d_I,
   a.w = w;
   a.keys = dsa::CacheView{static_cast<const uint8_t*>(k_idx), k_scale, nullptr,
                           0, L, fp8,
-                          (uint64_t)B * L * d_I * (fp8 ? 1 : 2)};
+                          (uint64_t)B * L * d_I * (fp8 ? 1 : 2), false};
   a.qp = dsa::QueryPos{q_pos, nullptr, T};
   a.scores = scores;
   a.row_len = L;
@@ -154,7 +167,7 @@ dsa_status dsa_topk(int B, int T, int L, int K, const float* scores,
 
 dsa_status dsa_sparse_mla_attn(int B, int T, int L, int H, int K,
                                const void* q, const void* kv, int kv_dtype,
-                               const uint8_t* kv_scale, const int32_t* idx,
+                               const void* kv_scale, const int32_t* idx,
                                float softmax_scale, float* out, float* lse,
                                void* workspace, size_t workspace_bytes,
                                void* stream) {
@@ -164,10 +177,10 @@ dsa_status dsa_sparse_mla_attn(int B, int T, int L, int H, int K,
   if (L < 1) return fail(DSA_ERR_SHAPE, "L must be >= 1");
   if ((long long)B * L > 0x7fffffffLL)
     return fail(DSA_ERR_UNSUPPORTED, "B*L must fit in int32");
-  if (!valid_dtype(kv_dtype))
+  if (!valid_kv_dtype(kv_dtype))
     return fail(DSA_ERR_UNSUPPORTED, "unknown kv dtype %d", kv_dtype);
-  const bool fp8 = kv_dtype == DSA_E4M3_MX32;
-  if (fp8 && !kv_scale) return fail(DSA_ERR_NULL, "MX KV needs kv_scale");
+  if (kv_dtype != DSA_BF16 && !kv_scale)
+    return fail(DSA_ERR_NULL, "FP8 KV needs kv_scale");
   const size_t need = dsa::attn_workspace_bytes(B * T, H, K);
   if (need && (!workspace || workspace_bytes < need))
     return fail(DSA_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", need,
@@ -175,9 +188,7 @@ dsa_status dsa_sparse_mla_attn(int B, int T, int L, int H, int K,
   dsa::AttnLaunch a{};
   a.B = B; a.T = T; a.H = H; a.K = K;
   a.q = static_cast<const uint16_t*>(q);
-  a.kv = dsa::CacheView{static_cast<const uint8_t*>(kv), kv_scale, nullptr, 0,
-                        L, fp8,
-                        (uint64_t)B * L * DSA_LATENT_DIM * (fp8 ? 1 : 2)};
+  a.kv = kv_view(kv, kv_scale, kv_dtype, nullptr, 0, L, (uint64_t)B * L);
   a.idx = idx;
   a.seq_lens = nullptr;
   a.scale = softmax_scale;
@@ -216,14 +227,13 @@ dsa_status dsa_decode_step(int B, int T, int H_I, int d_I, int H, int K,
       (long long)max_seq_len > (long long)cache->max_pages_per_seq * DSA_PAGE_SIZE)
     return fail(DSA_ERR_SHAPE,
                 "max_seq_len must be in [1, max_pages_per_seq * 64]");
-  if (!valid_dtype(cache->kidx_dtype) || !valid_dtype(cache->kv_dtype))
-    return fail(DSA_ERR_UNSUPPORTED, "unknown cache dtype");
+  if (!valid_key_dtype(cache->kidx_dtype) || !valid_kv_dtype(cache->kv_dtype))
+    return fail(DSA_ERR_UNSUPPORTED, "unsupported cache dtype");
   const bool kfp8 = cache->kidx_dtype == DSA_E4M3_MX32;
-  const bool vfp8 = cache->kv_dtype == DSA_E4M3_MX32;
   if (kfp8 && !cache->kidx_scale)
     return fail(DSA_ERR_NULL, "MX indexer keys need kidx_scale");
-  if (vfp8 && !cache->kv_scale)
-    return fail(DSA_ERR_NULL, "MX KV needs kv_scale");
+  if (cache->kv_dtype != DSA_BF16 && !cache->kv_scale)
+    return fail(DSA_ERR_NULL, "FP8 KV needs kv_scale");
   const size_t need = decode_ws(B, T, max_seq_len, H, K);
   if (!workspace || workspace_bytes < need)
     return fail(DSA_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", need,
@@ -252,7 +262,7 @@ dsa_status dsa_decode_step(int B, int T, int H_I, int d_I, int H, int K,
                            cache->kidx_scale, cache->page_table,
                            cache->max_pages_per_seq, 0, kfp8,
                            (uint64_t)cache->num_pages * DSA_PAGE_SIZE * d_I *
-                               (kfp8 ? 1 : 2)};
+                               (kfp8 ? 1 : 2), false};
   ia.qp = qp;
   ia.scores = scores;
   ia.row_len = max_seq_len;
@@ -272,11 +282,9 @@ dsa_status dsa_decode_step(int B, int T, int H_I, int d_I, int H, int K,
   dsa::AttnLaunch aa{};
   aa.B = B; aa.T = T; aa.H = H; aa.K = K;
   aa.q = static_cast<const uint16_t*>(q);
-  aa.kv = dsa::CacheView{static_cast<const uint8_t*>(cache->kv),
-                         cache->kv_scale, cache->page_table,
-                         cache->max_pages_per_seq, 0, vfp8,
-                         (uint64_t)cache->num_pages * DSA_PAGE_SIZE *
-                             DSA_LATENT_DIM * (vfp8 ? 1 : 2)};
+  aa.kv = kv_view(cache->kv, cache->kv_scale, cache->kv_dtype,
+                  cache->page_table, cache->max_pages_per_seq, 0,
+                  (uint64_t)cache->num_pages * DSA_PAGE_SIZE);
   aa.idx = idx;
   aa.seq_lens = cache->seq_lens;
   aa.scale = softmax_scale;
@@ -286,6 +294,60 @@ dsa_status dsa_decode_step(int B, int T, int H_I, int d_I, int H, int K,
   aa.splits = dsa::attn_splits((int)tokens, K);
   return hip_status(dsa::launch_sparse_mla(aa, st),
                     "dsa_decode_step: sparse attention");
+}
+
+dsa_status dsa_cache_append(int B, int T, int d_I, int num_pages,
+                            int max_pages_per_seq, const int32_t* page_table,
+                            const int32_t* pos, const void* k_new,
+                            int kidx_dtype, void* kidx, uint8_t* kidx_scale,
+                            const void* kv_new, int kv_dtype, void* kv,
+                            void* kv_scale, void* stream) {
+  if (!page_table || !pos)
+    return fail(DSA_ERR_NULL, "dsa_cache_append: NULL page_table or pos");
+  if (!k_new && !kv_new)
+    return fail(DSA_ERR_NULL, "dsa_cache_append: neither k_new nor kv_new");
+  if (B < 1 || T < 1) return fail(DSA_ERR_SHAPE, "B and T must be >= 1");
+  if ((long long)B * T > 0x7fffffffLL)
+    return fail(DSA_ERR_UNSUPPORTED, "B*T too large");
+  if (num_pages < 1 || max_pages_per_seq < 1)
+    return fail(DSA_ERR_SHAPE, "num_pages and max_pages_per_seq must be >= 1");
+  if ((long long)max_pages_per_seq * DSA_PAGE_SIZE > 0x7fffffffLL)
+    return fail(DSA_ERR_UNSUPPORTED, "max_pages_per_seq * 64 must fit in int32");
+  dsa::AppendLaunch a{};
+  a.tokens = B * T; a.T = T;
+  a.pos = pos;
+  a.page_table = page_table;
+  a.max_pages = max_pages_per_seq;
+  a.num_pages = num_pages;
+  if (k_new) {
+    if (d_I != 64 && d_I != 128)
+      return fail(DSA_ERR_UNSUPPORTED, "d_I must be 64 or 128, got %d", d_I);
+    if (!valid_key_dtype(kidx_dtype))
+      return fail(DSA_ERR_UNSUPPORTED, "unsupported key dtype %d", kidx_dtype);
+    if (!kidx) return fail(DSA_ERR_NULL, "k_new given without kidx pool");
+    if (kidx_dtype == DSA_E4M3_MX32 && !kidx_scale)
+      return fail(DSA_ERR_NULL, "MX indexer keys need kidx_scale");
+    a.d_I = d_I;
+    a.kidx_fmt = kidx_dtype == DSA_E4M3_MX32 ? dsa::kFmtMx32 : dsa::kFmtBf16;
+    a.k_new = static_cast<const uint16_t*>(k_new);
+    a.kidx = static_cast<uint8_t*>(kidx);
+    a.kidx_scale = kidx_scale;
+  }
+  if (kv_new) {
+    if (!valid_kv_dtype(kv_dtype))
+      return fail(DSA_ERR_UNSUPPORTED, "unknown kv dtype %d", kv_dtype);
+    if (!kv) return fail(DSA_ERR_NULL, "kv_new given without kv pool");
+    if (kv_dtype != DSA_BF16 && !kv_scale)
+      return fail(DSA_ERR_NULL, "FP8 KV needs kv_scale");
+    a.kv_fmt = kv_dtype == DSA_E4M3_T128   ? dsa::kFmtT128
+               : kv_dtype == DSA_E4M3_MX32 ? dsa::kFmtMx32
+                                           : dsa::kFmtBf16;
+    a.kv_new = static_cast<const uint16_t*>(kv_new);
+    a.kv = static_cast<uint8_t*>(kv);
+    a.kv_scale = kv_scale;
+  }
+  return hip_status(dsa::launch_cache_append(a, (hipStream_t)stream),
+                    "dsa_cache_append");
 }
 
 }  // extern "C"

@@ -45,12 +45,14 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
-// Eight e4m3fn codes (little-endian in a uint2) times 2^(scale_code - 127)
-// -> eight bf16 values (uint4).  The hardware conversion takes the scale as
-// the exponent field of an fp32.  Exact whenever the result is a normal bf16.
-__device__ __forceinline__ uint4 dequant8_e4m3(uint2 codes,
-                                               uint32_t scale_code) {
-  const float s = __builtin_bit_cast(float, scale_code << 23);
+// Eight e4m3fn codes (little-endian in a uint2) times the power of two whose
+// fp32 bit pattern is `pow2_bits` (an e8m0 scale code c gives c << 23) ->
+// eight bf16 values (uint4).  The hardware conversion uses only the exponent
+// field of its fp32 scale operand.  Exact whenever the result is a normal
+// bf16.
+__device__ __forceinline__ uint4 dequant8_pow2(uint2 codes,
+                                               uint32_t pow2_bits) {
+  const float s = __builtin_bit_cast(float, pow2_bits);
   uint4 r;
   r.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(
                                          codes.x, s, false));
@@ -61,6 +63,27 @@ __device__ __forceinline__ uint4 dequant8_e4m3(uint2 codes,
   r.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(
                                          codes.y, s, true));
   return r;
+}
+
+// The same with an e8m0 scale code: times 2^(scale_code - 127).
+__device__ __forceinline__ uint4 dequant8_e4m3(uint2 codes,
+                                               uint32_t scale_code) {
+  return dequant8_pow2(codes, scale_code << 23);
+}
+
+// Split of a non-negative fp32 scale s = 2^e * m for an exact bf16
+// dequantisation by the scaled conversion above, which applies only the
+// exponent field of its scale operand: returns the exponent part as the
+// fp32 bit pattern of 2^e (2^-126 for zero or subnormal s) and sets m = s /
+// 2^e (in [1, 2) for normal s; 1 for s = 0, where every code is zero).
+__device__ __forceinline__ uint32_t split_scale(uint32_t s_bits, float& m) {
+  const uint32_t e = s_bits & 0x7f800000u;
+  if (e != 0) {
+    m = __builtin_bit_cast(float, (s_bits & 0x007fffffu) | 0x3f800000u);
+    return e;
+  }
+  m = s_bits == 0 ? 1.0f : __builtin_bit_cast(float, s_bits) * 0x1p126f;
+  return 0x00800000u;
 }
 
 // 128-bit non-temporal-hint-free global load / LDS access helpers.

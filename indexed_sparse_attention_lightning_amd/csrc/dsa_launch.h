@@ -8,16 +8,24 @@
 
 namespace dsa {
 
+// Storage formats of a cache row: bf16; e4m3 codes with one e8m0 scale per
+// 32 features; e4m3 codes with one fp32 scale per 128-feature tile (a
+// 576-wide row has 5 tiles, the last of 64 features).
+constexpr int kFmtBf16 = 0, kFmtMx32 = 1, kFmtT128 = 2;
+constexpr int kT128Tiles = 5;
+
 // Where a query's history lives: either a contiguous [B, L, width] tensor
 // (page_table == nullptr) or a paged pool read through a page table.
 struct CacheView {
   const uint8_t* data;        // rows of `row_bytes` bytes
-  const uint8_t* scale;       // e8m0 codes, width/32 per row, or nullptr
+  const uint8_t* scale;       // e8m0 codes (width/32 per row), fp32 tile
+                              // scales (5 per row, t128) or nullptr
   const int32_t* page_table;  // [B, max_pages] or nullptr (contiguous)
   int max_pages;
   int L;                      // contiguous length (rows per sequence)
-  bool fp8;                   // e4m3 codes + MX-32 scales, else bf16
+  bool fp8;                   // e4m3 codes + scales, else bf16
   uint64_t bytes;             // size of `data` in bytes
+  bool t128;                  // fp8 with fp32 scales per 128-feature tile
 };
 
 // Query positions: q_pos[b*T + t] if given, else seq_lens[b] - 1; with
@@ -82,5 +90,22 @@ struct AttnLaunch {
 int attn_splits(int tokens, int K);
 size_t attn_workspace_bytes(int tokens, int H, int K);
 hipError_t launch_sparse_mla(const AttnLaunch& a, hipStream_t stream);
+
+struct AppendLaunch {
+  int tokens, T;               // tokens = B*T, T per sequence
+  const int32_t* pos;          // [tokens] logical positions; < 0 skipped
+  const int32_t* page_table;   // [B, max_pages]
+  int max_pages, num_pages;
+  int d_I, kidx_fmt;           // indexer keys: width, kFmtBf16 or kFmtMx32
+  const uint16_t* k_new;       // [tokens, d_I] bf16, or nullptr
+  uint8_t* kidx;               // pool [num_pages, 64, d_I]
+  void* kidx_scale;            // pool [num_pages, 64, d_I/32] e8m0
+  int kv_fmt;                  // latent rows: any format
+  const uint16_t* kv_new;      // [tokens, 576] bf16, or nullptr
+  uint8_t* kv;                 // pool [num_pages, 64, 576]
+  void* kv_scale;              // pool [num_pages, 64, 18] e8m0 or [.., 5] fp32
+};
+// One wave per token; tokens whose page is unmapped are skipped.
+hipError_t launch_cache_append(const AppendLaunch& a, hipStream_t stream);
 
 }  // namespace dsa

@@ -196,9 +196,10 @@ __device__ __forceinline__ int code_slot(int R, int c) {
   return ((c >> 2) * 2 + (R >> 4)) * 64 + (R & 15) * 4 + ((c & 3) ^ ((R >> 2) & 3));
 }
 
-// FP8: code blocks by DMA; the scale codes of this lane's conversion slots
-// (row lane%32, MX blocks 4k + wave) into registers.
-template <bool BUF>
+// FP8: code blocks by DMA; the scales of this lane's conversion slots (row
+// lane%32: MX blocks 4k + wave as e8m0 codes, or 128-feature tile k as fp32
+// bits) into registers.
+template <bool BUF, bool T128>
 __device__ __forceinline__ void issue_fp8(const AttnLaunch& p, const Split& s,
                                           __amdgpu_buffer_rsrc_t rsrc, int j,
                                           uint4* dst, uint32_t (&sc)[5],
@@ -220,30 +221,63 @@ __device__ __forceinline__ void issue_fp8(const AttnLaunch& p, const Split& s,
   {
     int ent = s.rows[j * kRowsT + (lane & 31)];
     ent ^= ent >> 31;
-    const uint8_t* srow = p.kv.scale + (int64_t)ent * (kLatent / 32);
+    if constexpr (T128) {
+      const uint32_t* srow =
+          reinterpret_cast<const uint32_t*>(p.kv.scale) + (int64_t)ent * kT128Tiles;
 #pragma unroll
-    for (int k = 0; k < 5; ++k) {
-      const int blk = 4 * k + wave;
-      sc[k] = srow[blk < kLatent / 32 ? blk : blk - 4];
+      for (int k = 0; k < 5; ++k) sc[k] = srow[k];
+    } else {
+      const uint8_t* srow = p.kv.scale + (int64_t)ent * (kLatent / 32);
+#pragma unroll
+      for (int k = 0; k < 5; ++k) {
+        const int blk = 4 * k + wave;
+        sc[k] = srow[blk < kLatent / 32 ? blk : blk - 4];
+      }
     }
   }
 }
 
-// FP8 staging -> bf16 swizzled tile (exact: e4m3 * 2^k fits bf16).  Lane l
-// of wave w converts row l%32, code chunks c = 8k + 2w + l/32 (k = 0..4,
-// c < 36): 16 lanes read one chunk of 16 rows and write two chunks of the
-// same rows, conflict-free both ways.
+// Tile-scale factors of a 32-row tile (T128), fp32 [9][32] in LDS, row-major
+// by tile row: rows 0..3 hold m_t / m_(t+1), row 4 m_4, rows 5..8 m_0..m_3,
+// where a row's scale of 128-feature tile t is s_t = 2^(e_t) * m_t and the
+// bf16 tile holds the exact code * 2^(e_t).
+constexpr int kTmulRows = 9;
+
+// FP8 staging -> bf16 swizzled tile, exact: e4m3 * 2^k fits bf16 (MX: the
+// group scale; T128: the exponent part of the tile scale, the mantissa part
+// m_t goes to `tmul`).  Lane l of wave w converts row l%32, code chunks c =
+// 8k + 2w + l/32 (k = 0..4, c < 36), which lie in 128-feature tile k: 16
+// lanes read one chunk of 16 rows and write two chunks of the same rows,
+// conflict-free both ways.
+template <bool T128>
 __device__ __forceinline__ void convert_fp8(const uint4* stg, uint4* tile,
                                             const uint32_t (&sc)[5], int wave,
-                                            int lane) {
+                                            int lane, float* tmul) {
   const int R = lane & 31;
+  float m[5];
+  uint32_t e[5];
+#pragma unroll
+  for (int k = 0; k < 5; ++k) {
+    if constexpr (T128) e[k] = split_scale(sc[k], m[k]);
+    else e[k] = sc[k] << 23;
+  }
+  if constexpr (T128) {
+    if (wave == 0 && lane < 32) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        tmul[t * 32 + R] = m[t] / m[t + 1];
+        tmul[(5 + t) * 32 + R] = m[t];
+      }
+      tmul[4 * 32 + R] = m[4];
+    }
+  }
 #pragma unroll
   for (int k = 0; k < 5; ++k) {
     const int c = 8 * k + 2 * wave + (lane >> 5);
     if (k < 4 || wave < 2) {   // c < 36 (wave-uniform)
       const uint4 v = stg[code_slot(R, c)];
-      tile[kv_slot(R, 2 * c)] = dequant8_e4m3(make_uint2(v.x, v.y), sc[k]);
-      tile[kv_slot(R, 2 * c + 1)] = dequant8_e4m3(make_uint2(v.z, v.w), sc[k]);
+      tile[kv_slot(R, 2 * c)] = dequant8_pow2(make_uint2(v.x, v.y), e[k]);
+      tile[kv_slot(R, 2 * c + 1)] = dequant8_pow2(make_uint2(v.z, v.w), e[k]);
     }
   }
 }
@@ -289,13 +323,59 @@ __device__ __forceinline__ void mfma32_vgpr_last(f32x16& c, const uint4& a,
       : "v"(__builtin_bit_cast(bf16x8, a)), "v"(__builtin_bit_cast(bf16x8, b)));
 }
 
+// A pair of chained products (one per chain) that start right after VALU
+// writes to their accumulators: the leading wait states cover the VALU-write
+// to matrix-core-read dependency.
+__device__ __forceinline__ void mfma32_pair_after_valu(f32x16& c0, const uint4& a0,
+                                                       const uint4& b0, f32x16& c1,
+                                                       const uint4& a1,
+                                                       const uint4& b1) {
+  asm("s_nop 4\n\t"
+      "v_mfma_f32_32x32x16_bf16 %0, %2, %3, %0\n\t"
+      "v_mfma_f32_32x32x16_bf16 %1, %4, %5, %1"
+      : "+v"(c0), "+v"(c1)
+      : "v"(__builtin_bit_cast(bf16x8, a0)), "v"(__builtin_bit_cast(bf16x8, b0)),
+        "v"(__builtin_bit_cast(bf16x8, a1)), "v"(__builtin_bit_cast(bf16x8, b1)));
+}
+// The last products of both chains, then enough wait states for VALU reads
+// of either accumulator.
+__device__ __forceinline__ void mfma32_pair_last(f32x16& c0, const uint4& a0,
+                                                 const uint4& b0, f32x16& c1,
+                                                 const uint4& a1, const uint4& b1) {
+  asm("v_mfma_f32_32x32x16_bf16 %0, %2, %3, %0\n\t"
+      "v_mfma_f32_32x32x16_bf16 %1, %4, %5, %1\n\t"
+      "s_nop 7\n\ts_nop 7\n\ts_nop 7"
+      : "+v"(c0), "+v"(c1)
+      : "v"(__builtin_bit_cast(bf16x8, a0)), "v"(__builtin_bit_cast(bf16x8, b0)),
+        "v"(__builtin_bit_cast(bf16x8, a1)), "v"(__builtin_bit_cast(bf16x8, b1)));
+}
+
+// Sixteen per-row factors of this lane's S^T rows 8(r/4) + 4h + r%4 from
+// row `a` of the T128 factor table.
+__device__ __forceinline__ void tile_factors(const float* tmul, int a, int h,
+                                             float (&f)[16]) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const float4 v = *reinterpret_cast<const float4*>(tmul + a * 32 + 8 * q + 4 * h);
+    f[4 * q] = v.x;
+    f[4 * q + 1] = v.y;
+    f[4 * q + 2] = v.z;
+    f[4 * q + 3] = v.w;
+  }
+}
+
 // One 32-row tile for this wave's 32 heads.  `vmask` bit R says whether tile
-// row R is a real selected row.
-template <class Loads>
+// row R is a real selected row.  T128: the tile holds code * 2^(e_t) and
+// row R's factor m_t(R) of 128-feature tile t enters exactly: the S^T chains
+// are rescaled by m_t / m_(t+1) at each tile boundary (k-step 8t) and by m_4
+// at the end, so S^T = sum_t m_t * S^T_t; for O^T the factor multiplies P
+// (rounded to bf16 with it) before the products of value tile t.
+template <bool T128, class Loads>
 __device__ __forceinline__ void compute_tile(const uint4* tile,
                                              const uint4* qrow, uint32_t vmask,
                                              HeadState& st, float sl2,
-                                             int lane, Loads& loads) {
+                                             int lane, Loads& loads,
+                                             const float* tmul) {
   const int n = lane & 31, h = lane >> 5;
   const char* tb = reinterpret_cast<const char*>(tile);
   loads.prepare();
@@ -324,6 +404,7 @@ __device__ __forceinline__ void compute_tile(const uint4* tile,
       bq[i] = b_at(i);
     }
     f32x16 acc1;
+    uint4 ap, bp;   // T128: the even operands of a pair issued together
 #pragma unroll
     for (int ks = 0; ks < kS; ++ks) {
       if (ks + kAhead < kS) {
@@ -335,15 +416,44 @@ __device__ __forceinline__ void compute_tile(const uint4* tile,
       if ((ks & 3) == 2) loads.block(ks >> 2);
       const uint4 a = aq[ks % (kAhead + 1)], b = bq[ks % (kAhead + 1)];
       f32x16& c = (ks & 1) ? acc1 : acc;
-      if (ks < 2)
-        mfma32_vgpr_first(c, a, b);
-      else if (ks + 2 < kS)
-        mfma32_vgpr(c, a, b);
-      else
-        mfma32_vgpr_last(c, a, b);
-    }
+      // T128: the first and last k-step pairs of each 128-feature tile
+      const bool pair_first = T128 && ks >= 8 && (ks & 7) < 2;
+      const bool pair_last = T128 && ((ks & 7) >= 6 || ks >= kS - 2);
+      if (pair_first || pair_last) {
+        if ((ks & 1) == 0) {
+          ap = a;
+          bp = b;
+        } else if (pair_first) {
+          mfma32_pair_after_valu(acc, ap, bp, acc1, a, b);
+        } else {
+          mfma32_pair_last(acc, ap, bp, acc1, a, b);
+          if (ks < kS - 2) {
+            float f[16];
+            tile_factors(tmul, ks >> 3, h, f);
 #pragma unroll
-    for (int r = 0; r < 16; ++r) acc[r] += acc1[r];
+            for (int r = 0; r < 16; ++r) {
+              acc[r] *= f[r];
+              acc1[r] *= f[r];
+            }
+          }
+        }
+      } else if (ks < 2) {
+        mfma32_vgpr_first(c, a, b);
+      } else if (T128 || ks + 2 < kS) {
+        mfma32_vgpr(c, a, b);
+      } else {
+        mfma32_vgpr_last(c, a, b);
+      }
+    }
+    if constexpr (T128) {
+      float f[16];
+      tile_factors(tmul, 4, h, f);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[r] = (acc[r] + acc1[r]) * f[r];
+    } else {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[r] += acc1[r];
+    }
   }
   // ---- online softmax (lane: head n, rows 8(r/4) + 4h + r%4 of the tile)
   if (vmask == 0xffffffffu) {   // every row of the tile is selected (uniform)
@@ -371,16 +481,18 @@ __device__ __forceinline__ void compute_tile(const uint4* tile,
   // below the largest p of the first valid tile.
   const float mref = st.m != -__builtin_inff() ? st.m : __builtin_inff();
   uint4 pb[2];
+  float pr[16];
 #pragma unroll
   for (int kk = 0; kk < 2; ++kk) {
-    float p[8];
+    float* p = pr + 8 * kk;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       p[e] = __builtin_amdgcn_exp2f(acc[8 * kk + e] - mref);
       st.l += p[e];
     }
-    pb[kk] = make_uint4(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
-                        pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7]));
+    if constexpr (!T128)
+      pb[kk] = make_uint4(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
+                          pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7]));
   }
   // ---- O^T += V^T . P^T with transposing LDS reads.  Lane (G = lane/16,
   // i = lane%16) supplies the address of row Ra = 16kk + 4h + i/4 (Rb = Ra+8
@@ -405,26 +517,48 @@ __device__ __forceinline__ void compute_tile(const uint4* tile,
       const uint2 ub = __builtin_bit_cast(uint2, lds_tr16(tb + ((t & 1) ? pb_o : pb_e) + off));
       return make_uint4(ua.x, ua.y, ub.x, ub.y);
     };
-    // V^T operands read three MFMAs ahead
+    // V^T operands read seven MFMAs ahead.  Product i covers k-half kk(i)
+    // and dv tile t(i); T128 orders them by 128-feature value tile (four dv
+    // tiles each) so that one scaled P serves eight products.
     constexpr int kN = 2 * (kValue / 32);   // 32 MFMAs
     constexpr int kAhead = 7;
+    auto kk_of = [](int i) { return T128 ? (i >> 2) & 1 : i / (kValue / 32); };
+    auto t_of = [](int i) {
+      return T128 ? 4 * (i >> 3) + (i & 3) : i % (kValue / 32);
+    };
     uint4 vq[kAhead + 1];
 #pragma unroll
-    for (int i = 0; i < kAhead; ++i) vq[i] = rd(i / (kValue / 32), i % (kValue / 32));
+    for (int i = 0; i < kAhead; ++i) vq[i] = rd(kk_of(i), t_of(i));
 #pragma unroll
     for (int i = 0; i < kN; ++i) {
       if (i + kAhead < kN)
-        vq[(i + kAhead) % (kAhead + 1)] =
-            rd((i + kAhead) / (kValue / 32), (i + kAhead) % (kValue / 32));
-      const int kk = i / (kValue / 32), t = i % (kValue / 32);
-      st.o[t] = mfma32(vq[i % (kAhead + 1)], pb[kk], st.o[t]);
+        vq[(i + kAhead) % (kAhead + 1)] = rd(kk_of(i + kAhead), t_of(i + kAhead));
+      if constexpr (T128) {
+        if ((i & 7) == 0) {
+          float f[16];
+          tile_factors(tmul, 5 + (i >> 3), h, f);
+#pragma unroll
+          for (int kk = 0; kk < 2; ++kk) {
+            const float* q = pr + 8 * kk;
+            const float* g = f + 8 * kk;
+            pb[kk] = make_uint4(pack_bf16x2(q[0] * g[0], q[1] * g[1]),
+                                pack_bf16x2(q[2] * g[2], q[3] * g[3]),
+                                pack_bf16x2(q[4] * g[4], q[5] * g[5]),
+                                pack_bf16x2(q[6] * g[6], q[7] * g[7]));
+          }
+        }
+      }
+      const int t = t_of(i);
+      st.o[t] = mfma32(vq[i % (kAhead + 1)], pb[kk_of(i)], st.o[t]);
     }
   }
 }
 
-template <bool FP8, bool BUF>
+template <int FMT, bool BUF>
 __global__ __launch_bounds__(kThreads, 1) void sparse_mla_kernel(
     AttnLaunch p, int rows_per_split) {
+  constexpr bool FP8 = FMT != kFmtBf16;
+  constexpr bool T128 = FMT == kFmtT128;
   constexpr int kBufSlots = FP8 ? kStageSlots : kTileSlots;
   // Separate arrays: the compiler then knows that reads of one tile buffer
   // cannot touch the direct-to-LDS loads in flight into another, and waits
@@ -435,6 +569,7 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_kernel(
   __shared__ uint4 ftile[FP8 ? kTileSlots : 1];
   __shared__ int32_t rows[kMaxSplitRows];
   __shared__ uint4 qlds[128 * kQLdsStride];
+  __shared__ float tmul[T128 ? kTmulRows * 32 : 1];
   static_assert(32 * kStageRow <= kBufSlots * 16 &&
                     32 * kStageRow <= (FP8 ? kTileSlots : 128 * kQLdsStride) * 16,
                 "epilogue staging regions");
@@ -521,7 +656,7 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_kernel(
   uint32_t sc0[5], sc1[5], sc2[5];
   constexpr int per_tile = FP8 ? 10 : 9;
   auto issue = [&](int j, uint4* dst, uint32_t (&sc)[5]) {
-    if constexpr (FP8) issue_fp8<BUF>(p, s, rsrc, j, dst, sc, wave);
+    if constexpr (FP8) issue_fp8<BUF, T128>(p, s, rsrc, j, dst, sc, wave);
     else issue_bf16<BUF>(p, s, rsrc, j, dst, wave);
   };
   issue(0, buf0, sc0);
@@ -566,7 +701,7 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_kernel(
       if (j < s.ntiles) {
         const uint4* tile = cur;
         if constexpr (FP8) {
-          convert_fp8(cur, ftile, scc, wave, lane);
+          convert_fp8<T128>(cur, ftile, scc, wave, lane, tmul);
           barrier(true);
           tile = ftile;
         }
@@ -575,10 +710,10 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_kernel(
               s.rows[j * kRowsT + (lane & 31)] >= 0);
           if constexpr (FP8) {
             NoLoads none;
-            compute_tile(tile, qrow, vmask, st, sl2, lane, none);
+            compute_tile<T128>(tile, qrow, vmask, st, sl2, lane, none, tmul);
           } else {
             TileLoads<BUF> tl{p.kv.data, rsrc, s.rows + jn * kRowsT, nxt, wave, 0u};
-            compute_tile(tile, qrow, vmask, st, sl2, lane, tl);
+            compute_tile<false>(tile, qrow, vmask, st, sl2, lane, tl, tmul);
           }
         }
         // FP8: the barrier at the start of the next step also keeps its
@@ -754,20 +889,18 @@ hipError_t launch_sparse_mla(const AttnLaunch& p, hipStream_t stream) {
   dim3 grid(used, tokens);
   // buffer-form loads address the pool with 32-bit offsets
   const bool buf = p.kv.bytes < (1ull << 32);
-  if (p.kv.fp8) {
-    if (buf)
-      hipLaunchKernelGGL((sparse_mla_kernel<true, true>), grid, dim3(kThreads),
-                         0, stream, p, rps);
-    else
-      hipLaunchKernelGGL((sparse_mla_kernel<true, false>), grid,
-                         dim3(kThreads), 0, stream, p, rps);
+  auto go = [&](auto kernel) {
+    hipLaunchKernelGGL(kernel, grid, dim3(kThreads), 0, stream, p, rps);
+  };
+  if (p.kv.t128) {
+    if (buf) go(sparse_mla_kernel<kFmtT128, true>);
+    else go(sparse_mla_kernel<kFmtT128, false>);
+  } else if (p.kv.fp8) {
+    if (buf) go(sparse_mla_kernel<kFmtMx32, true>);
+    else go(sparse_mla_kernel<kFmtMx32, false>);
   } else {
-    if (buf)
-      hipLaunchKernelGGL((sparse_mla_kernel<false, true>), grid,
-                         dim3(kThreads), 0, stream, p, rps);
-    else
-      hipLaunchKernelGGL((sparse_mla_kernel<false, false>), grid,
-                         dim3(kThreads), 0, stream, p, rps);
+    if (buf) go(sparse_mla_kernel<kFmtBf16, true>);
+    else go(sparse_mla_kernel<kFmtBf16, false>);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || used == 1) return e;

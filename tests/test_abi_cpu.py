@@ -26,8 +26,8 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("dsa_indexer_scores", "dsa_topk", "dsa_sparse_mla_attn",
-              "dsa_decode_step", "dsa_workspace_size", "dsa_status_string",
-              "dsa_last_error"):
+              "dsa_decode_step", "dsa_cache_append", "dsa_workspace_size",
+              "dsa_status_string", "dsa_last_error"):
         assert n in names
 
 
@@ -86,6 +86,8 @@ def test_sparse_mla_validation():
     assert f(H=129) == UNSUP
     assert f(K=0) == UNSUP
     assert f(kd=1) == NULL
+    assert f(kd=2) == NULL                      # tile scales too
+    assert f(kd=3) == UNSUP
     # 32 tokens split their rows: a workspace is needed
     assert f(B=32, K=2048) == WS
     need = dsa.workspace_size(dsa.OP_SPARSE_MLA, 32, 1, 64, 128, 2048)
@@ -118,6 +120,42 @@ def test_decode_step_validation():
     fp8 = dsa._PagedCacheC(64, 10, 4, 1, 0, 0x1000, None, 0x1000, None,
                            0x1000, 0x1000)
     assert f(cache=fp8) == NULL                 # MX keys need scales
+    t128_keys = dsa._PagedCacheC(64, 10, 4, 2, 0, 0x1000, 0x1000, 0x1000,
+                                 None, 0x1000, 0x1000)
+    assert f(cache=t128_keys) == UNSUP          # tiles are for the KV only
+    t128_kv = dsa._PagedCacheC(64, 10, 4, 0, 2, 0x1000, None, 0x1000, None,
+                               0x1000, 0x1000)
+    assert f(cache=t128_kv) == NULL             # tile scales missing
+
+
+def test_cache_append_validation():
+    def f(**kw):
+        a = dict(B=2, T=1, d_I=128, P=10, MP=4, pt=FAKE, pos=FAKE, kn=FAKE,
+                 kd=0, k=FAKE, ks=None, vn=FAKE, vd=0, v=FAKE, vs=None)
+        a.update(kw)
+        return lib.dsa_cache_append(a["B"], a["T"], a["d_I"], a["P"], a["MP"],
+                                    a["pt"], a["pos"], a["kn"], a["kd"],
+                                    a["k"], a["ks"], a["vn"], a["vd"], a["v"],
+                                    a["vs"], None)
+    assert f(pt=None) == NULL
+    assert f(pos=None) == NULL
+    assert f(kn=None, vn=None) == NULL          # nothing to append
+    assert f(B=0) == SHAPE
+    assert f(T=0) == SHAPE
+    assert f(P=0) == SHAPE
+    assert f(MP=0) == SHAPE
+    assert f(d_I=96) == UNSUP
+    assert f(kd=2) == UNSUP                     # keys: bf16 or MX32 only
+    assert f(kd=1) == NULL                      # MX keys need their scales
+    assert f(k=None) == NULL
+    assert f(vd=5) == UNSUP
+    assert f(vd=1) == NULL
+    assert f(vd=2) == NULL
+    assert f(v=None) == NULL
+    # a pool that is not appended to is not checked
+    assert f(kn=None, d_I=96, kd=9, k=None, vd=7, vn=None) == NULL
+    assert b"dsa_cache_append" in lib.dsa_last_error() or \
+        b"neither" in lib.dsa_last_error()
 
 
 def test_workspace_sizes():

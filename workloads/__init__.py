@@ -127,6 +127,59 @@ def mx32_quantize(x: np.ndarray):
             (X + 127).astype(np.uint8))
 
 
+def append_rows(seed: int, n: int, width: int) -> np.ndarray:
+    """bf16 bit patterns [n, width] of new cache rows, drawn to exercise the
+    cache-append quantizers: row kind i % 8 is
+      0 normal values times a per-row magnitude over a wide exponent range
+      1 normal values with some 32-groups zeroed and some -0.0 entries
+      2 tiny magnitudes, down into the bf16 subnormals
+      3 very large magnitudes, up to near the bf16 maximum
+      4 per 32-group: one element of magnitude 448 * 2^k, the rest exact
+        midpoints between neighbouring 3-bit-mantissa values times 2^k
+      5 small integers in [-4, 4]
+      6 one non-zero element per 32-group
+      7 uniform values with a different power-of-two magnitude per group
+    """
+    assert width % 32 == 0
+    rng = np.random.default_rng(seed)
+    g = width // 32
+    out = np.empty((n, width), dtype=np.float32)
+    for i in range(n):
+        kind = i % 8
+        if kind == 0:
+            r = rng.standard_normal(width) * np.exp(3 * rng.standard_normal())
+        elif kind == 1:
+            r = rng.standard_normal(width)
+            r.reshape(g, 32)[rng.random(g) < 0.4] = 0.0
+            r[rng.random(width) < 0.05] = -0.0
+        elif kind == 2:
+            r = rng.standard_normal(width) * np.ldexp(1.0, rng.integers(-136, -120))
+        elif kind == 3:
+            r = rng.uniform(-1, 1, width) * np.ldexp(1.0, rng.integers(100, 127))
+        elif kind == 4:
+            k = rng.integers(-20, 20, size=g)
+            m = rng.integers(0, 7, size=(g, 32))
+            e = rng.integers(-5, 8, size=(g, 32))
+            mid = (1.0 + (2 * m + 1) / 16.0) * np.ldexp(1.0, e)
+            mid *= rng.choice([-1.0, 1.0], size=(g, 32))
+            mid[np.arange(g), rng.integers(0, 32, size=g)] = \
+                E4M3_MAX * rng.choice([-1.0, 1.0], size=g)
+            r = (mid * np.ldexp(1.0, k)[:, None]).reshape(width)
+        elif kind == 5:
+            r = rng.integers(-4, 5, size=width).astype(np.float64)
+        elif kind == 6:
+            r = np.zeros((g, 32))
+            r[np.arange(g), rng.integers(0, 32, size=g)] = \
+                rng.standard_normal(g) * 10.0
+            r = r.reshape(width)
+        else:
+            r = (rng.uniform(-1, 1, (g, 32)) *
+                 np.ldexp(1.0, rng.integers(-30, 30, size=g))[:, None])
+            r = r.reshape(width)
+        out[i] = r
+    return f32_to_bf16_bits(out)
+
+
 # ---------------------------------------------------------------- caches
 
 @dataclasses.dataclass
