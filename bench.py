@@ -112,6 +112,109 @@ def decode_config(name, stream, steps=20, warmup=5, oracle_budget_s=0.0):
     return res
 
 
+def t128_step_bytes(wl, lens):
+    """Algorithmic bytes of one decode step over a cache of MX block-32
+    indexer keys and 128-tile latent KV (576 codes + 5 fp32 scales a row)."""
+    tot = 0
+    for L in lens:
+        L = int(L)
+        tot += (L * (wl.d_I + wl.d_I // 32) + min(wl.top_k, L) * (576 + 20)
+                + wl.H_I * wl.d_I * 2 + wl.H_I * 4 + wl.H * 576 * 2
+                + wl.H * 512 * 4 + wl.H * 4 + wl.top_k * 4)
+    return tot
+
+
+def decode_t128_config(stream, steps=20, warmup=5, oracle_budget_s=0.0):
+    """The decode batch (32 x 32768, top_k 2048) over a cache written by
+    dsa_cache_append from the bf16 rows: MX block-32 indexer keys and the
+    128-tile latent KV.  Times the decode step (rotating input replicas past
+    the Infinity Cache), the append of one new token per sequence, and the
+    append of the whole cache (1M tokens, the kernel's streaming rate)."""
+    import dataclasses
+    import torch
+    import indexed_sparse_attention_lightning_amd as dsa
+    import oracle
+    import workloads as wk
+    from workloads.device import to_device
+    wl = wk.WORKLOADS["decode"]
+    inp = wk.generate(wl)
+    B, L = wl.B, inp.L
+    sb = t128_step_bytes(wl, [L] * B)
+    nrep = max(3, -(-(1 << 30) // sb))
+    base = to_device(inp)
+    P = base["kv"].shape[0]
+    pos = torch.arange(L, dtype=torch.int32, device="cuda").repeat(B, 1)
+    k_rows = base["kidx"].view(B, L, wl.d_I)
+    v_rows = base["kv"].view(B, L, 576)
+
+    def new_cache():
+        return dsa.PagedCache(
+            kidx=torch.empty((P, 64, wl.d_I), dtype=torch.uint8, device="cuda"),
+            kv=torch.empty((P, 64, 576), dtype=torch.uint8, device="cuda"),
+            page_table=base["page_table"], seq_lens=base["seq_lens"],
+            kidx_scale=torch.empty((P, 64, wl.d_I // 32), dtype=torch.uint8,
+                                   device="cuda"),
+            kv_scale=torch.empty((P, 64, 5), dtype=torch.float32,
+                                 device="cuda"))
+
+    caches = []
+    for _ in range(nrep):
+        c = new_cache()
+        dsa.cache_append(c, pos, k_new=k_rows, kv_new=v_rows)
+        caches.append(c)
+    torch.cuda.synchronize()
+    ws = torch.empty(dsa.workspace_size(dsa.OP_DECODE_STEP, B, 1, L, wl.H,
+                                        wl.top_k), dtype=torch.uint8,
+                     device="cuda")
+    o = torch.empty((B, 1, wl.H, 512), device="cuda")
+    lse = torch.empty((B, 1, wl.H), device="cuda")
+    ms = time_loop(lambda i: dsa.decode_step(
+        caches[i % nrep], base["q_idx"], base["w"], base["q"], wl.top_k,
+        wl.softmax_scale, max_seq_len=L, out=o, lse=lse, workspace=ws),
+        steps, warmup, stream)
+    # one new token per sequence (the last position, rewritten in place)
+    last = pos[:, -1:].contiguous()
+    k1 = k_rows[:, -1:].contiguous()
+    v1 = v_rows[:, -1:].contiguous()
+    ms_app1 = time_loop(lambda i: dsa.cache_append(
+        caches[i % nrep], last, k_new=k1, kv_new=v1), steps, warmup, stream)
+    ms_bulk = time_loop(lambda i: dsa.cache_append(
+        caches[i % nrep], pos, k_new=k_rows, kv_new=v_rows), 5, 2, stream)
+    bulk_bytes = B * L * (wl.d_I * 2 + 576 * 2 + 4          # read: rows, pos
+                          + wl.d_I + wl.d_I // 32 + 576 + 20)  # written
+    bulk_gbps = bulk_bytes / (ms_bulk * 1e-3) / 1e9
+    gbps = sb / (ms * 1e-3) / 1e9
+    res = {"ms_per_step": round(ms, 5),
+           "tokens_per_s": round(B / (ms * 1e-3), 1),
+           "step_algorithmic_bytes": sb,
+           "step_hbm_gbps": round(gbps, 1),
+           "step_frac_of_peak": round(gbps / PEAK_HBM_GBPS, 4),
+           "input_replicas": nrep,
+           "cache_append": {
+               "one_token_per_sequence_us": round(ms_app1 * 1e3, 2),
+               "whole_cache_ms": round(ms_bulk, 4),
+               "whole_cache_tokens": B * L,
+               "whole_cache_algorithmic_bytes": bulk_bytes,
+               "whole_cache_hbm_gbps": round(bulk_gbps, 1),
+               "whole_cache_frac_of_peak": round(bulk_gbps / PEAK_HBM_GBPS, 4)}}
+    del caches, ws, base, k_rows, v_rows
+    torch.cuda.empty_cache()
+    if oracle_budget_s > 0:
+        # the oracle's own quantisation of the first two sequences' rows
+        sub = 2
+        npg = sub * L // 64
+        kd, ks = oracle.quantize_rows(inp.k_idx.data[:npg], "mx32")
+        vd, vs = oracle.quantize_rows(inp.kv.data[:npg], "t128")
+        wl_s = dataclasses.replace(wl, B=sub)
+        inp_s = dataclasses.replace(
+            inp, wl=wl_s, seq_lens=inp.seq_lens[:sub], q_pos=inp.q_pos[:sub],
+            page_table=inp.page_table[:sub], q_idx=inp.q_idx[:sub],
+            w=inp.w[:sub], q=inp.q[:sub], k_idx=wk.Cache(kd, ks, True),
+            kv=wk.Cache(vd, vs, "t128"))
+        res["cpu_oracle"] = oracle_rate(inp_s, oracle_budget_s)
+    return res
+
+
 def indexer_bytes(wl, L):
     """Algorithmic bytes of one indexer launch: keys + queries + weights."""
     return wl.B * wl.T * (L * wl.d_I * 2 + wl.H_I * wl.d_I * 2 + wl.H_I * 4)
@@ -264,7 +367,8 @@ def main(argv=None):
                     help="skip the prefill-chunk kernel timings")
     ap.add_argument("--no-configs", action="store_true",
                     help="skip the FP8 and ragged decode configurations")
-    ap.add_argument("--only-config", choices=["decode_fp8", "ragged"],
+    ap.add_argument("--only-config",
+                    choices=["decode_fp8", "ragged", "decode_t128"],
                     help="time only this decode configuration (10 steps after "
                          "3 warm-up steps) and print its JSON object; for "
                          "kernel traces")
@@ -285,8 +389,10 @@ def main(argv=None):
     from workloads.device import to_device
 
     if args.only_config:
-        res = decode_config(args.only_config, torch.cuda.current_stream(),
-                            steps=10, warmup=3)
+        st = torch.cuda.current_stream()
+        res = (decode_t128_config(st, steps=10, warmup=3)
+               if args.only_config == "decode_t128" else
+               decode_config(args.only_config, st, steps=10, warmup=3))
         print(json.dumps({"config": args.only_config, **res}), flush=True)
         return 0
 
@@ -448,6 +554,13 @@ def main(argv=None):
                            **decode_config(
                                "ragged", stream,
                                oracle_budget_s=0 if args.no_cpu_baseline else 4.0)),
+            "decode_t128": dict(workload="batch 32 x 32768, top_k 2048, cache "
+                                "written by dsa_cache_append: MX block-32 "
+                                "indexer keys, latent KV as e4m3 with one fp32 "
+                                "scale per 128-feature tile",
+                                **decode_t128_config(
+                                    stream, oracle_budget_s=0
+                                    if args.no_cpu_baseline else 4.0)),
         }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(inp)

@@ -16,31 +16,27 @@
 // e4m3fn rounding is to nearest, ties to even, in fp32 with correctly
 // rounded divisions, so the codes are a deterministic function of the input.
 //
-// One wave per token: lane l owns the 8-feature chunks l and 64 + l of a
-// row, a group of 32 is four neighbouring lanes and a tile of 128 sixteen, so
-// group maxima are butterfly reductions inside the wave.  The work is a few
-// KB per token; the launch is latency-bound, not bandwidth-bound.
+// A workgroup of four waves stores eight tokens, one 8-feature chunk per
+// lane and pass: wave w takes features 0..511 of tokens 2w and 2w+1 (lane =
+// chunk, so a group of 32 is four neighbouring lanes and a tile of 128
+// sixteen); wave 0 also takes the 64 rope features of all eight tokens (8
+// lanes each, one tile), waves 1 and 2 the indexer keys (4 or 8 tokens a
+// wave).  Group maxima are butterfly reductions inside the wave; every lane
+// is busy in every pass.
 #include "dsa_device.h"
 #include "dsa_launch.h"
 
 namespace dsa {
 namespace {
 
-constexpr int kTokensPerBlock = 4;
+constexpr int kTokensPerBlock = 8;   // per workgroup of four waves
 constexpr float kE4m3Max = 448.0f;
 
-// e4m3fn code of y, |y| <= 448: nearest, ties to even; the sign bit is y's.
-__device__ __forceinline__ uint32_t e4m3_code(float y) {
-  const uint32_t u = __builtin_bit_cast(uint32_t, y);
-  const uint32_t sign = (u >> 24) & 0x80u;
-  const uint32_t b = u & 0x7fffffffu;
-  const float a = __builtin_bit_cast(float, b);
-  // below 2^-6 the format steps by 2^-9: scale by 2^9 (exact) and round
-  const uint32_t sub = (uint32_t)__builtin_rintf(a * 512.0f);
-  // otherwise keep 3 mantissa bits: round half to even at bit 20, a carry
-  // moves into the exponent; rebias 127 -> 7
-  const uint32_t nrm = ((b + 0x7ffffu + ((b >> 20) & 1u)) >> 20) - (120u << 3);
-  return sign | (a < 0x1p-6f ? sub : nrm);
+// Four e4m3fn codes (nearest, ties to even, sign kept; |y| <= 448) packed
+// little-endian by the hardware conversion.
+__device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
+  const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true);
 }
 
 // Exponent X of an MX group scale for the group maximum amax (see above).
@@ -62,11 +58,6 @@ __device__ __forceinline__ void unpack8(const uint4 v, float (&f)[8]) {
   }
 }
 
-__device__ __forceinline__ uint2 pack_codes(const uint32_t (&c)[8]) {
-  return make_uint2(c[0] | c[1] << 8 | c[2] << 16 | c[3] << 24,
-                    c[4] | c[5] << 8 | c[6] << 16 | c[7] << 24);
-}
-
 // Maximum over the `lanes` neighbouring lanes (a power of two) holding x.
 template <int LANES>
 __device__ __forceinline__ float group_max(float x) {
@@ -75,87 +66,112 @@ __device__ __forceinline__ float group_max(float x) {
   return x;
 }
 
-// Store one bf16 row of `width` features (width / 8 <= 128 chunks) at pool
-// slot `slot` in format FMT.  Every lane of the wave must call this.
-template <int FMT>
-__device__ __forceinline__ void store_row(const uint16_t* src, int width,
+// Physical pool slot of token `tok`, or -1 when the token is skipped (past
+// the batch, negative position, position past the page table, page entry
+// outside the pool).
+__device__ __forceinline__ int64_t token_slot(const AppendLaunch& p, int tok) {
+  if (tok >= p.tokens) return -1;
+  const int pos = p.pos[tok];
+  if (pos < 0 || pos / kPage >= p.max_pages) return -1;
+  const int page = p.page_table[(int64_t)(tok / p.T) * p.max_pages + pos / kPage];
+  if (page < 0 || page >= p.num_pages) return -1;
+  return (int64_t)page * kPage + pos % kPage;
+}
+
+// This lane's chunk c (features 8c..8c+7) of a bf16 row into pool slot
+// `slot` (< 0: nothing stored) of a pool of `width`-feature rows in format
+// FMT.  GL neighbouring lanes form one scale group (scale index `gidx`,
+// written by the group's first lane).  Every lane of the wave must call
+// this: the group maximum is exchanged between lanes.
+template <int FMT, int GL>
+__device__ __forceinline__ void put_chunk(const uint16_t* src, int c,
+                                          int64_t slot, int width,
                                           uint8_t* pool, void* scale,
-                                          int64_t slot, int lane) {
-  const int nchunk = width / 8;
-#pragma unroll
-  for (int half = 0; half < 2; ++half) {
-    const int c = lane + 64 * half;
-    const bool own = c < nchunk;
-    if (half == 1 && nchunk <= 64) break;   // wave-uniform
-    uint4 v = make_uint4(0, 0, 0, 0);
-    if (own) v = reinterpret_cast<const uint4*>(src)[c];
-    if constexpr (FMT == kFmtBf16) {
-      if (own)
-        reinterpret_cast<uint4*>(pool + slot * width * 2)[c] = v;
-      continue;
-    }
+                                          int nscale, int gidx, int lane) {
+  const bool own = slot >= 0;
+  uint4 v = make_uint4(0, 0, 0, 0);
+  if (own) v = reinterpret_cast<const uint4*>(src)[c];
+  if constexpr (FMT == kFmtBf16) {
+    if (own) reinterpret_cast<uint4*>(pool + slot * width * 2)[c] = v;
+  } else {
     float f[8];
     unpack8(v, f);
     float amax = 0.0f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(f[i]));
-    uint32_t code[8];
+    amax = group_max<GL>(amax);
+    float y[8];
+    float sc;
     if constexpr (FMT == kFmtMx32) {
-      amax = group_max<4>(amax);
       const int X = mx_exponent(amax);
       const float inv = __builtin_bit_cast(float, (uint32_t)(127 - X) << 23);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) code[i] = e4m3_code(f[i] * inv);
-      if (own) {
-        reinterpret_cast<uint2*>(pool + slot * width)[c] = pack_codes(code);
-        if ((c & 3) == 0)
-          static_cast<uint8_t*>(scale)[slot * (width / 32) + c / 4] =
-              (uint8_t)(X + 127);
-      }
+      for (int i = 0; i < 8; ++i) y[i] = f[i] * inv;   // exact
+      sc = __builtin_bit_cast(float, (uint32_t)(X + 127));
     } else {
-      // tiles of 16 chunks; the 64-feature tail tile is chunks 64..71, and
-      // lanes 8..15 of the second half hold no chunk (amax 0)
-      amax = group_max<16>(amax);
-      const float sc = __fdiv_rn(amax, kE4m3Max);
+      sc = __fdiv_rn(amax, kE4m3Max);
       const float div = amax > 0.0f ? sc : 1.0f;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const float y = __fdiv_rn(f[i], div);
-        code[i] = e4m3_code(fminf(fmaxf(y, -kE4m3Max), kE4m3Max));
-      }
-      if (own) {
-        reinterpret_cast<uint2*>(pool + slot * width)[c] = pack_codes(code);
-        if ((c & 15) == 0)
-          static_cast<float*>(scale)[slot * kT128Tiles + c / 16] = sc;
+      for (int i = 0; i < 8; ++i)
+        y[i] = fminf(fmaxf(__fdiv_rn(f[i], div), -kE4m3Max), kE4m3Max);
+    }
+    if (own) {
+      reinterpret_cast<uint2*>(pool + slot * width)[c] =
+          make_uint2(e4m3x4(y[0], y[1], y[2], y[3]),
+                     e4m3x4(y[4], y[5], y[6], y[7]));
+      if ((lane & (GL - 1)) == 0) {
+        if constexpr (FMT == kFmtMx32)
+          static_cast<uint8_t*>(scale)[slot * nscale + gidx] =
+              (uint8_t)__builtin_bit_cast(uint32_t, sc);
+        else
+          static_cast<float*>(scale)[slot * nscale + gidx] = sc;
       }
     }
   }
 }
 
 template <int KFMT, int VFMT>
-__global__ __launch_bounds__(64 * kTokensPerBlock) void cache_append_kernel(
-    AppendLaunch p) {
+__global__ __launch_bounds__(64 * 4) void cache_append_kernel(AppendLaunch p) {
   const int lane = lane_id();
-  const int tok = blockIdx.x * kTokensPerBlock + threadIdx.x / 64;
-  if (tok >= p.tokens) return;   // wave-uniform
-  const int b = tok / p.T;
-  const int pos = p.pos[tok];
-  if (pos < 0 || pos / kPage >= p.max_pages) return;
-  const int page = p.page_table[(int64_t)b * p.max_pages + pos / kPage];
-  if (page < 0 || page >= p.num_pages) return;
-  const int64_t slot = (int64_t)page * kPage + pos % kPage;
-  if (p.k_new)
-    store_row<KFMT>(p.k_new + (int64_t)tok * p.d_I, p.d_I, p.kidx,
-                    p.kidx_scale, slot, lane);
-  if (p.kv_new)
-    store_row<VFMT>(p.kv_new + (int64_t)tok * kLatent, kLatent, p.kv,
-                    p.kv_scale, slot, lane);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);
+  const int tok0 = blockIdx.x * kTokensPerBlock;
+  constexpr int kVGroup = VFMT == kFmtT128 ? 16 : 4;   // lanes per scale
+  constexpr int kVScales = VFMT == kFmtT128 ? kT128Tiles : kLatent / 32;
+  if (p.kv_new) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int tok = tok0 + 2 * wave + u;
+      const int64_t slot = token_slot(p, tok);   // same for the whole wave
+      if (slot >= 0)
+        put_chunk<VFMT, kVGroup>(p.kv_new + (int64_t)tok * kLatent, lane, slot,
+                                 kLatent, p.kv, p.kv_scale, kVScales,
+                                 lane / kVGroup, lane);
+    }
+    if (wave == 0) {   // the rope features: 8 lanes per token
+      const int tok = tok0 + lane / 8;
+      const int c = 64 + (lane & 7);
+      put_chunk<VFMT, VFMT == kFmtT128 ? 8 : 4>(
+          p.kv_new + (int64_t)tok * kLatent, c, token_slot(p, tok), kLatent,
+          p.kv, p.kv_scale, kVScales, VFMT == kFmtT128 ? 4 : c / 4, lane);
+    }
+  }
+  if (p.k_new) {
+    const int cpt = p.d_I / 8;       // chunks per key row: 16 or 8
+    const int tpw = 64 / cpt;        // key rows per wave: 4 or 8
+    const int kw = wave - 1;
+    if (kw >= 0 && kw * tpw < kTokensPerBlock) {
+      const int tok = tok0 + kw * tpw + lane / cpt;
+      const int c = lane % cpt;
+      put_chunk<KFMT, 4>(p.k_new + (int64_t)tok * p.d_I, c, token_slot(p, tok),
+                         p.d_I, p.kidx, p.kidx_scale, p.d_I / 32, c / 4, lane);
+    }
+  }
 }
 
 template <int KFMT>
 hipError_t launch_v(const AppendLaunch& p, hipStream_t stream) {
   const dim3 grid((p.tokens + kTokensPerBlock - 1) / kTokensPerBlock);
-  const dim3 block(64 * kTokensPerBlock);
+  const dim3 block(64 * 4);
   switch (p.kv_fmt) {
     case kFmtBf16:
       hipLaunchKernelGGL((cache_append_kernel<KFMT, kFmtBf16>), grid, block, 0,
