@@ -190,10 +190,24 @@ def sparse_mla_row(q, kv_sel, softmax_scale):
 
 # ------------------------------------------------------- whole-path drivers
 
-def indexer_scores(inp, rows=None):
+def indexer_queries(q_bits, quantize=False):
+    """Indexer query values [..., H_I, d_I] (float64) from bf16 bits.  With
+    ``quantize``: the fully quantised indexer's queries -- each head's
+    features quantised to MX block-32 (the same rule as the caches) and
+    dequantised (page "Inference Adaptation and Performance Optimization for
+    New Large Language Model Architectures", section 4.2)."""
+    q = decode_bf16(q_bits)
+    if not quantize:
+        return q
+    codes, scales = quantize_mx32(q)
+    return dequant_mx32(codes, scales)
+
+
+def indexer_scores(inp, rows=None, quantize_queries=False):
     """Scores [B, T, L] (float64) for a contiguous-cache input set; positions
     past a query's position are -inf.  ``rows``: optional list of (b, t) to
-    compute (others stay NaN)."""
+    compute (others stay NaN).  ``quantize_queries``: the fully quantised
+    indexer (see indexer_queries)."""
     wl = inp.wl
     B, T, L = wl.B, wl.T, inp.L
     out = np.full((B, T, L), np.nan)
@@ -210,19 +224,21 @@ def indexer_scores(inp, rows=None):
         qp = int(inp.q_pos[b, t])
         n = min(qp + 1, L)
         row = np.full(L, -np.inf)
-        row[:n] = indexer_scores_row(decode_bf16(inp.q_idx[b, t]),
-                                     inp.w[b, t], keys[:n])
+        row[:n] = indexer_scores_row(
+            indexer_queries(inp.q_idx[b, t], quantize_queries), inp.w[b, t],
+            keys[:n])
         out[b, t] = row
     return out
 
 
-def decode_path(inp, rows=None, want_scores=False):
+def decode_path(inp, rows=None, want_scores=False, quantize_queries=False):
     """The whole hot path on the CPU: indexer -> Top-K -> sparse attention.
 
     Reads both caches through the page table.  Returns a dict with idx
     (int64 [B, T, K], -1 padded), out (float64 [B, T, H, 512]) and lse
     (float64 [B, T, H]); rows not requested stay -2 / NaN.  With
-    ``want_scores`` also the float64 scores of each requested row.
+    ``want_scores`` also the float64 scores of each requested row;
+    ``quantize_queries``: the fully quantised indexer (indexer_queries).
     """
     wl = inp.wl
     B, T, K, H = wl.B, wl.T, wl.top_k, wl.H
@@ -241,8 +257,9 @@ def decode_path(inp, rows=None, want_scores=False):
                               np.arange(inp.seq_lens[b]))
         qp = int(inp.q_pos[b, t])
         n = min(qp + 1, int(inp.seq_lens[b]))
-        s = indexer_scores_row(decode_bf16(inp.q_idx[b, t]), inp.w[b, t],
-                               keys[:n])
+        s = indexer_scores_row(
+            indexer_queries(inp.q_idx[b, t], quantize_queries), inp.w[b, t],
+            keys[:n])
         if want_scores:
             scores[(b, t)] = s
         sel = topk_row(s, qp, K)

@@ -292,3 +292,72 @@ def test_cache_append_read_back(fmt, width):
     assert np.array_equal(d1[~written], d0[~written])
     if s0 is not None:
         assert np.array_equal(s1[~written], s0[~written])
+
+
+# ------------------------------------------------ quantised indexer queries
+
+def test_indexer_queries_blocks_are_per_head():
+    """Heads of very different magnitude keep their own block scales: every
+    element stays within the e4m3 rounding bound of its own block."""
+    rng = np.random.default_rng(50)
+    q = rng.standard_normal((3, 8, 128)) * \
+        np.exp2(rng.integers(-40, 40, size=(3, 8, 1)))
+    q[1, 2, 32:64] = 0.0
+    bits = wk.f32_to_bf16_bits(q.astype(np.float32))
+    v = oracle.decode_bf16(bits)
+    got = oracle.indexer_queries(bits, quantize=True)
+    blk = np.abs(v).reshape(3, 8, 4, 32).max(-1)
+    step = np.repeat(blk, 32, axis=-1) * 2.0 ** -7    # subnormal headroom
+    assert np.all(np.abs(got - v) <= np.abs(v) * 2.0 ** -4 + step)
+    assert np.all(got[1, 2, 32:64] == 0)
+    assert np.array_equal(oracle.indexer_queries(bits), v)
+
+
+def test_indexer_queries_exact_on_small_integers():
+    rng = np.random.default_rng(51)
+    bits = wk.f32_to_bf16_bits(
+        rng.integers(-4, 5, size=(5, 64, 128)).astype(np.float32))
+    assert np.array_equal(oracle.indexer_queries(bits, quantize=True),
+                          oracle.decode_bf16(bits))
+
+
+def _brute_mx_values(row):
+    """MX block-32 values of one row by exact search: per block the smallest
+    power of two covering max/448, then the nearest code (rationals)."""
+    out = []
+    for blk in np.asarray(row, dtype=np.float64).reshape(-1, 32):
+        amax = Fraction(float(np.abs(blk).max()))
+        X = 0
+        if amax > 0:
+            X = -127
+            while Fraction(448) * Fraction(2) ** X < amax:
+                X += 1
+        scale = Fraction(2) ** X
+        for x in blk:
+            c = _brute_code(float(Fraction(float(x)) / scale))
+            out.append(Fraction(float(oracle.decode_e4m3fn(np.uint8(c)))) * scale)
+    return out
+
+
+def test_quantised_indexer_scores_brute_force():
+    wl = wk.WORKLOADS["tiny"]
+    inp = wk.generate(wl)
+    q = wk.eighths(52, inp.q_idx.shape)
+    inp = __import__("dataclasses").replace(inp, q_idx=q)
+    got = oracle.indexer_scores(inp, quantize_queries=True)
+    keys = oracle.cache_rows(inp.k_idx.data, inp.k_idx.scale,
+                             inp.k_idx.quantized, inp.page_table[0],
+                             np.arange(inp.seq_lens[0]))
+    qv = [_brute_mx_values(oracle.decode_bf16(q[0, 0, j]))
+          for j in range(wl.H_I)]
+    qp = int(inp.q_pos[0, 0])
+    for s in list(range(0, qp + 1, 37)) + [qp]:
+        tot = Fraction(0)
+        for j in range(wl.H_I):
+            d = sum(qv[j][c] * Fraction(float(keys[s, c]))
+                    for c in range(wl.d_I))
+            tot += Fraction(float(inp.w[0, 0, j])) * max(d, Fraction(0))
+        assert got[0, 0, s] == float(tot), s
+    # the quantisation changed some query values, so the pin is not vacuous
+    assert not np.array_equal(oracle.indexer_queries(q, True),
+                              oracle.indexer_queries(q))

@@ -180,6 +180,15 @@ def append_rows(seed: int, n: int, width: int) -> np.ndarray:
     return f32_to_bf16_bits(out)
 
 
+def eighths(seed: int, shape, limit: int = 39) -> np.ndarray:
+    """bf16 bit patterns of k/8 for integers k uniform in [-limit, limit]:
+    indexer queries with fractional parts (inputs of the quantised-indexer
+    tests; multiples of 1/8 keep every indexer sum exact in fp32)."""
+    rng = np.random.default_rng(seed)
+    k = rng.integers(-limit, limit + 1, size=shape)
+    return f32_to_bf16_bits((k / 8.0).astype(np.float32))
+
+
 # ---------------------------------------------------------------- caches
 
 @dataclasses.dataclass
