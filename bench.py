@@ -62,10 +62,12 @@ def step_bytes_general(wl, lens):
     return tot
 
 
-def decode_config(name, stream, steps=20, warmup=5, oracle_budget_s=0.0):
+def decode_config(name, stream, steps=20, warmup=5, oracle_budget_s=0.0,
+                  quantize_queries=False):
     """ms per dsa_decode_step call for another decode configuration, with
     enough input replicas rotating that a step's operands (over 1 GB in
-    total) are not served from the 256 MB Infinity Cache."""
+    total) are not served from the 256 MB Infinity Cache.  quantize_queries:
+    the fully quantised indexer (MX keys only)."""
     import torch
     import indexed_sparse_attention_lightning_amd as dsa
     import workloads as wk
@@ -95,7 +97,7 @@ def decode_config(name, stream, steps=20, warmup=5, oracle_budget_s=0.0):
         d = reps[r]
         dsa.decode_step(caches[r], d["q_idx"], d["w"], d["q"], wl.top_k,
                         wl.softmax_scale, max_seq_len=max_len, out=o, lse=l,
-                        workspace=ws)
+                        workspace=ws, quantize_queries=quantize_queries)
 
     ms = time_loop(step, steps, warmup, stream)
     gbps = sb / (ms * 1e-3) / 1e9
@@ -108,7 +110,8 @@ def decode_config(name, stream, steps=20, warmup=5, oracle_budget_s=0.0):
     del reps, caches, base, ws
     torch.cuda.empty_cache()
     if oracle_budget_s > 0:
-        res["cpu_oracle"] = oracle_rate(inp, oracle_budget_s)
+        res["cpu_oracle"] = oracle_rate(inp, oracle_budget_s,
+                                        quantize_queries=quantize_queries)
     return res
 
 
@@ -291,14 +294,15 @@ def cpu_baseline(inp, budget_s=12.0):
                       f"{inp.L} keys, top-k, attention), {dt:.1f} s"}
 
 
-def oracle_rate(inp, budget_s=4.0):
+def oracle_rate(inp, budget_s=4.0, quantize_queries=False):
     """The CPU oracle on whole query rows of `inp` (rows in order, cycling)
     for about `budget_s` seconds: query rows per second."""
     import oracle
     allrows = [(b, t) for b in range(inp.wl.B) for t in range(inp.wl.T)]
     n, t0 = 0, time.perf_counter()
     while time.perf_counter() - t0 < budget_s:
-        oracle.decode_path(inp, rows=[allrows[n % len(allrows)]])
+        oracle.decode_path(inp, rows=[allrows[n % len(allrows)]],
+                           quantize_queries=quantize_queries)
         n += 1
     dt = time.perf_counter() - t0
     return {"value": round(n / dt, 2), "unit": "query rows/s",
@@ -368,7 +372,8 @@ def main(argv=None):
     ap.add_argument("--no-configs", action="store_true",
                     help="skip the FP8 and ragged decode configurations")
     ap.add_argument("--only-config",
-                    choices=["decode_fp8", "ragged", "decode_t128"],
+                    choices=["decode_fp8", "decode_fp8_q8", "ragged",
+                             "decode_t128"],
                     help="time only this decode configuration (10 steps after "
                          "3 warm-up steps) and print its JSON object; for "
                          "kernel traces")
@@ -390,9 +395,13 @@ def main(argv=None):
 
     if args.only_config:
         st = torch.cuda.current_stream()
-        res = (decode_t128_config(st, steps=10, warmup=3)
-               if args.only_config == "decode_t128" else
-               decode_config(args.only_config, st, steps=10, warmup=3))
+        if args.only_config == "decode_t128":
+            res = decode_t128_config(st, steps=10, warmup=3)
+        elif args.only_config == "decode_fp8_q8":
+            res = decode_config("decode_fp8", st, steps=10, warmup=3,
+                                quantize_queries=True)
+        else:
+            res = decode_config(args.only_config, st, steps=10, warmup=3)
         print(json.dumps({"config": args.only_config, **res}), flush=True)
         return 0
 
@@ -548,6 +557,13 @@ def main(argv=None):
                                "top_k 2048", **decode_config(
                                    "decode_fp8", stream,
                                    oracle_budget_s=0 if args.no_cpu_baseline else 4.0)),
+            "decode_fp8_q8": dict(workload="the FP8 decode batch with the "
+                                  "fully quantised indexer: queries to MX "
+                                  "block-32 on the fly, scaled FP8 matrix "
+                                  "cores over the e4m3 keys", **decode_config(
+                                      "decode_fp8", stream, oracle_budget_s=0
+                                      if args.no_cpu_baseline else 4.0,
+                                      quantize_queries=True)),
             "ragged": dict(workload="batch 4, lengths uniform in [16384, "
                            "131072], 64-token pages scattered by a seeded "
                            "page table, FP8 keys and MXFP8 KV, top_k 2048",

@@ -80,6 +80,15 @@ typedef enum dsa_dtype {
 } dsa_dtype;
 
 /* Operation selector for dsa_workspace_size. */
+/* Precision of the indexer queries (step 1). */
+typedef enum dsa_q_mode {
+  DSA_Q_BF16 = 0,           /* bf16 queries; keys dequantised to bf16       */
+  DSA_Q_MX32 = 1            /* queries quantised on the fly to e4m3 with one
+                               e8m0 scale per 32 features of each head, the
+                               products on the scaled FP8 matrix cores (keys
+                               must be DSA_E4M3_MX32)                      */
+} dsa_q_mode;
+
 typedef enum dsa_op {
   DSA_OP_INDEXER_SCORES = 0,
   DSA_OP_TOPK = 1,
@@ -119,6 +128,16 @@ typedef struct dsa_paged_cache {
 /*
  * Lightning Indexer scores over a contiguous key cache (step 1).
  *   q_idx   [B, T, H_I, d_I] bf16   indexer queries
+ *   q_mode  dsa_q_mode.  DSA_Q_MX32 is the fully quantised indexer (page
+ *           "Inference Adaptation and Performance Optimization for New Large
+ *           Language Model Architectures", section 4.2: index Q and K in
+ *           MXFP8, per-group dynamic scales, groups of 32; page "Day-0
+ *           Inference Optimization for a New Sparse Attention Architecture:
+ *           A Technical Deep Dive", section 2): each head's 32-feature
+ *           blocks of q_idx take the scale 2^X, X the smallest integer
+ *           >= -127 with 448 * 2^X >= the block's largest magnitude (X = 0
+ *           for a zero block), codes are the nearest e4m3fn (ties to even)
+ *           of q * 2^-X, and the scores use those dequantised queries
  *   w       [B, T, H_I] fp32        head weights
  *   k_idx   [B, L, d_I]             bf16, or e4m3 codes if k_dtype is MX
  *   k_scale [B, L, d_I/32] e8m0     (NULL unless k_dtype == DSA_E4M3_MX32)
@@ -128,7 +147,7 @@ typedef struct dsa_paged_cache {
  * weights they are exact.  -0 is written as +0.
  */
 dsa_status dsa_indexer_scores(int B, int T, int L, int H_I, int d_I,
-                              const void* q_idx, const float* w,
+                              const void* q_idx, int q_mode, const float* w,
                               const void* k_idx, int k_dtype,
                               const uint8_t* k_scale, const int32_t* q_pos,
                               float* scores, void* stream);
@@ -178,7 +197,8 @@ dsa_status dsa_sparse_mla_attn(int B, int T, int L, int H, int K,
  * indexer -> Top-K -> sparse attention, enqueued on one stream.
  *   cache         see dsa_paged_cache; seq_lens[b] <= max_seq_len
  *   max_seq_len   host upper bound of seq_lens (sizes the score workspace)
- *   q_idx [B, T, H_I, d_I] bf16; w [B, T, H_I] fp32; q [B, T, H, 576] bf16
+ *   q_idx [B, T, H_I, d_I] bf16; q_mode as for dsa_indexer_scores
+ *   w [B, T, H_I] fp32; q [B, T, H, 576] bf16
  *   q_pos [B, T] int32, or NULL when T == 1: then q_pos = seq_lens[b] - 1
  *   out [B, T, H, 512] fp32; lse [B, T, H] fp32
  *   idx_out [B, T, K] int32 or NULL: the selected positions (as dsa_topk)
@@ -187,7 +207,8 @@ dsa_status dsa_sparse_mla_attn(int B, int T, int L, int H, int K,
  */
 dsa_status dsa_decode_step(int B, int T, int H_I, int d_I, int H, int K,
                            float softmax_scale, const dsa_paged_cache* cache,
-                           int max_seq_len, const void* q_idx, const float* w,
+                           int max_seq_len, const void* q_idx, int q_mode,
+                           const float* w,
                            const void* q, const int32_t* q_pos, float* out,
                            float* lse, int32_t* idx_out, void* workspace,
                            size_t workspace_bytes, void* stream);

@@ -27,7 +27,8 @@ from typing import Optional
 import torch
 
 __all__ = [
-    "DSA_BF16", "DSA_E4M3_MX32", "DSA_E4M3_T128", "DsaError", "PagedCache",
+    "DSA_BF16", "DSA_E4M3_MX32", "DSA_E4M3_T128", "DSA_Q_BF16", "DSA_Q_MX32",
+    "DsaError", "PagedCache",
     "cache_append", "decode_step", "indexer_scores", "library_path",
     "sparse_mla_attn", "topk", "workspace_size",
 ]
@@ -36,6 +37,7 @@ DSA_BF16 = 0
 DSA_E4M3_MX32 = 1
 DSA_E4M3_T128 = 2
 T128_TILES = 5
+DSA_Q_BF16, DSA_Q_MX32 = 0, 1
 OP_INDEXER_SCORES, OP_TOPK, OP_SPARSE_MLA, OP_DECODE_STEP = 0, 1, 2, 3
 LATENT, VALUE, PAGE = 576, 512, 64
 
@@ -71,11 +73,11 @@ def _load():
     lib = ctypes.CDLL(_LIB_PATH)
     I, P, F, S = ctypes.c_int, ctypes.c_void_p, ctypes.c_float, ctypes.c_size_t
     sig = {
-        "dsa_indexer_scores": [I, I, I, I, I, P, P, P, I, P, P, P, P],
+        "dsa_indexer_scores": [I, I, I, I, I, P, I, P, P, I, P, P, P, P],
         "dsa_topk": [I, I, I, I, P, P, P, P, S, P],
         "dsa_sparse_mla_attn": [I, I, I, I, I, P, P, I, P, P, F, P, P, P, S, P],
         "dsa_decode_step": [I, I, I, I, I, I, F, ctypes.POINTER(_PagedCacheC),
-                            I, P, P, P, P, P, P, P, P, S, P],
+                            I, P, I, P, P, P, P, P, P, P, S, P],
         "dsa_cache_append": [I, I, I, I, I, P, P, P, I, P, P, P, I, P, P, P],
         "dsa_workspace_size": [I, I, I, I, I, I],
         "dsa_status_string": [I],
@@ -161,10 +163,13 @@ def _scale_shape(dtype: int, lead, width: int):
 
 def indexer_scores(q_idx: torch.Tensor, w: torch.Tensor, k_idx: torch.Tensor,
                    q_pos: torch.Tensor, k_scale: Optional[torch.Tensor] = None,
-                   out: Optional[torch.Tensor] = None) -> torch.Tensor:
+                   out: Optional[torch.Tensor] = None,
+                   quantize_queries: bool = False) -> torch.Tensor:
     """Scores [B, T, L] fp32: sum_j w[t,j] * relu(q_I[t,j] . k_I[s]) for
     s <= q_pos, -inf beyond.  k_idx: [B, L, d_I] bf16, or uint8 e4m3 codes
-    with k_scale [B, L, d_I/32] uint8 e8m0."""
+    with k_scale [B, L, d_I/32] uint8 e8m0.  quantize_queries: the fully
+    quantised indexer (queries to MX block-32 on the fly, scaled FP8 matrix
+    cores; MX keys only)."""
     B, T, H_I, d_I = q_idx.shape
     L = k_idx.shape[1]
     _need(q_idx, "q_idx", torch.bfloat16)
@@ -177,7 +182,9 @@ def indexer_scores(q_idx: torch.Tensor, w: torch.Tensor, k_idx: torch.Tensor,
     if out is None:
         out = torch.empty((B, T, L), dtype=torch.float32, device=q_idx.device)
     _need(out, "scores", torch.float32, (B, T, L))
-    _check(_lib.dsa_indexer_scores(B, T, L, H_I, d_I, _ptr(q_idx), _ptr(w),
+    _check(_lib.dsa_indexer_scores(B, T, L, H_I, d_I, _ptr(q_idx),
+                                   DSA_Q_MX32 if quantize_queries else
+                                   DSA_Q_BF16, _ptr(w),
                                    _ptr(k_idx), kd, _ptr(k_scale),
                                    _ptr(q_pos), _ptr(out), _stream()),
            "dsa_indexer_scores")
@@ -291,11 +298,12 @@ def decode_step(cache: PagedCache, q_idx: torch.Tensor, w: torch.Tensor,
                 out: Optional[torch.Tensor] = None,
                 lse: Optional[torch.Tensor] = None,
                 idx_out: Optional[torch.Tensor] = None,
-                workspace: Optional[torch.Tensor] = None):
+                workspace: Optional[torch.Tensor] = None,
+                quantize_queries: bool = False):
     """Indexer -> Top-K -> sparse attention for q_idx [B, T, H_I, d_I] bf16,
     w [B, T, H_I] fp32, q [B, T, H, 576] bf16 over a paged cache.  q_pos
-    [B, T] int32, or None for T == 1 (the last cached token).  Returns
-    (out, lse, idx_out)."""
+    [B, T] int32, or None for T == 1 (the last cached token).
+    quantize_queries as for indexer_scores.  Returns (out, lse, idx_out)."""
     B, T, H_I, d_I = q_idx.shape
     H = q.shape[2]
     _need(q_idx, "q_idx", torch.bfloat16)
@@ -319,7 +327,9 @@ def decode_step(cache: PagedCache, q_idx: torch.Tensor, w: torch.Tensor,
                                 device=dev)
     _check(_lib.dsa_decode_step(
         B, T, H_I, d_I, H, k, float(softmax_scale), ctypes.byref(c),
-        int(max_seq_len), _ptr(q_idx), _ptr(w), _ptr(q), _ptr(q_pos),
+        int(max_seq_len), _ptr(q_idx),
+        DSA_Q_MX32 if quantize_queries else DSA_Q_BF16, _ptr(w), _ptr(q),
+        _ptr(q_pos),
         _ptr(out), _ptr(lse), _ptr(idx_out), _ptr(workspace),
         workspace.numel(), _stream()), "dsa_decode_step")
     return out, lse, idx_out

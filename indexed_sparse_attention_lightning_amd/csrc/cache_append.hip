@@ -32,32 +32,6 @@ namespace {
 constexpr int kTokensPerBlock = 8;   // per workgroup of four waves
 constexpr float kE4m3Max = 448.0f;
 
-// Four e4m3fn codes (nearest, ties to even, sign kept; |y| <= 448) packed
-// little-endian by the hardware conversion.
-__device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
-  const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
-  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true);
-}
-
-// Exponent X of an MX group scale for the group maximum amax (see above).
-__device__ __forceinline__ int mx_exponent(float amax) {
-  if (amax == 0.0f) return 0;
-  const uint32_t b = __builtin_bit_cast(uint32_t, amax);
-  // amax = m * 2^E, m in [1, 2): 448 * 2^(E-8) = 1.75 * 2^E covers it
-  // unless m > 1.75 (mantissa field above 0x600000)
-  const int X = (int)(b >> 23) - 127 - 8 + ((b & 0x7fffffu) > 0x600000u);
-  return max(X, -127);
-}
-
-__device__ __forceinline__ void unpack8(const uint4 v, float (&f)[8]) {
-  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    f[2 * i] = __builtin_bit_cast(float, w[i] << 16);
-    f[2 * i + 1] = __builtin_bit_cast(float, w[i] & 0xffff0000u);
-  }
-}
-
 // Maximum over the `lanes` neighbouring lanes (a power of two) holding x.
 template <int LANES>
 __device__ __forceinline__ float group_max(float x) {
@@ -104,7 +78,7 @@ __device__ __forceinline__ void put_chunk(const uint16_t* src, int c,
     float sc;
     if constexpr (FMT == kFmtMx32) {
       const int X = mx_exponent(amax);
-      const float inv = __builtin_bit_cast(float, (uint32_t)(127 - X) << 23);
+      const float inv = pow2_neg(X);
 #pragma unroll
       for (int i = 0; i < 8; ++i) y[i] = f[i] * inv;   // exact
       sc = __builtin_bit_cast(float, (uint32_t)(X + 127));

@@ -80,6 +80,15 @@ size_t decode_ws(int B, int T, int L, int H, int K) {
          align_up(dsa::attn_workspace_bytes((int)tokens, H, K));
 }
 
+// Quantised queries need MX keys: both operands of the scaled FP8 products.
+dsa_status check_q_mode(int q_mode, bool mx_keys) {
+  if (q_mode != DSA_Q_BF16 && q_mode != DSA_Q_MX32)
+    return fail(DSA_ERR_UNSUPPORTED, "unknown q_mode %d", q_mode);
+  if (q_mode == DSA_Q_MX32 && !mx_keys)
+    return fail(DSA_ERR_UNSUPPORTED, "q_mode DSA_Q_MX32 needs MX32 keys");
+  return DSA_OK;
+}
+
 dsa_status hip_status(hipError_t e, const char* what) {
   if (e == hipSuccess) return ok();
   return fail(DSA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
@@ -115,7 +124,7 @@ size_t dsa_workspace_size(int op, int B, int T, int L, int H, int K) {
 }
 
 dsa_status dsa_indexer_scores(int B, int T, int L, int H_I, int d_I,
-                              const void* q_idx, const float* w,
+                              const void* q_idx, int q_mode, const float* w,
                               const void* k_idx, int k_dtype,
                               const uint8_t* k_scale, const int32_t* q_pos,
                               float* scores, void* stream) {
@@ -129,7 +138,9 @@ dsa_status dsa_indexer_scores(int B, int T, int L, int H_I, int d_I,
     return fail(DSA_ERR_UNSUPPORTED, "unsupported key dtype %d", k_dtype);
   const bool fp8 = k_dtype == DSA_E4M3_MX32;
   if (fp8 && !k_scale) return fail(DSA_ERR_NULL, "MX keys need k_scale");
+  if (dsa_status st = check_q_mode(q_mode, fp8)) return st;
   dsa::IndexerLaunch a{};
+  a.q8 = q_mode == DSA_Q_MX32;
   a.B = B; a.T = T; a.H_I = H_I; a.d_I = d_I;
   a.q_idx = static_cast<const uint16_t*>(q_idx);
   a.w = w;
@@ -202,7 +213,8 @@ dsa_status dsa_sparse_mla_attn(int B, int T, int L, int H, int K,
 
 dsa_status dsa_decode_step(int B, int T, int H_I, int d_I, int H, int K,
                            float softmax_scale, const dsa_paged_cache* cache,
-                           int max_seq_len, const void* q_idx, const float* w,
+                           int max_seq_len, const void* q_idx, int q_mode,
+                           const float* w,
                            const void* q, const int32_t* q_pos, float* out,
                            float* lse, int32_t* idx_out, void* workspace,
                            size_t workspace_bytes, void* stream) {
@@ -232,6 +244,7 @@ dsa_status dsa_decode_step(int B, int T, int H_I, int d_I, int H, int K,
   const bool kfp8 = cache->kidx_dtype == DSA_E4M3_MX32;
   if (kfp8 && !cache->kidx_scale)
     return fail(DSA_ERR_NULL, "MX indexer keys need kidx_scale");
+  if (dsa_status st = check_q_mode(q_mode, kfp8)) return st;
   if (cache->kv_dtype != DSA_BF16 && !cache->kv_scale)
     return fail(DSA_ERR_NULL, "FP8 KV needs kv_scale");
   const size_t need = decode_ws(B, T, max_seq_len, H, K);
@@ -267,6 +280,7 @@ dsa_status dsa_decode_step(int B, int T, int H_I, int d_I, int H, int K,
   ia.scores = scores;
   ia.row_len = max_seq_len;
   ia.keys_out = 1;   // the Top-K below reads keys: no conversion there
+  ia.q8 = q_mode == DSA_Q_MX32;
   if (hipError_t e = dsa::launch_indexer(ia, st))
     return hip_status(e, "dsa_decode_step: indexer");
 

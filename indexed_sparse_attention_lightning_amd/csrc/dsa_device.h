@@ -71,6 +71,39 @@ __device__ __forceinline__ uint4 dequant8_e4m3(uint2 codes,
   return dequant8_pow2(codes, scale_code << 23);
 }
 
+// Eight bf16 values (a uint4) widened to fp32 (exact).
+__device__ __forceinline__ void unpack8(const uint4 v, float (&f)[8]) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[2 * i] = __builtin_bit_cast(float, w[i] << 16);
+    f[2 * i + 1] = __builtin_bit_cast(float, w[i] & 0xffff0000u);
+  }
+}
+
+// Four e4m3fn codes (nearest, ties to even, sign kept; |y| <= 448) packed
+// little-endian by the hardware conversion.
+__device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
+  const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true);
+}
+
+// Exponent X of an MX block-32 scale for the block's largest magnitude amax:
+// the smallest X >= -127 with 448 * 2^X >= amax (X = 0 for amax = 0), so no
+// element saturates.  amax = m * 2^E, m in [1, 2): 448 * 2^(E-8) = 1.75 * 2^E
+// covers it unless m > 1.75 (mantissa field above 0x600000).
+__device__ __forceinline__ int mx_exponent(float amax) {
+  if (amax == 0.0f) return 0;
+  const uint32_t b = __builtin_bit_cast(uint32_t, amax);
+  const int X = (int)(b >> 23) - 127 - 8 + ((b & 0x7fffffu) > 0x600000u);
+  return max(X, -127);
+}
+
+// 2^-X as an fp32 (X in [-127, 126]): multiplying by it is exact.
+__device__ __forceinline__ float pow2_neg(int X) {
+  return __builtin_bit_cast(float, (uint32_t)(127 - X) << 23);
+}
+
 // Split of a non-negative fp32 scale s = 2^e * m for an exact bf16
 // dequantisation by the scaled conversion above, which applies only the
 // exponent field of its scale operand: returns the exponent part as the

@@ -51,6 +51,8 @@ struct IndexerLaunch {
   float* scores;           // [B*T, row_len]
   int row_len;             // positions written per row (L or max_seq_len)
   int keys_out;            // store score_key(score) bit patterns, not scores
+  int q8;                  // quantise q_idx to MX block-32 and use the scaled
+                           // FP8 matrix cores (keys must be MX32)
 };
 hipError_t launch_indexer(const IndexerLaunch& a, hipStream_t stream);
 

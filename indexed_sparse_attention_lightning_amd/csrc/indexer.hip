@@ -104,9 +104,14 @@ __device__ __forceinline__ void stage_load_f8(StageF8<DI>& st,
   }
 }
 
+// The codes go to the wave's LDS tile and the scale words to `scl` (one per
+// key): a scale word kept in a register across the next load of the same
+// stage would make the compiler move it at the loop back edge, which waits
+// for every load in flight.
 template <int DI>
 __device__ __forceinline__ void stage_store_f8(const StageF8<DI>& st,
-                                               uint4* tile, int lane) {
+                                               uint4* tile, uint32_t* scl,
+                                               int lane) {
   using CL = CodeLayout<DI>;
 #pragma unroll
   for (int i = 0; i < CL::kLoads; ++i) {
@@ -114,16 +119,18 @@ __device__ __forceinline__ void stage_store_f8(const StageF8<DI>& st,
     const int n = id / CL::kChunks, c = id % CL::kChunks;
     tile[n * CL::kChunks + CL::slot(n, c)] = st.v[i];
   }
+  if (lane < kSub) scl[lane] = st.sc;
 }
 
-// tile_scores for a code tile; `sc` holds the scale codes of key lane % 32.
+// tile_scores for a code tile; `scl` holds the scale words of its keys.
 template <int DI, int MB>
 __device__ __forceinline__ float tile_scores_f8(const uint4* tile,
                                                 const uint4 (&a)[MB][DI / 16],
                                                 const float (&wv)[MB][16],
-                                                uint32_t sc, int lane) {
+                                                const uint32_t* scl, int lane) {
   using CL = CodeLayout<DI>;
   const int n = lane & 31, h = lane >> 5;
+  const uint32_t sc = scl[n];
   f32x16 acc[MB];
 #pragma unroll
   for (int m = 0; m < MB; ++m) acc[m] = f32x16{};
@@ -285,6 +292,7 @@ __global__ __launch_bounds__(256, 2) void indexer_stream_kernel(
   // scores leave in bursts of up to kFlush: a steady trickle of small
   // writes into the key stream costs read bandwidth
   __shared__ float sbuf[kWavesPerWG][kFlush];
+  __shared__ uint32_t sscale[kWavesPerWG][FP8 ? kSub : 1];
   const int lane = lane_id();
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   int b = blockIdx.z, t = blockIdx.y, chunk = blockIdx.x;
@@ -316,6 +324,7 @@ __global__ __launch_bounds__(256, 2) void indexer_stream_kernel(
                           p.H_I, lane, a, wv);
 
   uint4* tile = lds[wave];
+  uint32_t* scl = sscale[wave];
   // Every iteration issues the same loads and stores (the tail re-reads the
   // last stage, an L2 hit, and its scores are masked), so the compiler can
   // count them and wait only for the stage it consumes.
@@ -333,11 +342,10 @@ __global__ __launch_bounds__(256, 2) void indexer_stream_kernel(
     for (int i = 0; i < nsub; i += 4) {
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        stage_store_f8<DI>(st[u], tile, lane);
-        const uint32_t scs = st[u].sc;
+        stage_store_f8<DI>(st[u], tile, scl, lane);
         stage_load_f8<DI>(st[u], p.keys, b, k0 + min(i + u + 4, last) * kSub,
                           lane);
-        const float sc = tile_scores_f8<DI, MB>(tile, a, wv, scs, lane);
+        const float sc = tile_scores_f8<DI, MB>(tile, a, wv, scl, lane);
         // stages past the end (re-read tail) are not buffered
         if (lane < 32 && i + u < nsub)
           sb[((i + u) * kSub + lane) % kFlush] = out_val(p, sc);
@@ -365,6 +373,252 @@ __global__ __launch_bounds__(256, 2) void indexer_stream_kernel(
       if ((i + 2) * kSub % kFlush == 0 && i + 2 < nsub)   // a full buffer
         flush(k0 + (i + 2) * kSub - kFlush, k0 + (i + 2) * kSub);
     }
+  }
+  const int done = (nsub - 1) / (kFlush / kSub) * kFlush;   // flushed so far
+  flush(k0 + done, kend);
+}
+
+// ------------------------------------------------ quantised indexer (MX32)
+// The fully quantised indexer (page "Inference Adaptation and Performance
+// Optimization for New Large Language Model Architectures", section 4.2:
+// index Q and K in MXFP8, one scale per 32 elements; "Day-0 Inference
+// Optimization ...: A Technical Deep Dive", section 2): the bf16 queries are
+// quantised per head and 32-feature block on load (the rule of the cache
+// append: scale 2^X, X the smallest with 448 * 2^X >= the block maximum),
+// and the products run on the 32x32x64 scaled FP8 matrix cores, which take
+// the e8m0 block scales of both operands as they are: the key codes go from
+// HBM straight into operand registers, with no LDS staging and no
+// dequantisation.
+//
+// Operand layout of k-step ks (64 features): lane l = n + 32h holds 32 codes
+// of row n (query head or key); bytes 0..15 are features 64ks + 16h + 0..15
+// (MX block 2ks), bytes 16..31 features 64ks + 32 + 16h + 0..15 (block
+// 2ks+1), and its scale operand is row n's e8m0 code of block 2ks + h.  (The
+// matrix core takes the 32 values of a scale block 16 from each lane half,
+// and the scale of row n's block b from lane n + 32b.)
+typedef int v8i __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ v8i join8(const uint4& lo, const uint4& hi) {
+  v8i r;
+  r[0] = (int)lo.x; r[1] = (int)lo.y; r[2] = (int)lo.z; r[3] = (int)lo.w;
+  r[4] = (int)hi.x; r[5] = (int)hi.y; r[6] = (int)hi.z; r[7] = (int)hi.w;
+  return r;
+}
+
+// One 32-key stage in registers: lane (n, h) holds key n's codes of pieces
+// (ks, p) at byte 64ks + 32p + 16h, and the key's scale word.
+template <int DI>
+struct KeysQ8 {
+  uint4 v[DI / 32];   // v[2ks + p]
+  uint32_t sc;        // e8m0 codes of the key's DI/32 blocks, block j in byte j
+};
+
+template <int DI>
+__device__ __forceinline__ void keys_load_q8(KeysQ8<DI>& st,
+                                             const CacheView& kc, int b,
+                                             int kbase, int lane) {
+  const int n = lane & 31, h = lane >> 5;
+  int64_t row;
+  if (kc.page_table != nullptr) {
+    // the 32 keys of a stage share one page (stages are 32-aligned, pages 64)
+    row = cache_row(kc.page_table, kc.max_pages, kc.L, b, kbase) + n;
+  } else {
+    row = (int64_t)b * kc.L + min(kbase + n, kc.L - 1);
+  }
+  const uint8_t* base = kc.data + row * DI + 16 * h;
+#pragma unroll
+  for (int i = 0; i < DI / 32; ++i) st.v[i] = ld16(base + 32 * i);
+  if constexpr (DI == 128)
+    st.sc = *reinterpret_cast<const uint32_t*>(kc.scale + row * 4);
+  else
+    st.sc = *reinterpret_cast<const uint16_t*>(kc.scale + row * 2);
+}
+
+// The query's A operands: quantised codes and the scale operands, plus the
+// head weights in accumulator-row layout (heads >= H_I contribute zero).
+// One share of a query's A operands -- head block m, k-step ks -- for the
+// 64 lanes: the bf16 features 64ks + 32(i/2) + 16h + 8(i%2) of head 32m + n
+// (loads first, addresses clamped to a real head), then quantised per MX
+// block (scale 2^X, X the smallest with 448 * 2^X >= the block's largest
+// magnitude) into the operand codes and this lane's scale operand.  Heads
+// past H_I quantise to zero.
+template <int DI>
+__device__ __forceinline__ void load_share_q8(const uint16_t* q_idx, int H_I,
+                                              int m, int ks, int lane,
+                                              uint4 (&raw)[4]) {
+  const int n = lane & 31, h = lane >> 5;
+  const uint16_t* src = q_idx + min(m * 32 + n, H_I - 1) * DI + 64 * ks + 16 * h;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) raw[i] = ld16(src + 32 * (i >> 1) + 8 * (i & 1));
+}
+
+__device__ __forceinline__ void quantise_share_q8(const uint4 (&raw)[4],
+                                                  bool valid, int lane,
+                                                  v8i& code_out,
+                                                  int& scale_out) {
+  const int h = lane >> 5;
+  uint32_t code[2][4];
+  int X[2];
+#pragma unroll
+  for (int pc = 0; pc < 2; ++pc) {
+    float f[16];
+    {
+      float t[8];
+      unpack8(raw[2 * pc], t);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) f[i] = valid ? t[i] : 0.0f;
+      unpack8(raw[2 * pc + 1], t);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) f[8 + i] = valid ? t[i] : 0.0f;
+    }
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(f[i]));
+    // the block's other 16 features sit in lane n + 32(1-h)
+    amax = fmaxf(amax, swap_halves(amax));
+    X[pc] = mx_exponent(amax);
+    const float inv = pow2_neg(X[pc]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      code[pc][i] = e4m3x4(f[4 * i] * inv, f[4 * i + 1] * inv,
+                           f[4 * i + 2] * inv, f[4 * i + 3] * inv);
+  }
+  code_out = join8(make_uint4(code[0][0], code[0][1], code[0][2], code[0][3]),
+                   make_uint4(code[1][0], code[1][1], code[1][2], code[1][3]));
+  scale_out = (h ? X[1] : X[0]) + 127;
+}
+
+// Head weights in accumulator-row layout 8(r/4) + 4h + r%4 of block m from
+// `wl`, the weight of head `lane` (0 past H_I), by lane exchange.
+template <int MB>
+__device__ __forceinline__ void spread_weights_q8(float wl, int lane,
+                                                  float (&wv)[MB][16]) {
+  const int h = lane >> 5;
+#pragma unroll
+  for (int m = 0; m < MB; ++m)
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      wv[m][r] = __shfl(wl, m * 32 + 8 * (r >> 2) + 4 * h + (r & 3));
+}
+
+// Scores of the stage's 32 keys against the query: in every lane, the score
+// of key lane % 32.
+template <int DI, int MB>
+__device__ __forceinline__ float scores_q8(const KeysQ8<DI>& st,
+                                           const v8i (&a)[MB][DI / 64],
+                                           const int (&as)[MB][DI / 64],
+                                           const float (&wv)[MB][16],
+                                           int lane) {
+  const int h = lane >> 5;
+  f32x16 acc[MB];
+#pragma unroll
+  for (int m = 0; m < MB; ++m) acc[m] = f32x16{};
+#pragma unroll
+  for (int ks = 0; ks < DI / 64; ++ks) {
+    const v8i bop = join8(st.v[2 * ks], st.v[2 * ks + 1]);
+    const int bs = (int)((st.sc >> (8 * (2 * ks + h))) & 0xffu);
+#pragma unroll
+    for (int m = 0; m < MB; ++m)
+      acc[m] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+          a[m][ks], bop, acc[m], 0, 0, 0, as[m][ks], 0, bs);
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int m = 0; m < MB; ++m)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s += wv[m][r] * fmaxf(acc[m][r], 0.f);
+  return s + swap_halves(s);
+}
+
+// Streaming indexer with quantised queries over MX keys: the grid and the
+// score buffering of indexer_stream_kernel; four stages in flight.  The four
+// waves of a workgroup score the same query row, so each quantises one share
+// of its operands into LDS (before any wave leaves) and all read them.
+template <int DI, int MB>
+__global__ __launch_bounds__(256, 2) void indexer_stream_q8_kernel(
+    IndexerLaunch p, int kpw, int xcd_rows) {
+  constexpr int kShares = MB * (DI / 64);   // (head block, k-step) pairs
+  static_assert(kShares <= kWavesPerWG, "one share per wave");
+  __shared__ float sbuf[kWavesPerWG][kFlush];
+  __shared__ v8i qcode[kShares][kWave];
+  __shared__ int qscale[kShares][kWave];
+  const int lane = lane_id();
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  int b = blockIdx.z, t = blockIdx.y, chunk = blockIdx.x;
+  if (xcd_rows) {
+    const int lin = (blockIdx.z * gridDim.y + blockIdx.y) * gridDim.x + blockIdx.x;
+    const int slot = lin >> 3;
+    const int row = (slot / gridDim.x) * 8 + (lin & 7);
+    chunk = slot % gridDim.x;
+    b = row / p.T;
+    t = row % p.T;
+  }
+  const int k0 = (chunk * kWavesPerWG + wave) * kpw;
+  const int k1 = min(k0 + kpw, p.row_len);
+  const int qpos = __builtin_amdgcn_readfirstlane(query_pos(p.qp, b, t));
+  float* srow = p.scores + ((int64_t)b * p.T + t) * p.row_len;
+  for (int s = max(k0, qpos + 1) + lane; s < k1; s += kWave)
+    srow[s] = out_val(p, -__builtin_inff());
+  const int kend = min(k1, qpos + 1);
+  const bool work = kend > k0;   // wave-uniform
+  const int nsub = work ? (kend - k0 + kSub - 1) / kSub : 1;
+  const int last = nsub - 1;
+  // Every iteration issues the same loads (the tail re-reads the last stage,
+  // an L2 hit, and its scores are dropped), so the compiler waits only for
+  // the stage it consumes.
+  // this wave's share of the query first, then the first four key stages,
+  // so that the quantisation waits only for the query.  Both are issued by
+  // every wave (a wave without a share re-loads share 0, one without keys
+  // loads position 0): loads under a branch would make the compiler's wait
+  // before the quantisation cover the key loads as well.
+  const int64_t qrow = (int64_t)b * p.T + t;
+  const int share = wave < kShares ? wave : 0;
+  const int qm = share / (DI / 64), qks = share % (DI / 64);
+  uint4 raw[4];
+  load_share_q8<DI>(p.q_idx + qrow * p.H_I * DI, p.H_I, qm, qks, lane, raw);
+  const float wraw = p.w[qrow * p.H_I + min(lane, p.H_I - 1)];
+  KeysQ8<DI> st[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+    keys_load_q8<DI>(st[u], p.keys, b, work ? k0 + min(u, last) * kSub : 0,
+                     lane);
+  if (wave < kShares) {
+    v8i c;
+    int sc;
+    quantise_share_q8(raw, qm * 32 + (lane & 31) < p.H_I, lane, c, sc);
+    qcode[wave][lane] = c;
+    qscale[wave][lane] = sc;
+  }
+  __syncthreads();
+  if (!work) return;
+  v8i a[MB][DI / 64];
+  int as[MB][DI / 64];
+#pragma unroll
+  for (int m = 0; m < MB; ++m)
+#pragma unroll
+    for (int ks = 0; ks < DI / 64; ++ks) {
+      a[m][ks] = qcode[m * (DI / 64) + ks][lane];
+      as[m][ks] = qscale[m * (DI / 64) + ks][lane];
+    }
+  float wv[MB][16];
+  spread_weights_q8<MB>(lane < p.H_I ? wraw : 0.f, lane, wv);
+  float* sb = sbuf[wave];
+  const auto flush = [&](int from, int to) {   // positions [from, to)
+    for (int s = from + lane; s < to; s += kWave) srow[s] = sb[(s - k0) % kFlush];
+  };
+  for (int i = 0; i < nsub; i += 4) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      // the products read the stage's registers, then its next load goes
+      // into the same registers (no copies: moving a register whose load is
+      // in flight would wait for every load)
+      const float sc = scores_q8<DI, MB>(st[u], a, as, wv, lane);
+      keys_load_q8<DI>(st[u], p.keys, b, k0 + min(i + u + 4, last) * kSub, lane);
+      if (lane < 32 && i + u < nsub)
+        sb[((i + u) * kSub + lane) % kFlush] = out_val(p, sc);
+    }
+    if ((i + 4) * kSub % kFlush == 0 && i + 4 < nsub)   // a full buffer
+      flush(k0 + (i + 4) * kSub - kFlush, k0 + (i + 4) * kSub);
   }
   const int done = (nsub - 1) / (kFlush / kSub) * kFlush;   // flushed so far
   flush(k0 + done, kend);
@@ -538,6 +792,24 @@ hipError_t launch_stream(const IndexerLaunch& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
+template <int DI, int MB>
+hipError_t launch_stream_q8(const IndexerLaunch& p, hipStream_t stream) {
+  // about 4 resident waves per CU (one per SIMD) on 256 CUs: with the query
+  // setup shared per workgroup, longer waves beat more of them (measured
+  // 29.5 us for 1024 waves against 30.3-31.6 us for 2048 on the FP8 decode
+  // batch)
+  const int64_t total = (int64_t)p.B * p.T * p.row_len;
+  int64_t kpw = (total + 1023) / 1024;
+  kpw = (kpw + kSub - 1) / kSub * kSub;
+  kpw = kpw < 64 ? 64 : (kpw > 4096 ? 4096 : kpw);
+  const int per_wg = (int)kpw * kWavesPerWG;
+  dim3 grid((p.row_len + per_wg - 1) / per_wg, p.T, p.B);
+  const int xcd_rows = ((p.B * p.T) & 7) == 0 ? 1 : 0;
+  hipLaunchKernelGGL((indexer_stream_q8_kernel<DI, MB>), grid, dim3(256), 0,
+                     stream, p, (int)kpw, xcd_rows);
+  return hipGetLastError();
+}
+
 template <int DI, int MB, bool FP8>
 hipError_t launch_any(const IndexerLaunch& p, hipStream_t stream) {
   // several queries per sequence share every key read: tile them
@@ -549,6 +821,13 @@ hipError_t launch_any(const IndexerLaunch& p, hipStream_t stream) {
 
 hipError_t launch_indexer(const IndexerLaunch& p, hipStream_t stream) {
   const bool mb1 = p.H_I <= 32;
+  if (p.q8) {   // quantised queries over MX keys
+    if (p.d_I == 128)
+      return mb1 ? launch_stream_q8<128, 1>(p, stream)
+                 : launch_stream_q8<128, 2>(p, stream);
+    return mb1 ? launch_stream_q8<64, 1>(p, stream)
+               : launch_stream_q8<64, 2>(p, stream);
+  }
   if (p.d_I == 128) {
     if (p.keys.fp8)
       return mb1 ? launch_any<128, 1, true>(p, stream)

@@ -2,6 +2,8 @@
 binding on seeded workloads and compare with the CPU oracle."""
 from __future__ import annotations
 
+import dataclasses
+
 import numpy as np
 import torch
 
@@ -20,7 +22,7 @@ def paged_cache(d) -> dsa.PagedCache:
                           kv_scale=d["kv_scale"])
 
 
-def run_decode_step(inp, d, pass_qpos=None):
+def run_decode_step(inp, d, pass_qpos=None, quantize_queries=False):
     """The whole path through dsa_decode_step; returns numpy idx/out/lse."""
     wl = inp.wl
     use_qpos = (wl.T > 1) if pass_qpos is None else pass_qpos
@@ -28,17 +30,19 @@ def run_decode_step(inp, d, pass_qpos=None):
     out, lse, _ = dsa.decode_step(
         paged_cache(d), d["q_idx"], d["w"], d["q"], wl.top_k, wl.softmax_scale,
         max_seq_len=int(inp.seq_lens.max()),
-        q_pos=d["q_pos"] if use_qpos else None, idx_out=idx)
+        q_pos=d["q_pos"] if use_qpos else None, idx_out=idx,
+        quantize_queries=quantize_queries)
     torch.cuda.synchronize()
     return idx.cpu().numpy(), out.cpu().numpy(), lse.cpu().numpy()
 
 
-def run_separate_ops(inp, d):
+def run_separate_ops(inp, d, quantize_queries=False):
     """Indexer -> Top-K -> attention through the three separate entry points
     (contiguous caches).  Returns numpy scores/idx/out/lse."""
     wl = inp.wl
     scores = dsa.indexer_scores(d["q_idx"], d["w"], d["kidx_c"], d["q_pos"],
-                                k_scale=d["kidx_scale_c"])
+                                k_scale=d["kidx_scale_c"],
+                                quantize_queries=quantize_queries)
     idx = dsa.topk(scores, d["q_pos"], wl.top_k)
     out, lse = dsa.sparse_mla_attn(d["q"], d["kv_c"], idx, wl.softmax_scale,
                                    kv_scale=d["kv_scale_c"])
@@ -70,19 +74,26 @@ def assert_attn_close(out, lse, ref, rows):
     assert lerr <= LSE_ABS_TOL, f"lse max|diff| {lerr:.3e} > {LSE_ABS_TOL}"
 
 
-def check_workload(wl, rows=None, separate=None):
-    """Generate, run the HIP path, run the oracle on `rows`, compare."""
+def check_workload(wl, rows=None, separate=None, q_idx=None,
+                   quantize_queries=False):
+    """Generate, run the HIP path, run the oracle on `rows`, compare.
+    ``q_idx``: bf16 bits replacing the generated indexer queries;
+    ``quantize_queries``: the fully quantised indexer on both sides."""
     inp = wk.generate(wl)
+    if q_idx is not None:
+        inp = dataclasses.replace(inp, q_idx=q_idx)
     d = to_device(inp)
     rows = rows or [(b, t) for b in range(wl.B) for t in range(wl.T)]
-    ref = oracle.decode_path(inp, rows=rows, want_scores=True)
-    idx, out, lse = run_decode_step(inp, d)
+    ref = oracle.decode_path(inp, rows=rows, want_scores=True,
+                             quantize_queries=quantize_queries)
+    idx, out, lse = run_decode_step(inp, d, quantize_queries=quantize_queries)
     assert_idx_equal(idx, ref["idx"], rows)
     assert_attn_close(out, lse, ref, rows)
     if separate is None:
         separate = inp.contiguous
     if separate:
-        scores, idx2, out2, lse2 = run_separate_ops(inp, d)
+        scores, idx2, out2, lse2 = run_separate_ops(
+            inp, d, quantize_queries=quantize_queries)
         L = inp.L
         for b, t in rows:
             qp = int(inp.q_pos[b, t])

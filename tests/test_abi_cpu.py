@@ -44,12 +44,12 @@ def test_status_strings():
 
 
 def scores_call(**kw):
-    a = dict(B=1, T=1, L=64, H_I=64, d_I=128, q=FAKE, w=FAKE, k=FAKE,
+    a = dict(B=1, T=1, L=64, H_I=64, d_I=128, q=FAKE, qm=0, w=FAKE, k=FAKE,
              kd=0, ks=None, qp=FAKE, out=FAKE)
     a.update(kw)
     return lib.dsa_indexer_scores(a["B"], a["T"], a["L"], a["H_I"], a["d_I"],
-                                  a["q"], a["w"], a["k"], a["kd"], a["ks"],
-                                  a["qp"], a["out"], None)
+                                  a["q"], a["qm"], a["w"], a["k"], a["kd"],
+                                  a["ks"], a["qp"], a["out"], None)
 
 
 def test_indexer_scores_validation():
@@ -61,6 +61,9 @@ def test_indexer_scores_validation():
     assert scores_call(d_I=96) == UNSUP
     assert scores_call(kd=7) == UNSUP
     assert scores_call(kd=1, ks=None) == NULL
+    assert scores_call(qm=2) == UNSUP             # unknown query mode
+    assert scores_call(qm=1) == UNSUP             # quantised queries: MX keys
+    assert scores_call(qm=1, kd=1, ks=FAKE, q=None) == NULL
     assert b"d_I" in lib.dsa_last_error() or True
 
 
@@ -101,14 +104,16 @@ def test_decode_step_validation():
 
     def f(cache=c, **kw):
         a = dict(B=2, T=1, H_I=64, d_I=128, H=128, K=64, msl=256, qp=None,
-                 ws=FAKE, wsb=1 << 40)
+                 ws=FAKE, wsb=1 << 40, qm=0)
         a.update(kw)
         return lib.dsa_decode_step(a["B"], a["T"], a["H_I"], a["d_I"], a["H"],
                                    a["K"], 0.07, ctypes.byref(cache) if cache
-                                   else None, a["msl"], FAKE, FAKE, FAKE,
-                                   a["qp"], FAKE, FAKE, None, a["ws"],
+                                   else None, a["msl"], FAKE, a["qm"], FAKE,
+                                   FAKE, a["qp"], FAKE, FAKE, None, a["ws"],
                                    a["wsb"], None)
     assert f(cache=None) == NULL
+    assert f(qm=1) == UNSUP                     # quantised queries: MX keys
+    assert f(qm=-1) == UNSUP
     assert f(T=2) == NULL                       # q_pos required for T > 1
     assert f(msl=257) == SHAPE                  # beyond max_pages * 64
     assert f(ws=None) == WS
