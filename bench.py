@@ -28,6 +28,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBPS = 8000.0
 PEAK_BF16_TFLOPS = 2500.0   # dense bf16 matrix-core peak of one MI355X
+PEAK_FP8_TFLOPS = 5000.0    # dense fp8 matrix-core peak of one MI355X
 METRIC = ("DSA decode tokens/sec at B=32,L=32K,k=2048; achieved HBM GB/s vs "
           "peak")
 REPLICAS = 3
@@ -309,18 +310,24 @@ def oracle_rate(inp, budget_s=4.0, quantize_queries=False):
             "kind": "oracle", "sample": f"{n} query rows, {dt:.1f} s"}
 
 
-def prefill_kernels(stream, steps=5, warmup=2, oracle_budget_s=0.0):
+def prefill_kernels(stream, steps=5, warmup=2, oracle_budget_s=0.0,
+                    quantized=False):
     """The prefill chunk (4096 queries at positions 61440..65535 of a
     65536-token bf16 context, 64 indexer heads x 128, top_k 2048, 128 MLA
     heads) through the three separate entry points, each timed on its own.
     The indexer is the dense contraction here: its rate is reported against
-    the bf16 matrix-core peak, with the causal (query, key) pairs as work."""
+    the matrix-core peak of its operand type, with the causal (query, key)
+    pairs as work.  quantized: MX keys and KV, and the fully quantised
+    indexer (queries to MX block-32, scaled FP8 products, FP8 peak)."""
+    import dataclasses
     import torch
     import indexed_sparse_attention_lightning_amd as dsa
     import workloads as wk
     from workloads.device import to_device
 
     wl = wk.WORKLOADS["prefill"]
+    if quantized:
+        wl = dataclasses.replace(wl, quantized=True)
     inp = wk.generate(wl)
     d = to_device(inp)
     L = inp.L
@@ -332,30 +339,35 @@ def prefill_kernels(stream, steps=5, warmup=2, oracle_budget_s=0.0):
                                                wl.H, wl.top_k)),
                      dtype=torch.uint8, device="cuda")
     ms_i = time_loop(lambda i: dsa.indexer_scores(
-        d["q_idx"], d["w"], d["kidx_c"], d["q_pos"], out=scores),
+        d["q_idx"], d["w"], d["kidx_c"], d["q_pos"], out=scores,
+        k_scale=d["kidx_scale_c"], quantize_queries=quantized),
         steps, warmup, stream)
     ms_t = time_loop(lambda i: dsa.topk(scores, d["q_pos"], wl.top_k,
                                         out=idx), steps, warmup, stream)
     ms_a = time_loop(lambda i: dsa.sparse_mla_attn(
         d["q"], d["kv_c"], idx, wl.softmax_scale, out=out, lse=lse,
-        workspace=ws), steps, warmup, stream)
+        kv_scale=d["kv_scale_c"], workspace=ws), steps, warmup, stream)
     pairs = int(np.sum(inp.q_pos.astype(np.int64) + 1))
     idx_flop = pairs * 2 * wl.H_I * wl.d_I
     attn_flop = wl.T * wl.H * wl.top_k * 2 * (576 + 512)
     idx_tf = idx_flop / (ms_i * 1e-3) / 1e12
     attn_tf = attn_flop / (ms_a * 1e-3) / 1e12
+    ipeak = PEAK_FP8_TFLOPS if quantized else PEAK_BF16_TFLOPS
     return {
-        "workload": "prefill chunk: 4096 queries at 61440..65535 of a 65536 "
-                    "bf16 context, top_k 2048",
+        "workload": ("prefill chunk: 4096 queries at 61440..65535 of a 65536 "
+                     "context, top_k 2048, " +
+                     ("MX keys and KV, quantised indexer queries (scaled FP8 "
+                      "products)" if quantized else "bf16")),
         "indexer_ms": round(ms_i, 4), "topk_ms": round(ms_t, 4),
         "sparse_mla_attn_ms": round(ms_a, 4),
         "indexer_roofline": {"bound": "mfma", "achieved": round(idx_tf, 1),
-                             "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                             "frac": round(idx_tf / PEAK_BF16_TFLOPS, 4),
+                             "peak": ipeak, "unit": "TFLOP/s",
+                             "frac": round(idx_tf / ipeak, 4),
                              "algorithmic_flop": idx_flop},
         "attn_tflops": round(attn_tf, 1),
         "attn_frac_of_bf16_peak": round(attn_tf / PEAK_BF16_TFLOPS, 4),
-        **({"cpu_oracle": oracle_rate(inp, oracle_budget_s)}
+        **({"cpu_oracle": oracle_rate(inp, oracle_budget_s,
+                                      quantize_queries=quantized)}
            if oracle_budget_s > 0 else {}),
         "tokens_per_s": round(wl.T / ((ms_i + ms_t + ms_a) * 1e-3), 1),
     }
@@ -373,7 +385,7 @@ def main(argv=None):
                     help="skip the FP8 and ragged decode configurations")
     ap.add_argument("--only-config",
                     choices=["decode_fp8", "decode_fp8_q8", "ragged",
-                             "decode_t128"],
+                             "decode_t128", "prefill", "prefill_quantized"],
                     help="time only this decode configuration (10 steps after "
                          "3 warm-up steps) and print its JSON object; for "
                          "kernel traces")
@@ -395,7 +407,10 @@ def main(argv=None):
 
     if args.only_config:
         st = torch.cuda.current_stream()
-        if args.only_config == "decode_t128":
+        if args.only_config.startswith("prefill"):
+            res = prefill_kernels(
+                st, quantized=args.only_config == "prefill_quantized")
+        elif args.only_config == "decode_t128":
             res = decode_t128_config(st, steps=10, warmup=3)
         elif args.only_config == "decode_fp8_q8":
             res = decode_config("decode_fp8", st, steps=10, warmup=3,
@@ -550,6 +565,9 @@ def main(argv=None):
     if not args.no_prefill:
         line["prefill"] = prefill_kernels(
             stream, oracle_budget_s=0 if args.no_cpu_baseline else 4.0)
+        line["prefill_quantized"] = prefill_kernels(
+            stream, oracle_budget_s=0 if args.no_cpu_baseline else 4.0,
+            quantized=True)
     if not args.no_configs:
         line["other_configs"] = {
             "decode_fp8": dict(workload="batch 32 x 32768, e4m3 indexer keys "

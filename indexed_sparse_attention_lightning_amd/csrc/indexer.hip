@@ -767,6 +767,195 @@ __global__ __launch_bounds__(kTileQ * kWave, 2) void indexer_tile_kernel(
   if (i < nst) stage(i, st[0]);
 }
 
+// Query-tiled quantised indexer (prefill chunks with quantised queries over
+// MX keys): the workgroup shape and causal skipping of indexer_tile_kernel;
+// the 64-key stages hold the e4m3 codes as they are (16-byte chunk c of key
+// n at chunk slot c ^ swz(n), conflict-free for the operand reads) plus the
+// keys' scale words, and every wave runs the scaled FP8 products against its
+// own query, quantised on load.
+template <int DI>
+struct TileStageQ8 {
+  static constexpr int kChunks = kStageKeys * DI / 16;   // 16-B code chunks
+  static constexpr int kThreads = kTileQ * kWave;
+  static constexpr int kLoads = (kChunks + kThreads - 1) / kThreads;
+  static_assert(kChunks % kThreads == 0 || kLoads == 1, "stage loads");
+  uint4 v[kLoads];
+  uint32_t sc;   // scale word of key tid (tid < 64)
+};
+
+template <int DI>
+__device__ __forceinline__ void tile_load_q8(TileStageQ8<DI>& st,
+                                             const CacheView& kc, int b,
+                                             int kbase, int tid) {
+  using CL = CodeLayout<DI>;
+  int64_t row0;
+  bool clamp = false;
+  if (kc.page_table != nullptr) {
+    row0 = cache_row(kc.page_table, kc.max_pages, kc.L, b, kbase);
+  } else {
+    row0 = (int64_t)b * kc.L + kbase;
+    clamp = kbase + kStageKeys > kc.L;
+  }
+#pragma unroll
+  for (int i = 0; i < TileStageQ8<DI>::kLoads; ++i) {
+    const int id = min(i * TileStageQ8<DI>::kThreads + tid,
+                       TileStageQ8<DI>::kChunks - 1);
+    const int n = id / CL::kChunks, c = id % CL::kChunks;
+    int64_t row = row0 + n;
+    if (clamp) row = (int64_t)b * kc.L + min(kbase + n, kc.L - 1);
+    st.v[i] = ld16(kc.data + row * DI + c * 16);
+  }
+  {
+    const int n = tid & (kStageKeys - 1);
+    int64_t row = row0 + n;
+    if (clamp) row = (int64_t)b * kc.L + min(kbase + n, kc.L - 1);
+    if constexpr (DI == 128)
+      st.sc = *reinterpret_cast<const uint32_t*>(kc.scale + row * 4);
+    else
+      st.sc = *reinterpret_cast<const uint16_t*>(kc.scale + row * 2);
+  }
+}
+
+template <int DI>
+__device__ __forceinline__ void tile_store_q8(const TileStageQ8<DI>& st,
+                                              uint4* tile, uint32_t* scl,
+                                              int tid) {
+  using CL = CodeLayout<DI>;
+#pragma unroll
+  for (int i = 0; i < TileStageQ8<DI>::kLoads; ++i) {
+    const int id = i * TileStageQ8<DI>::kThreads + tid;
+    if (id < TileStageQ8<DI>::kChunks) {
+      const int n = id / CL::kChunks, c = id % CL::kChunks;
+      tile[n * CL::kChunks + CL::slot(n, c)] = st.v[i];
+    }
+  }
+  if (tid < kStageKeys) scl[tid] = st.sc;
+}
+
+// Scores of 32 keys of an LDS stage (keys 0..31 of `tile`, scale words
+// `scl`) against the wave's quantised query: in every lane, the score of key
+// lane % 32.
+template <int DI, int MB>
+__device__ __forceinline__ float tile_scores_q8(const uint4* tile,
+                                                const uint32_t* scl,
+                                                const v8i (&a)[MB][DI / 64],
+                                                const int (&as)[MB][DI / 64],
+                                                const float (&wv)[MB][16],
+                                                int lane) {
+  using CL = CodeLayout<DI>;
+  const int n = lane & 31, h = lane >> 5;
+  const uint32_t sc = scl[n];
+  f32x16 acc[MB];
+#pragma unroll
+  for (int m = 0; m < MB; ++m) acc[m] = f32x16{};
+#pragma unroll
+  for (int ks = 0; ks < DI / 64; ++ks) {
+    const v8i bop = join8(tile[n * CL::kChunks + CL::slot(n, 4 * ks + h)],
+                          tile[n * CL::kChunks + CL::slot(n, 4 * ks + 2 + h)]);
+    const int bs = (int)((sc >> (8 * (2 * ks + h))) & 0xffu);
+#pragma unroll
+    for (int m = 0; m < MB; ++m)
+      acc[m] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+          a[m][ks], bop, acc[m], 0, 0, 0, as[m][ks], 0, bs);
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int m = 0; m < MB; ++m)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s += wv[m][r] * fmaxf(acc[m][r], 0.f);
+  return s + swap_halves(s);
+}
+
+template <int DI, int MB>
+__global__ __launch_bounds__(kTileQ * kWave, 2) void indexer_tile_q8_kernel(
+    IndexerLaunch p, int keys_per_wg) {
+  using CL = CodeLayout<DI>;
+  constexpr int kTileU4 = kStageKeys * DI / 16;
+  __shared__ uint4 lds[2][kTileU4];
+  __shared__ uint32_t scl[2][kStageKeys];
+  const int tid = threadIdx.x, lane = lane_id();
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int b = blockIdx.z;
+  const int t = blockIdx.y * kTileQ + wave;
+  const bool has_q = t < p.T;
+  const int c0 = blockIdx.x * keys_per_wg;
+  const int c1 = min(c0 + keys_per_wg, p.row_len);
+  // causal extent of the tile: its last query
+  int qmax = -1;
+  for (int w = 0; w < kTileQ; ++w) {
+    const int tt = blockIdx.y * kTileQ + w;
+    if (tt < p.T) qmax = max(qmax, query_pos(p.qp, b, tt));
+  }
+  const int qpos = has_q ? __builtin_amdgcn_readfirstlane(query_pos(p.qp, b, t)) : -1;
+  float* srow = has_q ? p.scores + ((int64_t)b * p.T + t) * p.row_len : nullptr;
+  if (has_q)
+    for (int s = max(c0, qpos + 1) + lane; s < c1; s += kWave)
+      srow[s] = out_val(p, -__builtin_inff());
+  const int kend = min(c1, qmax + 1);
+  if (kend <= c0) return;   // workgroup-uniform
+  const int nst = (kend - c0 + kStageKeys - 1) / kStageKeys;
+
+  // this wave's query: every share's loads, the first two key stages, then
+  // the quantisation (a query row past T re-reads row 0 and scores nothing)
+  const int64_t qrow = (int64_t)b * p.T + (has_q ? t : 0);
+  const uint16_t* qsrc = p.q_idx + qrow * p.H_I * DI;
+  uint4 raw[MB][DI / 64][4];
+#pragma unroll
+  for (int m = 0; m < MB; ++m)
+#pragma unroll
+    for (int ks = 0; ks < DI / 64; ++ks)
+      load_share_q8<DI>(qsrc, p.H_I, m, ks, lane, raw[m][ks]);
+  const float wraw = p.w[qrow * p.H_I + min(lane, p.H_I - 1)];
+  TileStageQ8<DI> st[2];
+  tile_load_q8<DI>(st[0], p.keys, b, c0, tid);
+  tile_load_q8<DI>(st[1], p.keys, b, c0 + min(1, nst - 1) * kStageKeys, tid);
+  v8i a[MB][DI / 64];
+  int as[MB][DI / 64];
+#pragma unroll
+  for (int m = 0; m < MB; ++m)
+#pragma unroll
+    for (int ks = 0; ks < DI / 64; ++ks)
+      quantise_share_q8(raw[m][ks], m * 32 + (lane & 31) < p.H_I, lane,
+                        a[m][ks], as[m][ks]);
+  float wv[MB][16];
+  spread_weights_q8<MB>(lane < p.H_I ? wraw : 0.f, lane, wv);
+
+  // two stages in flight in registers: stage i+2 loads while stage i is
+  // computed (the tail re-loads the last stage, whose loads are never stored)
+  const auto stage = [&](int i, TileStageQ8<DI>& sr) {
+    uint4* tile = lds[i & 1];
+    uint32_t* sl = scl[i & 1];
+    tile_store_q8<DI>(sr, tile, sl, tid);
+    tile_load_q8<DI>(sr, p.keys, b, c0 + min(i + 2, nst - 1) * kStageKeys, tid);
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < kStageKeys / kSub; ++u) {
+      const int kb = c0 + i * kStageKeys + u * kSub;
+      if (has_q && kb <= qpos) {   // wave-uniform
+        const float sc = tile_scores_q8<DI, MB>(tile + u * kSub * CL::kChunks,
+                                                sl + u * kSub, a, as, wv, lane);
+        const int s = kb + (lane & 31);
+        if (lane < 32 && s <= qpos && s < c1) srow[s] = out_val(p, sc);
+      }
+    }
+  };
+  int i = 0;
+  for (; i + 1 < nst; i += 2) {
+    stage(i, st[0]);
+    stage(i + 1, st[1]);
+  }
+  if (i < nst) stage(i, st[0]);
+}
+
+template <int DI, int MB>
+hipError_t launch_tile_q8(const IndexerLaunch& p, hipStream_t stream) {
+  const int kpw = 2048;
+  dim3 grid((p.row_len + kpw - 1) / kpw, (p.T + kTileQ - 1) / kTileQ, p.B);
+  hipLaunchKernelGGL((indexer_tile_q8_kernel<DI, MB>), grid,
+                     dim3(kTileQ * kWave), 0, stream, p, kpw);
+  return hipGetLastError();
+}
+
 template <int DI, int MB, bool FP8>
 hipError_t launch_tile(const IndexerLaunch& p, hipStream_t stream) {
   // chunks of 2048 keys: enough workgroups for 256 CUs at prefill sizes
@@ -817,16 +1006,20 @@ hipError_t launch_any(const IndexerLaunch& p, hipStream_t stream) {
                        : launch_stream<DI, MB, FP8>(p, stream);
 }
 
+template <int DI, int MB>
+hipError_t launch_q8(const IndexerLaunch& p, hipStream_t stream) {
+  return p.T >= kTileQ ? launch_tile_q8<DI, MB>(p, stream)
+                       : launch_stream_q8<DI, MB>(p, stream);
+}
+
 }  // namespace
 
 hipError_t launch_indexer(const IndexerLaunch& p, hipStream_t stream) {
   const bool mb1 = p.H_I <= 32;
   if (p.q8) {   // quantised queries over MX keys
     if (p.d_I == 128)
-      return mb1 ? launch_stream_q8<128, 1>(p, stream)
-                 : launch_stream_q8<128, 2>(p, stream);
-    return mb1 ? launch_stream_q8<64, 1>(p, stream)
-               : launch_stream_q8<64, 2>(p, stream);
+      return mb1 ? launch_q8<128, 1>(p, stream) : launch_q8<128, 2>(p, stream);
+    return mb1 ? launch_q8<64, 1>(p, stream) : launch_q8<64, 2>(p, stream);
   }
   if (p.d_I == 128) {
     if (p.keys.fp8)

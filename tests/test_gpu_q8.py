@@ -55,3 +55,14 @@ def test_quantised_indexer_full_decode_fp8():
     print("q8 full decode_fp8", flush=True)
     check_workload(wl, rows=[(0, 0), (13, 0), (31, 0)], q_idx=q,
                    quantize_queries=True)
+
+
+def test_quantised_indexer_full_prefill_chunk():
+    """The 4096-query prefill chunk over a 65536-token MX cache, sampled
+    rows (the query-tiled quantised kernel at full size)."""
+    wl = wk.scaled(W["prefill"], quantized=True)
+    q = wk.eighths(1002, (wl.B, wl.T, wl.H_I, wl.d_I))
+    print("q8 full prefill chunk", flush=True)
+    check_workload(wl, rows=[(0, 0), (0, 1), (0, 7), (0, 8), (0, 2047),
+                             (0, 4090), (0, 4095)], q_idx=q,
+                   quantize_queries=True)
