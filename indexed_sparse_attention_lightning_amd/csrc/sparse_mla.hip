@@ -568,6 +568,7 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_kernel(
   __shared__ uint4 buf2[kBufSlots];
   __shared__ uint4 ftile[FP8 ? kTileSlots : 1];
   __shared__ int32_t rows[kMaxSplitRows];
+  __shared__ int rowcnt[kMaxSplitRows / kThreads][kThreads / kWave];
   __shared__ uint4 qlds[128 * kQLdsStride];
   __shared__ float tmul[T128 ? kTmulRows * 32 : 1];
   static_assert(32 * kStageRow <= kBufSlots * 16 &&
@@ -611,7 +612,7 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_kernel(
   for (int u = 0; u < kRowIter; ++u) {
     const int i = tid + u * kThreads;
     const int r = s.r0 + i;
-    pos[u] = (i < s.ntiles * kRowsT && r < s.r1) ? idx[r] : -1;
+    pos[u] = r < s.r1 ? idx[r] : -1;
   }
   const int n = lane & 31, h = lane >> 5;
   const int head = wave * 32 + n;
@@ -639,13 +640,35 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_kernel(
 #pragma unroll
   for (int u = 0; u < kRowIter; ++u)
     if (!(pos[u] >= 0 && pos[u] < nvalid)) pos[u] = -1;
+  // The valid entries are compacted, in index order, to the front of the row
+  // table and only their tiles are run: padding (-1) and out-of-range entries
+  // cost neither loads nor products (a causal row shorter than K, or a short
+  // sequence, leaves most of its K entries empty).  A split without valid
+  // entries keeps one all-masked tile (out = 0, lse = -inf).
+  uint64_t bal[kRowIter];
 #pragma unroll
   for (int u = 0; u < kRowIter; ++u) {
-    const int i = tid + u * kThreads;
-    if (i < s.ntiles * kRowsT)
-      rows[i] = pos[u] >= 0 ? (int)cache_row(p.kv.page_table, p.kv.max_pages,
-                                              p.kv.L, s.b, pos[u])
-                            : ~dummy;
+    bal[u] = __builtin_amdgcn_ballot_w64(pos[u] >= 0);
+    if (lane == 0) rowcnt[u][wave] = __builtin_popcountll(bal[u]);
+  }
+  barrier(true);
+  {
+    const uint64_t below = (1ull << lane) - 1;
+    int base = 0;
+#pragma unroll
+    for (int u = 0; u < kRowIter; ++u) {
+      int off = base;
+#pragma unroll
+      for (int w = 0; w < kThreads / kWave; ++w) {
+        off += w < wave ? rowcnt[u][w] : 0;
+        base += rowcnt[u][w];
+      }
+      if (pos[u] >= 0)
+        rows[off + __builtin_popcountll(bal[u] & below)] =
+            (int)cache_row(p.kv.page_table, p.kv.max_pages, p.kv.L, s.b, pos[u]);
+    }
+    s.ntiles = max(1, (base + kRowsT - 1) / kRowsT);
+    if (base + tid < s.ntiles * kRowsT) rows[base + tid] = ~dummy;
   }
   barrier(true);
 
