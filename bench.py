@@ -311,7 +311,7 @@ def oracle_rate(inp, budget_s=4.0, quantize_queries=False):
 
 
 def prefill_kernels(stream, steps=5, warmup=2, oracle_budget_s=0.0,
-                    quantized=False):
+                    quantized=False, from_start=False):
     """The prefill chunk (4096 queries at positions 61440..65535 of a
     65536-token bf16 context, 64 indexer heads x 128, top_k 2048, 128 MLA
     heads) through the three separate entry points, each timed on its own.
@@ -328,6 +328,8 @@ def prefill_kernels(stream, steps=5, warmup=2, oracle_budget_s=0.0,
     wl = wk.WORKLOADS["prefill"]
     if quantized:
         wl = dataclasses.replace(wl, quantized=True)
+    if from_start:
+        wl = dataclasses.replace(wl, L=4096, first_pos=0)
     inp = wk.generate(wl)
     d = to_device(inp)
     L = inp.L
@@ -349,13 +351,18 @@ def prefill_kernels(stream, steps=5, warmup=2, oracle_budget_s=0.0,
         kv_scale=d["kv_scale_c"], workspace=ws), steps, warmup, stream)
     pairs = int(np.sum(inp.q_pos.astype(np.int64) + 1))
     idx_flop = pairs * 2 * wl.H_I * wl.d_I
-    attn_flop = wl.T * wl.H * wl.top_k * 2 * (576 + 512)
+    # attention work over the selected rows only (a causal row shorter than
+    # top_k selects all of its positions)
+    sel = int(np.sum(np.minimum(inp.q_pos.astype(np.int64) + 1, wl.top_k)))
+    attn_flop = sel * wl.H * 2 * (576 + 512)
     idx_tf = idx_flop / (ms_i * 1e-3) / 1e12
     attn_tf = attn_flop / (ms_a * 1e-3) / 1e12
     ipeak = PEAK_FP8_TFLOPS if quantized else PEAK_BF16_TFLOPS
+    where = ("0..4095 of a 4096" if from_start else
+             "61440..65535 of a 65536")
     return {
-        "workload": ("prefill chunk: 4096 queries at 61440..65535 of a 65536 "
-                     "context, top_k 2048, " +
+        "workload": (f"prefill chunk: 4096 queries at {where} context, "
+                     "top_k 2048, " +
                      ("MX keys and KV, quantised indexer queries (scaled FP8 "
                       "products)" if quantized else "bf16")),
         "indexer_ms": round(ms_i, 4), "topk_ms": round(ms_t, 4),
@@ -385,7 +392,8 @@ def main(argv=None):
                     help="skip the FP8 and ragged decode configurations")
     ap.add_argument("--only-config",
                     choices=["decode_fp8", "decode_fp8_q8", "ragged",
-                             "decode_t128", "prefill", "prefill_quantized"],
+                             "decode_t128", "prefill", "prefill_quantized",
+                             "prefill_from_start"],
                     help="time only this decode configuration (10 steps after "
                          "3 warm-up steps) and print its JSON object; for "
                          "kernel traces")
@@ -409,7 +417,8 @@ def main(argv=None):
         st = torch.cuda.current_stream()
         if args.only_config.startswith("prefill"):
             res = prefill_kernels(
-                st, quantized=args.only_config == "prefill_quantized")
+                st, quantized=args.only_config == "prefill_quantized",
+                from_start=args.only_config == "prefill_from_start")
         elif args.only_config == "decode_t128":
             res = decode_t128_config(st, steps=10, warmup=3)
         elif args.only_config == "decode_fp8_q8":
@@ -568,6 +577,9 @@ def main(argv=None):
         line["prefill_quantized"] = prefill_kernels(
             stream, oracle_budget_s=0 if args.no_cpu_baseline else 4.0,
             quantized=True)
+        line["prefill_from_start"] = prefill_kernels(
+            stream, oracle_budget_s=0 if args.no_cpu_baseline else 4.0,
+            from_start=True)
     if not args.no_configs:
         line["other_configs"] = {
             "decode_fp8": dict(workload="batch 32 x 32768, e4m3 indexer keys "

@@ -588,6 +588,15 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_kernel(
     token = (slot / nsplit) * 8 + xcd;
     split = slot % nsplit;
   }
+  // Several queries per sequence (a prefill chunk): take them last to first.
+  // Later queries have the longer causal rows, so the longest work items
+  // start first and the short ones fill the tail (largest-first list
+  // scheduling; measured 1.77 -> 1.73 ms for a 4096-query chunk from
+  // position 0, no change when every row is full).
+  if (p.T > 1) {
+    const int bb = token / p.T, tt = token % p.T;
+    token = bb * p.T + (p.T - 1 - tt);
+  }
   Split s;
   s.token = token;
   s.b = s.token / p.T;
