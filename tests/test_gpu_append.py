@@ -216,3 +216,41 @@ def test_decode_over_appended_t128_cache(name):
             kv_scale=cache.kv_scale.view(B, L, 5))
         torch.cuda.synchronize()
         assert_attn_close(out2.cpu().numpy(), lse2.cpu().numpy(), ref, rows)
+
+
+@pytest.mark.parametrize("which", ["keys_only", "latent_only"])
+def test_append_one_pool(which):
+    """Appending only one pool leaves the other untouched."""
+    rng = np.random.default_rng(230)
+    B, T, max_pages, num_pages = 2, 9, 2, 4
+    page_table = np.array([[0, 2], [1, 3]], dtype=np.int32)
+    kd, ks = _pool(rng, "mx32", num_pages, 128)
+    vd, vs = _pool(rng, "t128", num_pages, 576)
+    pos = np.stack([rng.permutation(128)[:T] for _ in range(B)]).astype(np.int32)
+    k_rows = wk.append_rows(231, B * T, 128).reshape(B, T, 128)
+    v_rows = wk.append_rows(232, B * T, 576).reshape(B, T, 576)
+    dk, dks = _dev_pool(kd, ks)
+    dv, dvs = _dev_pool(vd, vs)
+    cache = dsa.PagedCache(kidx=dk, kv=dv,
+                           page_table=torch.from_numpy(page_table).cuda(),
+                           seq_lens=torch.ones(B, dtype=torch.int32).cuda(),
+                           kidx_scale=dks, kv_scale=dvs)
+    keys = which == "keys_only"
+    dsa.cache_append(cache, torch.from_numpy(pos).cuda(),
+                     k_new=_bf16_t(k_rows) if keys else None,
+                     kv_new=None if keys else _bf16_t(v_rows))
+    torch.cuda.synchronize()
+    if keys:
+        ok_, oks = oracle.cache_append(kd.copy(), ks.copy(), "mx32",
+                                       page_table, pos, k_rows)
+        _same_bytes(dk, ok_, "key pool")
+        _same_bytes(dks, oks, "key scales")
+        _same_bytes(dv, vd, "latent pool (untouched)")
+        _same_bytes(dvs, vs, "latent scales (untouched)")
+    else:
+        ov, ovs = oracle.cache_append(vd.copy(), vs.copy(), "t128",
+                                      page_table, pos, v_rows)
+        _same_bytes(dv, ov, "latent pool")
+        _same_bytes(dvs, ovs, "latent scales")
+        _same_bytes(dk, kd, "key pool (untouched)")
+        _same_bytes(dks, ks, "key scales (untouched)")
