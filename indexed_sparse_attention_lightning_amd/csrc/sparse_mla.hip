@@ -836,13 +836,18 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_kernel(
 
 // Merge split partials: out = sum_s w_s * (O_s / l_s) / sum_s w_s with
 // w_s = l_s * 2^(m_s - M), M the largest m_s; lse = ln(2^M * sum_s w_s).
-// Every load of a thread (all splits' (m, l), then all splits' partial
-// values) is issued before any is used: the splits' latencies overlap.
+// One wave per (token, head), kCombHeads heads per workgroup; a lane merges
+// 8 consecutive values (16-byte loads).  Every load of a lane (all splits'
+// (m, l), then all splits' partial values) is issued before any is used, so
+// the splits' latencies overlap.
 constexpr int kMaxSplits = 16;
-__global__ __launch_bounds__(128) void combine_kernel(AttnLaunch p,
-                                                      int splits) {
-  const int token = blockIdx.x, head = blockIdx.y;
-  const int dv = threadIdx.x * 4;
+constexpr int kCombHeads = 4;
+__global__ __launch_bounds__(64 * kCombHeads) void combine_kernel(AttnLaunch p,
+                                                                  int splits) {
+  const int token = blockIdx.x;
+  const int head = blockIdx.y * kCombHeads + (int)(threadIdx.x / 64);
+  if (head >= p.H) return;
+  const int dv = (threadIdx.x & 63) * 8;
   const int64_t nslots = (int64_t)gridDim.x * splits * p.H;
   const uint16_t* po = reinterpret_cast<const uint16_t*>(p.partial);
   const float* ml = reinterpret_cast<const float*>(po + nslots * kValue);
@@ -853,12 +858,12 @@ __global__ __launch_bounds__(128) void combine_kernel(AttnLaunch p,
     mls[sp] = sp < splits
                   ? *reinterpret_cast<const float2*>(ml + 2 * (slot0 + (int64_t)sp * p.H))
                   : make_float2(-__builtin_inff(), 0.f);
-  uint2 v[kMaxSplits];
+  uint4 v[kMaxSplits];
 #pragma unroll
   for (int sp = 0; sp < kMaxSplits; ++sp)
     v[sp] = sp < splits
-                ? *reinterpret_cast<const uint2*>(po + (slot0 + (int64_t)sp * p.H) * kValue + dv)
-                : make_uint2(0u, 0u);
+                ? *reinterpret_cast<const uint4*>(po + (slot0 + (int64_t)sp * p.H) * kValue + dv)
+                : make_uint4(0u, 0u, 0u, 0u);
   float M = -__builtin_inff();
 #pragma unroll
   for (int sp = 0; sp < kMaxSplits; ++sp) {
@@ -866,7 +871,7 @@ __global__ __launch_bounds__(128) void combine_kernel(AttnLaunch p,
     M = (m != m || M != M) ? __builtin_nanf("") : fmaxf(M, m);
   }
   float wsum = 0.f;
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   if (M != -__builtin_inff() && M == M) {
 #pragma unroll
     for (int sp = 0; sp < kMaxSplits; ++sp) {
@@ -876,18 +881,20 @@ __global__ __launch_bounds__(128) void combine_kernel(AttnLaunch p,
                                                              : l * exp2f(m - M);
       wsum += f;
       if (f > 0.f) {   // a skipped split's values are never read
-        acc.x += f * __builtin_bit_cast(float, v[sp].x << 16);
-        acc.y += f * __builtin_bit_cast(float, v[sp].x & 0xffff0000u);
-        acc.z += f * __builtin_bit_cast(float, v[sp].y << 16);
-        acc.w += f * __builtin_bit_cast(float, v[sp].y & 0xffff0000u);
+        const uint32_t w[4] = {v[sp].x, v[sp].y, v[sp].z, v[sp].w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          acc[2 * i] += f * __builtin_bit_cast(float, w[i] << 16);
+          acc[2 * i + 1] += f * __builtin_bit_cast(float, w[i] & 0xffff0000u);
+        }
       }
     }
   }
   const float inv = wsum > 0.f ? 1.0f / wsum : 0.f;
-  *reinterpret_cast<float4*>(p.out + ((int64_t)token * p.H + head) * kValue +
-                             dv) =
-      make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
-  if (threadIdx.x == 0)
+  float4* o = reinterpret_cast<float4*>(p.out + ((int64_t)token * p.H + head) * kValue + dv);
+  o[0] = make_float4(acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv);
+  o[1] = make_float4(acc[4] * inv, acc[5] * inv, acc[6] * inv, acc[7] * inv);
+  if ((threadIdx.x & 63) == 0)
     p.lse[(int64_t)token * p.H + head] =
         M != M ? M
                : (wsum > 0.f ? (M + __builtin_log2f(wsum)) * kLn2
@@ -936,8 +943,9 @@ hipError_t launch_sparse_mla(const AttnLaunch& p, hipStream_t stream) {
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || used == 1) return e;
-  hipLaunchKernelGGL(combine_kernel, dim3(tokens, p.H), dim3(128), 0, stream,
-                     p, used);
+  hipLaunchKernelGGL(combine_kernel,
+                     dim3(tokens, (p.H + kCombHeads - 1) / kCombHeads),
+                     dim3(64 * kCombHeads), 0, stream, p, used);
   return hipGetLastError();
 }
 

@@ -4,7 +4,9 @@ Rows cover each workgroup shape of the kernel (rows up to 4K, 16K, 32K and
 64K positions keep their keys in registers; longer rows re-read them) and
 score distributions that stress the digit passes: heavy ties, a few
 distinct values, NaN / +-inf / -0 / subnormals, huge dynamic range, and
-the indexer's own distribution (multiples of 1/8 in a narrow band).
+the indexer's own distribution (multiples of 1/8 in a narrow band); and
+rows far from normal: light and heavy tails, two clusters, all-negative
+rows, far outliers, and a spike row with K - 1 keys above a constant.
 Index sets must match exactly.
 """
 import numpy as np
@@ -17,7 +19,7 @@ import oracle
 pytestmark = pytest.mark.gpu
 
 
-def _rows(kind, rng, R, L):
+def _rows(kind, rng, R, L, K=2048):
     if kind == "normal":
         return rng.standard_normal((R, L)).astype(np.float32)
     if kind == "indexer_like":
@@ -33,10 +35,31 @@ def _rows(kind, rng, R, L):
         return x
     if kind == "all_equal":
         return np.full((R, L), 7.5, dtype=np.float32)
+    if kind == "uniform":
+        return rng.random((R, L)).astype(np.float32)
+    if kind == "heavy_tail":
+        return (rng.standard_exponential((R, L)) ** 3).astype(np.float32)
+    if kind == "two_clusters":
+        x = rng.standard_normal((R, L))
+        x[rng.random((R, L)) < 0.1] += 50.0
+        return x.astype(np.float32)
+    if kind == "negative":
+        return (-1000.0 + rng.standard_normal((R, L))).astype(np.float32)
+    if kind == "outlier":
+        x = rng.standard_normal((R, L)).astype(np.float32)
+        x[:, ::977] = 3e37
+        return x
+    if kind == "spike":
+        x = np.ones((R, L), dtype=np.float32)
+        for r in range(R):
+            x[r, rng.choice(L, size=min(K - 1, L), replace=False)] = 2.0
+        return x
     raise ValueError(kind)
 
 
-KINDS = ["normal", "indexer_like", "few_values", "specials", "all_equal"]
+KINDS = ["normal", "indexer_like", "few_values", "specials", "all_equal",
+         "uniform", "heavy_tail", "two_clusters", "negative", "outlier",
+         "spike"]
 LENGTHS = [700, 4096, 9000, 32768, 50000, 65536, 100000, 131072]
 
 
@@ -46,7 +69,7 @@ def test_topk_lengths_and_distributions(L):
     K = 2048 if L > 4096 else 300
     for kind in KINDS:
         R = 3
-        x = _rows(kind, rng, R, L)
+        x = _rows(kind, rng, R, L, K)
         # causal extents: full row, a ragged middle, and one short of K
         q_pos = np.array([[L - 1], [int(rng.integers(K, L))],
                           [min(K - 2, L - 1)]], dtype=np.int32)
