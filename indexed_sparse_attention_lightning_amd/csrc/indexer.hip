@@ -72,10 +72,21 @@ struct StageF8 {
   uint32_t sc;   // scale codes of key (lane % 32) of the stage, block j in byte j
 };
 
+// Past-the-end stages (a wave issues the same loads every step, so its last
+// steps load stages beyond its range, whose scores are dropped) read their
+// code or key bytes from `park` instead: the wave's own query row (pmask + 1
+// bytes of it), which the plain query loads left in L2.  Re-reading the last
+// real stage would go to HBM again, since the key stream's non-temporal
+// loads do not keep it in the caches.
+struct Park {
+  const uint8_t* at;   // nullptr: a real stage
+  int mask;            // a power of two minus one, within the query row
+};
+
 template <int DI>
 __device__ __forceinline__ void stage_load_f8(StageF8<DI>& st,
                                               const CacheView& kc, int b,
-                                              int kbase, int lane) {
+                                              int kbase, int lane, Park park) {
   using CL = CodeLayout<DI>;
   int64_t row0;
   bool clamp = false;
@@ -91,7 +102,8 @@ __device__ __forceinline__ void stage_load_f8(StageF8<DI>& st,
     const int n = id / CL::kChunks, c = id % CL::kChunks;
     int64_t row = row0 + n;
     if (clamp) row = (int64_t)b * kc.L + min(kbase + n, kc.L - 1);
-    st.v[i] = ld16(kc.data + row * DI + c * 16);
+    st.v[i] = ld16_stream(park.at ? park.at + ((id * 16) & park.mask)
+                                  : kc.data + row * DI + c * 16);
   }
   {
     const int n = lane & 31;
@@ -176,7 +188,7 @@ struct Stage {
 template <int DI, bool FP8>
 __device__ __forceinline__ void stage_load(Stage<DI, FP8>& st,
                                            const CacheView& kc, int b,
-                                           int kbase, int lane) {
+                                           int kbase, int lane, Park park) {
   using KL = KeyLayout<DI>;
   // the 32 keys of a stage share one page (stages are 32-aligned, pages 64)
   int64_t row0;
@@ -194,7 +206,8 @@ __device__ __forceinline__ void stage_load(Stage<DI, FP8>& st,
       const int n = id / KL::kChunks, c = id % KL::kChunks;
       int64_t row = row0 + n;
       if (clamp) row = (int64_t)b * kc.L + min(kbase + n, kc.L - 1);
-      st.v[i] = ld16(kc.data + row * (DI * 2) + c * 16);
+      st.v[i] = ld16_stream(park.at ? park.at + ((id * 16) & park.mask)
+                                    : kc.data + row * (DI * 2) + c * 16);
     } else {
       const int n = id / KL::kCodeChunks, c = id % KL::kCodeChunks;
       int64_t row = row0 + n;
@@ -325,6 +338,10 @@ __global__ __launch_bounds__(256, 2) void indexer_stream_kernel(
 
   uint4* tile = lds[wave];
   uint32_t* scl = sscale[wave];
+  const int qbytes = p.H_I * DI * 2;
+  const Park parked{reinterpret_cast<const uint8_t*>(p.q_idx + qrow * p.H_I * DI),
+                    (1 << (31 - __builtin_clz(qbytes))) - 1};
+  const auto park_if = [&](int stage) { return stage > nsub - 1 ? parked : Park{nullptr, 0}; };
   // Every iteration issues the same loads and stores (the tail re-reads the
   // last stage, an L2 hit, and its scores are masked), so the compiler can
   // count them and wait only for the stage it consumes.
@@ -338,13 +355,14 @@ __global__ __launch_bounds__(256, 2) void indexer_stream_kernel(
     StageF8<DI> st[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u)
-      stage_load_f8<DI>(st[u], p.keys, b, k0 + min(u, last) * kSub, lane);
+      stage_load_f8<DI>(st[u], p.keys, b, k0 + min(u, last) * kSub, lane,
+                        park_if(u));
     for (int i = 0; i < nsub; i += 4) {
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         stage_store_f8<DI>(st[u], tile, scl, lane);
         stage_load_f8<DI>(st[u], p.keys, b, k0 + min(i + u + 4, last) * kSub,
-                          lane);
+                          lane, park_if(i + u + 4));
         const float sc = tile_scores_f8<DI, MB>(tile, a, wv, scl, lane);
         // stages past the end (re-read tail) are not buffered
         if (lane < 32 && i + u < nsub)
@@ -355,17 +373,20 @@ __global__ __launch_bounds__(256, 2) void indexer_stream_kernel(
     }
   } else {
     Stage<DI, FP8> s0, s1;
-    stage_load<DI, FP8>(s0, p.keys, b, k0, lane);
-    stage_load<DI, FP8>(s1, p.keys, b, k0 + min(1, last) * kSub, lane);
+    stage_load<DI, FP8>(s0, p.keys, b, k0, lane, park_if(0));
+    stage_load<DI, FP8>(s1, p.keys, b, k0 + min(1, last) * kSub, lane,
+                        park_if(1));
     for (int i = 0; i < nsub; i += 2) {
       stage_store<DI, FP8>(s0, tile, lane);
-      stage_load<DI, FP8>(s0, p.keys, b, k0 + min(i + 2, last) * kSub, lane);
+      stage_load<DI, FP8>(s0, p.keys, b, k0 + min(i + 2, last) * kSub, lane,
+                          park_if(i + 2));
       {
         const float sc = tile_scores<DI, MB>(tile, a, wv, lane);
         if (lane < 32) sb[(i * kSub + lane) % kFlush] = out_val(p, sc);
       }
       stage_store<DI, FP8>(s1, tile, lane);
-      stage_load<DI, FP8>(s1, p.keys, b, k0 + min(i + 3, last) * kSub, lane);
+      stage_load<DI, FP8>(s1, p.keys, b, k0 + min(i + 3, last) * kSub, lane,
+                          park_if(i + 3));
       {
         const float sc = tile_scores<DI, MB>(tile, a, wv, lane);
         if (lane < 32) sb[((i + 1) * kSub + lane) % kFlush] = out_val(p, sc);
@@ -426,6 +447,9 @@ __device__ __forceinline__ void keys_load_q8(KeysQ8<DI>& st,
     row = (int64_t)b * kc.L + min(kbase + n, kc.L - 1);
   }
   const uint8_t* base = kc.data + row * DI + 16 * h;
+  // plain loads: an instruction reads 32 of a line's 128 bytes, and the
+  // line must stay in L2 for the other three (non-temporal loads, which do
+  // not keep it, fetched each line four times: 113 us against 98 per step)
 #pragma unroll
   for (int i = 0; i < DI / 32; ++i) st.v[i] = ld16(base + 32 * i);
   if constexpr (DI == 128)
