@@ -13,6 +13,8 @@
 //   T128  tiles of 128 features (the last of a 576-wide row holds 64): an fp32
 //         scale max|tile| / 448, elements as e4m3fn of x / scale, saturated
 //         at +-448 (an all-zero tile stores scale 0 and signed-zero codes).
+// Rows are read and pool bytes written with non-temporal accesses (each is
+// touched once).
 // e4m3fn rounding is to nearest, ties to even, in fp32 with correctly
 // rounded divisions, so the codes are a deterministic function of the input.
 //
@@ -64,9 +66,9 @@ __device__ __forceinline__ void put_chunk(const uint16_t* src, int c,
                                           int nscale, int gidx, int lane) {
   const bool own = slot >= 0;
   uint4 v = make_uint4(0, 0, 0, 0);
-  if (own) v = reinterpret_cast<const uint4*>(src)[c];
+  if (own) v = ld16_stream(reinterpret_cast<const uint4*>(src) + c);
   if constexpr (FMT == kFmtBf16) {
-    if (own) reinterpret_cast<uint4*>(pool + slot * width * 2)[c] = v;
+    if (own) st16_stream(reinterpret_cast<uint4*>(pool + slot * width * 2) + c, v);
   } else {
     float f[8];
     unpack8(v, f);
@@ -90,9 +92,9 @@ __device__ __forceinline__ void put_chunk(const uint16_t* src, int c,
         y[i] = fminf(fmaxf(__fdiv_rn(f[i], div), -kE4m3Max), kE4m3Max);
     }
     if (own) {
-      reinterpret_cast<uint2*>(pool + slot * width)[c] =
-          make_uint2(e4m3x4(y[0], y[1], y[2], y[3]),
-                     e4m3x4(y[4], y[5], y[6], y[7]));
+      st8_stream(reinterpret_cast<uint2*>(pool + slot * width) + c,
+                 make_uint2(e4m3x4(y[0], y[1], y[2], y[3]),
+                            e4m3x4(y[4], y[5], y[6], y[7])));
       if ((lane & (GL - 1)) == 0) {
         if constexpr (FMT == kFmtMx32)
           static_cast<uint8_t*>(scale)[slot * nscale + gidx] =

@@ -123,14 +123,25 @@ __device__ __forceinline__ uint32_t split_scale(uint32_t s_bits, float& m) {
 __device__ __forceinline__ uint4 ld16(const void* p) {
   return *reinterpret_cast<const uint4*>(p);
 }
-// A 16-byte load marked non-temporal, for bytes a launch reads exactly once
-// (the indexer's key stream): the caches do not keep the line, and the
-// stream reads faster (measured on the bf16 decode batch: 49.7-51.1 us
-// against 53.2-53.8 us per launch).
+// Loads and stores marked non-temporal, for bytes a launch touches exactly
+// once in whole cache lines (the indexer's key stream, the split partials,
+// the rows of a cache append): the caches do not keep the lines, and the
+// streams run faster (bf16 decode indexer 49.7-51.1 us against 53.2-53.8 us
+// per launch; whole-cache append 510-518 us against 531-535 us).  Where an
+// instruction reads only part of a line that later ones read again, plain
+// loads must stay: the line would be fetched again each time.
+typedef unsigned int u32x4_nt __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2_nt __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint4 ld16_stream(const void* p) {
-  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  const u32x4_nt v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_nt*>(p));
   return make_uint4(v[0], v[1], v[2], v[3]);
+}
+__device__ __forceinline__ void st16_stream(void* p, const uint4& v) {
+  __builtin_nontemporal_store(u32x4_nt{v.x, v.y, v.z, v.w},
+                              reinterpret_cast<u32x4_nt*>(p));
+}
+__device__ __forceinline__ void st8_stream(void* p, const uint2& v) {
+  __builtin_nontemporal_store(u32x2_nt{v.x, v.y}, reinterpret_cast<u32x2_nt*>(p));
 }
 __device__ __forceinline__ uint2 ld8(const void* p) {
   return *reinterpret_cast<const uint2*>(p);

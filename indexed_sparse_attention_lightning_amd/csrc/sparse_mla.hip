@@ -816,8 +816,8 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_kernel(
         uint4 v = *reinterpret_cast<const uint4*>(stg + r * kStageRow + (lane & 31) * 16);
         if (r >= 16) v = make_uint4(v.z, v.w, v.x, v.y);
         if (wave * 32 + r < p.H)
-          *reinterpret_cast<uint4*>(o0 + (int64_t)r * kValue + half * (kValue / 2) +
-                                    (lane & 31) * 8) = v;
+          st16_stream(o0 + (int64_t)r * kValue + half * (kValue / 2) + (lane & 31) * 8,
+                      v);
       }
       // a wave's LDS accesses run in order: the second half may overwrite
       // the first once its reads are issued
@@ -834,7 +834,9 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_kernel(
   }
 }
 
-// Merge split partials: out = sum_s w_s * (O_s / l_s) / sum_s w_s with
+// Merge split partials (written and read non-temporal: each is touched once
+// per step; 41.6-42.0 us against 42.9-43.0 us for the attention and the
+// merge together): out = sum_s w_s * (O_s / l_s) / sum_s w_s with
 // w_s = l_s * 2^(m_s - M), M the largest m_s; lse = ln(2^M * sum_s w_s).
 // One wave per (token, head), kCombHeads heads per workgroup; a lane merges
 // 8 consecutive values (16-byte loads).  Every load of a lane (all splits'
@@ -862,7 +864,7 @@ __global__ __launch_bounds__(64 * kCombHeads) void combine_kernel(AttnLaunch p,
 #pragma unroll
   for (int sp = 0; sp < kMaxSplits; ++sp)
     v[sp] = sp < splits
-                ? *reinterpret_cast<const uint4*>(po + (slot0 + (int64_t)sp * p.H) * kValue + dv)
+                ? ld16_stream(po + (slot0 + (int64_t)sp * p.H) * kValue + dv)
                 : make_uint4(0u, 0u, 0u, 0u);
   float M = -__builtin_inff();
 #pragma unroll
