@@ -74,8 +74,8 @@ struct StageF8 {
 
 // Past-the-end stages (a wave issues the same loads every step, so its last
 // steps load stages beyond its range, whose scores are dropped) read their
-// code or key bytes from `park` instead: the wave's own query row (pmask + 1
-// bytes of it), which the plain query loads left in L2.  Re-reading the last
+// code or key bytes from `park` instead: the first mask + 1 bytes of the
+// wave's own query row, which the plain query loads left in L2.  Re-reading the last
 // real stage would go to HBM again, since the key stream's non-temporal
 // loads do not keep it in the caches.
 struct Park {
@@ -341,10 +341,12 @@ __global__ __launch_bounds__(256, 2) void indexer_stream_kernel(
   const int qbytes = p.H_I * DI * 2;
   const Park parked{reinterpret_cast<const uint8_t*>(p.q_idx + qrow * p.H_I * DI),
                     (1 << (31 - __builtin_clz(qbytes))) - 1};
-  const auto park_if = [&](int stage) { return stage > nsub - 1 ? parked : Park{nullptr, 0}; };
-  // Every iteration issues the same loads and stores (the tail re-reads the
-  // last stage, an L2 hit, and its scores are masked), so the compiler can
-  // count them and wait only for the stage it consumes.
+  const auto park_if = [&](int stage) {
+    return stage > nsub - 1 ? parked : Park{nullptr, 0};
+  };
+  // Every iteration issues the same loads and stores (stages past the end
+  // read the parked query row and their scores are dropped), so the
+  // compiler can count them and wait only for the stage it consumes.
   const int last = nsub - 1;
   float* sb = sbuf[wave];
   const auto flush = [&](int from, int to) {   // positions [from, to)
@@ -364,7 +366,7 @@ __global__ __launch_bounds__(256, 2) void indexer_stream_kernel(
         stage_load_f8<DI>(st[u], p.keys, b, k0 + min(i + u + 4, last) * kSub,
                           lane, park_if(i + u + 4));
         const float sc = tile_scores_f8<DI, MB>(tile, a, wv, scl, lane);
-        // stages past the end (re-read tail) are not buffered
+        // stages past the end (parked) are not buffered
         if (lane < 32 && i + u < nsub)
           sb[((i + u) * kSub + lane) % kFlush] = out_val(p, sc);
       }
