@@ -77,7 +77,8 @@ size_t decode_ws(int B, int T, int L, int H, int K) {
   return align_up(tokens * (size_t)L * sizeof(float)) +
          align_up(tokens * (size_t)K * sizeof(int32_t)) +
          align_up(dsa::topk_workspace_bytes((int)tokens, L, K)) +
-         align_up(dsa::attn_workspace_bytes((int)tokens, H, K));
+         align_up(dsa::attn_workspace_bytes((int)tokens, H, K)) +
+         align_up(tokens * dsa::kSpanMax * 2 * sizeof(uint32_t));
 }
 
 // Quantised queries need MX keys: both operands of the scaled FP8 products.
@@ -262,6 +263,8 @@ dsa_status dsa_decode_step(int B, int T, int H_I, int d_I, int H, int K,
   const size_t topk_bytes = dsa::topk_workspace_bytes((int)tokens, max_seq_len, K);
   ws += align_up(topk_bytes);
   float* partial = reinterpret_cast<float*>(ws);
+  ws += align_up(dsa::attn_workspace_bytes((int)tokens, H, K));
+  uint32_t* span = reinterpret_cast<uint32_t*>(ws);
   if (idx_out) idx = idx_out;
 
   const hipStream_t st = (hipStream_t)stream;
@@ -281,6 +284,11 @@ dsa_status dsa_decode_step(int B, int T, int H_I, int d_I, int H, int K,
   ia.row_len = max_seq_len;
   ia.keys_out = 1;   // the Top-K below reads keys: no conversion there
   ia.q8 = q_mode == DSA_Q_MX32;
+  // the stream kernels also leave each wave's key range for the Top-K
+  const int span_kpw = dsa::indexer_span_kpw(ia);
+  const bool spans = span_kpw > 0 &&
+                     (max_seq_len + span_kpw - 1) / span_kpw <= dsa::kSpanMax;
+  ia.span = spans ? reinterpret_cast<float*>(span) : nullptr;
   if (hipError_t e = dsa::launch_indexer(ia, st))
     return hip_status(e, "dsa_decode_step: indexer");
 
@@ -289,6 +297,8 @@ dsa_status dsa_decode_step(int B, int T, int H_I, int d_I, int H, int K,
   ta.scores = scores;
   ta.qp = qp;
   ta.keys_in = 1;
+  ta.span = reinterpret_cast<const uint32_t*>(ia.span);
+  ta.span_kpw = spans ? span_kpw : 0;
   ta.idx = idx;
   if (hipError_t e = dsa::launch_topk(ta, topk_ws, topk_bytes, st))
     return hip_status(e, "dsa_decode_step: topk");

@@ -53,8 +53,21 @@ struct IndexerLaunch {
   int keys_out;            // store score_key(score) bit patterns, not scores
   int q8;                  // quantise q_idx to MX block-32 and use the scaled
                            // FP8 matrix cores (keys must be MX32)
+  float* span;             // keys_out only, or nullptr: per query row
+                           // kSpanMax (min, max) key pairs, one per wave of
+                           // the row (wave c covers positions c*kpw ..);
+                           // waves past the row's causal positions write
+                           // nothing.  The uint32 keys are stored as float bit
+                           // patterns: stores of an integer type could alias
+                           // the page table, whose loads then could not be
+                           // scalar loads
 };
+constexpr int kSpanMax = 64;   // waves per row with a key-range entry
 hipError_t launch_indexer(const IndexerLaunch& a, hipStream_t stream);
+// Positions per wave (and per span entry) of the stream kernel a launch
+// runs, or 0 when it keeps no key ranges (a tile kernel for several queries
+// per sequence, or the FP8-key kernel with bf16 queries).
+int indexer_span_kpw(const IndexerLaunch& a);
 
 struct TopkLaunch {
   int rows, T, L, K;       // rows = B*T; scores row stride = L
@@ -64,6 +77,9 @@ struct TopkLaunch {
   int nchunks, chunk;      // long rows: chunks per row, positions per chunk
   int32_t* cand;           // long rows: [rows, nchunks, K] candidate lists
   int keys_in;             // scores holds score_key bit patterns already
+  const uint32_t* span;    // keys_in rows only, or nullptr: the indexer's
+  int span_kpw;            // per-row key ranges, one per span_kpw positions
+                           // (entries past a row's causal positions unused)
 };
 // One workgroup per row.
 hipError_t launch_topk(const TopkLaunch& a, hipStream_t stream);

@@ -88,6 +88,10 @@ __device__ __forceinline__ void stage_load_f8(StageF8<DI>& st,
                                               const CacheView& kc, int b,
                                               int kbase, int lane, Park park) {
   using CL = CodeLayout<DI>;
+  // wave-uniform: the page-table lookup is then a scalar load (a vector one
+  // would be waited for with every key load in flight)
+  b = __builtin_amdgcn_readfirstlane(b);
+  kbase = __builtin_amdgcn_readfirstlane(kbase);
   int64_t row0;
   bool clamp = false;
   if (kc.page_table != nullptr) {
@@ -190,6 +194,10 @@ __device__ __forceinline__ void stage_load(Stage<DI, FP8>& st,
                                            const CacheView& kc, int b,
                                            int kbase, int lane, Park park) {
   using KL = KeyLayout<DI>;
+  // wave-uniform: the page-table lookup is then a scalar load (a vector one
+  // would be waited for with every key load in flight)
+  b = __builtin_amdgcn_readfirstlane(b);
+  kbase = __builtin_amdgcn_readfirstlane(kbase);
   // the 32 keys of a stage share one page (stages are 32-aligned, pages 64)
   int64_t row0;
   bool clamp = false;
@@ -292,6 +300,23 @@ __device__ __forceinline__ void load_query(const uint16_t* q_idx,
   }
 }
 
+// The (min, max) of the keys a wave wrote, over its lanes, into its span
+// entry (lane 0 stores).  Waves without causal positions store nothing (a
+// store on their early-exit path cost the page-table lookups their scalar
+// loads: the compiler then waited for every key load in flight at each).
+__device__ __forceinline__ void span_store(float* span, int64_t qrow,
+                                           int entry, uint32_t mn,
+                                           uint32_t mx, int lane) {
+#pragma unroll
+  for (int m = 1; m < kWave; m <<= 1) {
+    mn = min(mn, (uint32_t)__shfl_xor((int)mn, m));
+    mx = max(mx, (uint32_t)__shfl_xor((int)mx, m));
+  }
+  if (lane == 0)
+    reinterpret_cast<float2*>(span)[qrow * kSpanMax + entry] =
+        make_float2(__builtin_bit_cast(float, mn), __builtin_bit_cast(float, mx));
+}
+
 // Streaming indexer: grid (chunks, T, B); each wave scores `kpw`
 // consecutive positions of one query.  With `xcd_rows` (a row count that is
 // a multiple of 8) the linear workgroup id, which the dispatcher deals to the
@@ -327,12 +352,12 @@ __global__ __launch_bounds__(256, 2) void indexer_stream_kernel(
   for (int s = max(k0, qpos + 1) + lane; s < k1; s += kWave)
     srow[s] = out_val(p, -__builtin_inff());
   const int kend = min(k1, qpos + 1);
+  const int64_t qrow = (int64_t)b * p.T + t;
   if (kend <= k0) return;
   const int nsub = (kend - k0 + kSub - 1) / kSub;
 
   uint4 a[MB][DI / 16];
   float wv[MB][16];
-  const int64_t qrow = (int64_t)b * p.T + t;
   load_query<DI, MB, FP8>(p.q_idx + qrow * p.H_I * DI, p.w + qrow * p.H_I,
                           p.H_I, lane, a, wv);
 
@@ -349,8 +374,20 @@ __global__ __launch_bounds__(256, 2) void indexer_stream_kernel(
   // compiler can count them and wait only for the stage it consumes.
   const int last = nsub - 1;
   float* sb = sbuf[wave];
+  // The flushes also take this lane's (min, max) key over what they write:
+  // the wave's causal positions, once each (for the span entry; about 2
+  // instructions per 8 keys a lane, where tracking each stage cost the
+  // kernel about 1 us).
+  uint32_t kmn = ~0u, kmx = 0u;
   const auto flush = [&](int from, int to) {   // positions [from, to)
-    for (int s = from + lane; s < to; s += kWave) srow[s] = sb[(s - k0) % kFlush];
+    for (int s = from + lane; s < to; s += kWave) {
+      const float v = sb[(s - k0) % kFlush];
+      srow[s] = v;
+      if constexpr (!FP8) {   // (the FP8 kernel keeps no ranges: no registers)
+        kmn = min(kmn, __builtin_bit_cast(uint32_t, v));
+        kmx = max(kmx, __builtin_bit_cast(uint32_t, v));
+      }
+    }
   };
   if constexpr (FP8) {
     // stages are half the bytes of bf16 ones: four in flight
@@ -399,6 +436,7 @@ __global__ __launch_bounds__(256, 2) void indexer_stream_kernel(
   }
   const int done = (nsub - 1) / (kFlush / kSub) * kFlush;   // flushed so far
   flush(k0 + done, kend);
+  if (!FP8 && p.span) span_store(p.span, qrow, k0 / kpw, kmn, kmx, lane);
 }
 
 // ------------------------------------------------ quantised indexer (MX32)
@@ -440,6 +478,10 @@ template <int DI>
 __device__ __forceinline__ void keys_load_q8(KeysQ8<DI>& st,
                                              const CacheView& kc, int b,
                                              int kbase, int lane) {
+  // wave-uniform: the page-table lookup is then a scalar load (a vector one
+  // would be waited for with every key load in flight)
+  b = __builtin_amdgcn_readfirstlane(b);
+  kbase = __builtin_amdgcn_readfirstlane(kbase);
   const int n = lane & 31, h = lane >> 5;
   int64_t row;
   if (kc.page_table != nullptr) {
@@ -629,8 +671,18 @@ __global__ __launch_bounds__(256, 2) void indexer_stream_q8_kernel(
   float wv[MB][16];
   spread_weights_q8<MB>(lane < p.H_I ? wraw : 0.f, lane, wv);
   float* sb = sbuf[wave];
+  // The flushes also take this lane's (min, max) key over what they write:
+  // the wave's causal positions, once each (for the span entry; about 2
+  // instructions per 8 keys a lane, where tracking each stage cost the
+  // kernel about 1 us).
+  uint32_t kmn = ~0u, kmx = 0u;
   const auto flush = [&](int from, int to) {   // positions [from, to)
-    for (int s = from + lane; s < to; s += kWave) srow[s] = sb[(s - k0) % kFlush];
+    for (int s = from + lane; s < to; s += kWave) {
+      const float v = sb[(s - k0) % kFlush];
+      srow[s] = v;
+      kmn = min(kmn, __builtin_bit_cast(uint32_t, v));
+      kmx = max(kmx, __builtin_bit_cast(uint32_t, v));
+    }
   };
   for (int i = 0; i < nsub; i += 4) {
 #pragma unroll
@@ -648,6 +700,7 @@ __global__ __launch_bounds__(256, 2) void indexer_stream_q8_kernel(
   }
   const int done = (nsub - 1) / (kFlush / kSub) * kFlush;   // flushed so far
   flush(k0 + done, kend);
+  if (p.span) span_store(p.span, qrow, k0 / kpw, kmn, kmx, lane);
 }
 
 // ---------------------------------------------------------------- prefill
@@ -992,14 +1045,23 @@ hipError_t launch_tile(const IndexerLaunch& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// Positions per wave of the stream kernels: bf16 and FP8 keys about 8
+// resident waves per CU on 256 CUs (2048 waves); the quantised kernel about
+// 4 (one per SIMD: with the query setup shared per workgroup, longer waves
+// beat more of them, measured 29.5 us for 1024 waves against 30.3-31.6 us
+// for 2048 on the FP8 decode batch).  Whole 32-key stages, 64..4096.
+int stream_kpw(const IndexerLaunch& p) {
+  const int64_t total = (int64_t)p.B * p.T * p.row_len;
+  const int64_t waves = p.q8 ? 1024 : 2048;
+  int64_t kpw = (total + waves - 1) / waves;
+  kpw = (kpw + kSub - 1) / kSub * kSub;
+  return (int)(kpw < 64 ? 64 : (kpw > 4096 ? 4096 : kpw));
+}
+
 template <int DI, int MB, bool FP8>
 hipError_t launch_stream(const IndexerLaunch& p, hipStream_t stream) {
-  // about 8 resident waves per CU on 256 CUs
-  const int64_t total = (int64_t)p.B * p.T * p.row_len;
-  int64_t kpw = (total + 2047) / 2048;
-  kpw = (kpw + kSub - 1) / kSub * kSub;
-  kpw = kpw < 64 ? 64 : (kpw > 4096 ? 4096 : kpw);
-  const int per_wg = (int)kpw * kWavesPerWG;
+  const int kpw = stream_kpw(p);
+  const int per_wg = kpw * kWavesPerWG;
   dim3 grid((p.row_len + per_wg - 1) / per_wg, p.T, p.B);
   const int xcd_rows = ((p.B * p.T) & 7) == 0 ? 1 : 0;
   hipLaunchKernelGGL((indexer_stream_kernel<DI, MB, FP8>), grid, dim3(256), 0,
@@ -1009,15 +1071,8 @@ hipError_t launch_stream(const IndexerLaunch& p, hipStream_t stream) {
 
 template <int DI, int MB>
 hipError_t launch_stream_q8(const IndexerLaunch& p, hipStream_t stream) {
-  // about 4 resident waves per CU (one per SIMD) on 256 CUs: with the query
-  // setup shared per workgroup, longer waves beat more of them (measured
-  // 29.5 us for 1024 waves against 30.3-31.6 us for 2048 on the FP8 decode
-  // batch)
-  const int64_t total = (int64_t)p.B * p.T * p.row_len;
-  int64_t kpw = (total + 1023) / 1024;
-  kpw = (kpw + kSub - 1) / kSub * kSub;
-  kpw = kpw < 64 ? 64 : (kpw > 4096 ? 4096 : kpw);
-  const int per_wg = (int)kpw * kWavesPerWG;
+  const int kpw = stream_kpw(p);
+  const int per_wg = kpw * kWavesPerWG;
   dim3 grid((p.row_len + per_wg - 1) / per_wg, p.T, p.B);
   const int xcd_rows = ((p.B * p.T) & 7) == 0 ? 1 : 0;
   hipLaunchKernelGGL((indexer_stream_q8_kernel<DI, MB>), grid, dim3(256), 0,
@@ -1059,6 +1114,12 @@ hipError_t launch_indexer(const IndexerLaunch& p, hipStream_t stream) {
                : launch_any<64, 2, true>(p, stream);
   return mb1 ? launch_any<64, 1, false>(p, stream)
              : launch_any<64, 2, false>(p, stream);
+}
+
+int indexer_span_kpw(const IndexerLaunch& p) {
+  // the FP8 stream kernel (MX keys, bf16 queries) keeps no key ranges
+  const bool fp8_stream = p.keys.fp8 && !p.q8;
+  return p.T >= kTileQ || fp8_stream ? 0 : stream_kpw(p);
 }
 
 }  // namespace dsa

@@ -264,7 +264,11 @@ struct RowKeys {
 //            Top-Ks (an entry of the row's Top-K has fewer than K entries
 //            above it in its own chunk), and slot order is position order,
 //            so ties still go to the lower position.
-enum TopkMode { kRow = 0, kChunk = 1, kGather = 2 };
+//   kRowSpan as kRow, for rows whose keys the indexer wrote together with
+//            each of its waves' (min, max) key: the row's range is known
+//            before the keys arrive, so the first histogram counts each key
+//            step as its load completes (no pass and barrier for the range)
+enum TopkMode { kRow = 0, kChunk = 1, kGather = 2, kRowSpan = 3 };
 
 template <int KPT, bool RES, int MODE = kRow>
 __global__ __launch_bounds__(kThreads, 1) void topk_kernel(TopkLaunch p) {
@@ -279,7 +283,7 @@ __global__ __launch_bounds__(kThreads, 1) void topk_kernel(TopkLaunch p) {
   const float* rowp = p.scores + (int64_t)r * p.L;
   const int32_t* cand = nullptr;
   int32_t* out;
-  if constexpr (MODE == kRow) {
+  if constexpr (MODE == kRow || MODE == kRowSpan) {
     n = nrow;
     kk = min(p.K, n);
     out = p.idx + (int64_t)r * p.K;
@@ -304,6 +308,20 @@ __global__ __launch_bounds__(kThreads, 1) void topk_kernel(TopkLaunch p) {
     return;
   }
   if (MODE == kGather && kk == 0) return;
+
+  // the row's key range from the indexer's span entries, loaded before the
+  // keys (the wait counter retires loads in issue order)
+  // (entries 0 .. ns-1 cover the row's causal positions 0 .. n-1; ns <= 64)
+  uint32_t smn = 0xffffffffu, smx = 0u;
+  if constexpr (MODE == kRowSpan) {
+    const int ns = (n + p.span_kpw - 1) / p.span_kpw;
+    const uint2 v = reinterpret_cast<const uint2*>(
+        p.span)[(int64_t)r * kSpanMax + min(lane, ns - 1)];
+    if (lane < ns) {
+      smn = v.x;
+      smx = v.y;
+    }
+  }
 
   RowKeys<KPT, RES> keys;
   keys.row = rowp;
@@ -355,22 +373,26 @@ __global__ __launch_bounds__(kThreads, 1) void topk_kernel(TopkLaunch p) {
             rs, (keys.wbase + lane) * 4, j * kWave * 4, 0);
       // keys of candidates are >= 1 (NaN maps to 1): 0 marks a lane past n
       // (only waves that reach past n test positions; the conversion is
-      // skipped when the row holds keys)
-      const bool padded = keys.wbase + KPT * kWave > n;   // wave-uniform
-      const bool kin = keys.keys_in;
-      if (padded) {
+      // skipped when the row holds keys).  kRowSpan rows hold keys and
+      // the bounded loads read 0 past n: nothing to convert, and the range
+      // comes from the span entries.
+      if constexpr (MODE != kRowSpan) {
+        const bool padded = keys.wbase + KPT * kWave > n;   // wave-uniform
+        const bool kin = keys.keys_in;
+        if (padded) {
 #pragma unroll
-        for (int j = 0; j < KPT; ++j)
-          keys.k[j] = keys.valid(j) ? as_key(keys.k[j], kin) : 0u;
-      } else if (!kin) {
+          for (int j = 0; j < KPT; ++j)
+            keys.k[j] = keys.valid(j) ? as_key(keys.k[j], kin) : 0u;
+        } else if (!kin) {
 #pragma unroll
-        for (int j = 0; j < KPT; ++j)
-          keys.k[j] = score_key(__builtin_bit_cast(float, keys.k[j]));
-      }
+          for (int j = 0; j < KPT; ++j)
+            keys.k[j] = score_key(__builtin_bit_cast(float, keys.k[j]));
+        }
 #pragma unroll
-      for (int j = 0; j < KPT; ++j) {
-        mn = min(mn, keys.k[j] - 1u);
-        mx = max(mx, keys.k[j]);
+        for (int j = 0; j < KPT; ++j) {
+          mn = min(mn, keys.k[j] - 1u);
+          mx = max(mx, keys.k[j]);
+        }
       }
     }
   } else {
@@ -389,21 +411,30 @@ __global__ __launch_bounds__(kThreads, 1) void topk_kernel(TopkLaunch p) {
       e[i] = make_uint4(0, 0, 0, 0);
     if (tid == 0) sm.overflow = 0u;
   }
-  wave_minmax(mn, mx);
-  if (lane == 0) {
-    sm.wmin[wave] = mn;
-    sm.wmax[wave] = mx;
+  uint32_t kmin, kmax;
+  if constexpr (MODE == kRowSpan) {
+    // every wave reduces the span entries itself: no exchange
+    kmin = smn != 0xffffffffu ? smn - 1u : 0xffffffffu;
+    kmax = smx;
+    wave_minmax(kmin, kmax);
+    __syncthreads();   // the cleared histogram and bitmap
+  } else {
+    wave_minmax(mn, mx);
+    if (lane == 0) {
+      sm.wmin[wave] = mn;
+      sm.wmax[wave] = mx;
+    }
+    __syncthreads();
+    kmin = lane < kWaves ? sm.wmin[lane] : 0xffffffffu;
+    kmax = lane < kWaves ? sm.wmax[lane] : 0u;
+    wave_minmax(kmin, kmax);
   }
-  __syncthreads();
-  uint32_t kmin = lane < kWaves ? sm.wmin[lane] : 0xffffffffu;
-  uint32_t kmax = lane < kWaves ? sm.wmax[lane] : 0u;
-  wave_minmax(kmin, kmax);
   // some lane holds a candidate (n >= 2 here).  kmin is the smallest
   // candidate key minus one: candidates have relative keys >= 1 and lanes
   // past n (or holes between candidate slots) the relative key 0, which no
   // histogram, candidate list or bitmap takes.
   keys.kmin = kmin;
-  if constexpr (RES) {
+  if constexpr (RES && MODE != kRowSpan) {   // kRowSpan: in the first count
 #pragma unroll
     for (int j = 0; j < KPT; ++j)
       keys.k[j] = keys.k[j] ? keys.k[j] - kmin : 0u;
@@ -427,7 +458,27 @@ __global__ __launch_bounds__(kThreads, 1) void topk_kernel(TopkLaunch p) {
     // only waves that reach past n (or hold candidate-slot holes) have
     // keys to skip; the others count without the test
     const bool padded = MODE == kGather || keys.wbase + KPT * kWave > n;
-    if constexpr (RES) {
+    if constexpr (MODE == kRowSpan) {
+      // each key step is made relative and counted as its load completes
+      if (padded) {
+#pragma unroll
+        for (int j = 0; j < KPT; ++j) {
+          const uint32_t k = keys.k[j];
+          const uint32_t rk = k ? k - kmin : 0u;
+          keys.k[j] = rk;
+          if (rk != 0u) atomicAdd(&sm.hist[rk >> nsh], 1u);
+          TOPK_STEP_FENCE(j);
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < KPT; ++j) {
+          const uint32_t rk = keys.k[j] - kmin;   // keys >= 1 > kmin
+          keys.k[j] = rk;
+          atomicAdd(&sm.hist[rk >> nsh], 1u);
+          TOPK_STEP_FENCE(j);
+        }
+      }
+    } else if constexpr (RES) {
       if (padded) {
 #pragma unroll
         for (int j = 0; j < KPT; ++j) {
@@ -657,10 +708,10 @@ __global__ __launch_bounds__(kThreads, 1) void topk_kernel(TopkLaunch p) {
   }
 }
 
-template <int KPT, bool RES>
+template <int KPT, bool RES, int MODE = kRow>
 void launch_kpt(const TopkLaunch& p, hipStream_t stream) {
-  hipLaunchKernelGGL((topk_kernel<KPT, RES>), dim3(p.rows), dim3(kThreads), 0,
-                     stream, p);
+  hipLaunchKernelGGL((topk_kernel<KPT, RES, MODE>), dim3(p.rows),
+                     dim3(kThreads), 0, stream, p);
 }
 
 constexpr int kChunkLen = 16 * kThreads;   // positions per chunk workgroup
@@ -704,6 +755,18 @@ hipError_t launch_topk(const TopkLaunch& p0, void* workspace,
 
 hipError_t launch_topk(const TopkLaunch& p, hipStream_t stream) {
   // positions per row a workgroup covers: 1024 * KPT
+  if (p.span != nullptr && p.keys_in && p.span_kpw > 0 &&
+      (p.L + p.span_kpw - 1) / p.span_kpw <= kSpanMax && p.L <= 64 * kThreads) {
+    if (p.L <= 4 * kThreads)
+      launch_kpt<4, true, kRowSpan>(p, stream);
+    else if (p.L <= 16 * kThreads)
+      launch_kpt<16, true, kRowSpan>(p, stream);
+    else if (p.L <= 32 * kThreads)
+      launch_kpt<32, true, kRowSpan>(p, stream);
+    else
+      launch_kpt<64, true, kRowSpan>(p, stream);
+    return hipGetLastError();
+  }
   if (p.L <= 4 * kThreads)
     launch_kpt<4, true>(p, stream);
   else if (p.L <= 16 * kThreads)

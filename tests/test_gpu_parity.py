@@ -189,6 +189,31 @@ def test_contiguous_api_unaligned_length(T, first_pos):
     assert_attn_close(out.cpu().numpy(), lse.cpu().numpy(), ref, rows)
 
 
+def test_decode_rows_shorter_than_context():
+    """The decode batch (32 x 32768) with some sequences far shorter than
+    the context.  The indexer's waves past a row's last position leave no
+    key range, and the Top-K (which takes each row's key range from the
+    waves that scored it) must use only the ranges of waves with causal
+    positions: rows of several lengths, one shorter than K (every position
+    selected), compared with the oracle."""
+    import dataclasses
+    wl = W["decode"]
+    inp = wk.generate(wl)
+    lens = inp.seq_lens.copy()
+    short = {0: 2100, 5: 9000, 17: 20000, 30: 1500, 31: 30001}
+    for b, n in short.items():
+        lens[b] = n
+    inp = dataclasses.replace(inp, seq_lens=lens,
+                              q_pos=(lens - 1).reshape(-1, 1).astype(np.int32))
+    d = to_device(inp)
+    rows = [(b, 0) for b in sorted(short)] + [(3, 0)]
+    ref = oracle.decode_path(inp, rows=rows)
+    idx, out, lse = run_decode_step(inp, d)
+    assert_idx_equal(idx, ref["idx"], rows)
+    assert_attn_close(out, lse, ref, rows)
+    assert np.all(idx[30, 0, 1500:] == -1)
+
+
 def test_indexer_long_wave_ranges():
     """Many long rows: each wave scores more than one LDS score buffer
     (several flushes per wave) and a tail shorter than a stage; queries at
