@@ -309,9 +309,9 @@ __global__ __launch_bounds__(kThreads, 1) void topk_kernel(TopkLaunch p) {
   }
   if (MODE == kGather && kk == 0) return;
 
-  // the row's key range from the indexer's span entries, loaded before the
-  // keys (the wait counter retires loads in issue order)
-  // (entries 0 .. ns-1 cover the row's causal positions 0 .. n-1; ns <= 64)
+  // the row's key range from the indexer's span entries 0 .. ns-1 (those
+  // that cover its causal positions 0 .. n-1), loaded before the keys: the
+  // wait counter retires loads in issue order
   uint32_t smn = 0xffffffffu, smx = 0u;
   if constexpr (MODE == kRowSpan) {
     const int ns = (n + p.span_kpw - 1) / p.span_kpw;
