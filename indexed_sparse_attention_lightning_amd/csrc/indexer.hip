@@ -1045,14 +1045,17 @@ hipError_t launch_tile(const IndexerLaunch& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// Positions per wave of the stream kernels: bf16 and FP8 keys about 8
-// resident waves per CU on 256 CUs (2048 waves); the quantised kernel about
-// 4 (one per SIMD: with the query setup shared per workgroup, longer waves
-// beat more of them, measured 29.5 us for 1024 waves against 30.3-31.6 us
-// for 2048 on the FP8 decode batch).  Whole 32-key stages, 64..4096.
+// Positions per wave of the stream kernels, for about 1024 waves (one per
+// SIMD on 256 CUs) or, for FP8 keys with bf16 queries, 2048 (that kernel is
+// bound by each wave's matrix and dequantisation work, which a second wave
+// per SIMD hides).  Longer waves pay their query setup less often: the
+// quantised kernel measured 29.5 us for 1024 waves against 30.3-31.6 us for
+// 2048 on the FP8 decode batch, and the bf16 one, with the non-temporal key
+// stream, 47.7-48.8 us against 48.7-49.7 us (4096: 48.2-49.2) on the bf16
+// decode batch.  Whole 32-key stages, 64..4096.
 int stream_kpw(const IndexerLaunch& p) {
   const int64_t total = (int64_t)p.B * p.T * p.row_len;
-  const int64_t waves = p.q8 ? 1024 : 2048;
+  const int64_t waves = p.keys.fp8 && !p.q8 ? 2048 : 1024;
   int64_t kpw = (total + waves - 1) / waves;
   kpw = (kpw + kSub - 1) / kSub * kSub;
   return (int)(kpw < 64 ? 64 : (kpw > 4096 ? 4096 : kpw));
