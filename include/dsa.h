@@ -108,7 +108,10 @@ typedef enum dsa_op {
  * Architectures", section 3: the fused indexer reads the paged key cache
  * directly).  Logical position s of sequence b lives in physical page
  * page_table[b * max_pages_per_seq + s / 64], row s % 64.  Entries past a
- * sequence's last page are never read.
+ * sequence's last page are never read.  Every entry that is read (the
+ * pages of positions 0 .. seq_lens[b]-1) must lie in [0, num_pages): the
+ * kernels clamp an entry outside that range into it, so a bad table reads
+ * wrong rows but never outside the pools.
  */
 typedef struct dsa_paged_cache {
   int32_t page_size;          /* tokens per page; must be 64                */
@@ -153,7 +156,12 @@ dsa_status dsa_indexer_scores(int B, int T, int L, int H_I, int d_I,
                               float* scores, void* stream);
 
 /*
- * Top-K per score row (step 2).
+ * Top-K per score row (step 2): the indexer's selection of the most relevant
+ * history positions (page "Day-0 Inference Optimization for a New Sparse
+ * Attention Architecture: A Technical Deep Dive", section 1, Lightning
+ * Indexer; page "Inference Optimization for New Open-Source LLM
+ * Architectures", "Architectural Overview": the Top-K most relevant
+ * positions).  The pages give no tie rule; ties go to the lower position.
  *   scores [B, T, L] fp32; candidates of row (b,t) are positions
  *          0..min(q_pos[b,t], L-1); NaN ranks below every number
  *   q_pos  [B, T] int32
@@ -173,7 +181,12 @@ dsa_status dsa_topk(int B, int T, int L, int K, const float* scores,
 
 /*
  * Sparse absorbed-MLA attention over selected latent rows of a contiguous
- * KV cache (step 3).
+ * KV cache (step 3): Sparse Flash Attention reads only the cache entries at
+ * the selected indices (page "Inference Optimization for New Open-Source LLM
+ * Architectures", "Architectural Overview"; page "Day-0 Inference
+ * Optimization for a New Sparse Attention Architecture: A Technical Deep
+ * Dive", section 1, Sparse Flash Attention), with MLA absorbed: keys are
+ * the 576-wide latent rows, values their first 512 features.
  *   q        [B, T, H, 576] bf16    absorbed queries (512 latent + 64 rope)
  *   kv       [B, L, 576]            bf16, or e4m3 codes (MX32 / T128)
  *   kv_scale [B, L, 18] e8m0 (MX32), [B, L, 5] fp32 (T128); NULL for bf16
@@ -183,6 +196,11 @@ dsa_status dsa_topk(int B, int T, int L, int K, const float* scores,
  *   lse      [B, T, H] fp32         natural-log sum of exp(scale * q.k);
  *                                   a row with no valid index gets out = 0,
  *                                   lse = -inf
+ * Logits may span any range that fp32 holds: a head whose logits rise more
+ * than 128 (in log2 units) above its first tile's max takes a second pass
+ * with its true max as the softmax reference, and split partial sums are
+ * merged by their log-sum-exp.  Inputs whose scaled logits overflow fp32
+ * are outside the support set.
  *   workspace: dsa_workspace_size(DSA_OP_SPARSE_MLA, ...) bytes
  */
 dsa_status dsa_sparse_mla_attn(int B, int T, int L, int H, int K,
@@ -194,7 +212,11 @@ dsa_status dsa_sparse_mla_attn(int B, int T, int L, int H, int K,
 
 /*
  * The whole path for T query tokens per sequence over a paged cache:
- * indexer -> Top-K -> sparse attention, enqueued on one stream.
+ * indexer -> Top-K -> sparse attention, enqueued on one stream (page
+ * "Optimizing Inference for New Model Architectures", section 3: the index
+ * stage reads the paged key cache, the sparse attention kernel then reads
+ * the KV cache by index; page "Inference Adaptation and Performance
+ * Optimization for New Large Language Model Architectures", section 3.1).
  *   cache         see dsa_paged_cache; seq_lens[b] <= max_seq_len
  *   max_seq_len   host upper bound of seq_lens (sizes the score workspace)
  *   q_idx [B, T, H_I, d_I] bf16; q_mode as for dsa_indexer_scores

@@ -292,6 +292,34 @@ class PagedCache:
                             _ptr(self.page_table), _ptr(self.seq_lens))
 
 
+def _decode_args(cache, q_idx, w, q, k, q_pos, out, lse, idx_out):
+    """Shape checks and output allocation shared by the decode entry points."""
+    B, T, H_I, d_I = q_idx.shape
+    H = q.shape[2]
+    _need(q_idx, "q_idx", torch.bfloat16)
+    _need(w, "w", torch.float32, (B, T, H_I))
+    _need(q, "q", torch.bfloat16, (B, T, H, LATENT))
+    if q_pos is not None:
+        _need(q_pos, "q_pos", torch.int32, (B, T))
+    c = cache.as_c()
+    if cache.kidx.shape[2] != d_I:
+        raise ValueError(f"kidx rows are {cache.kidx.shape[2]} wide, the "
+                         f"indexer queries {d_I}")
+    if cache.page_table.shape[0] != B:
+        raise ValueError(f"page_table has {cache.page_table.shape[0]} rows, "
+                         f"the batch {B}")
+    dev = q.device
+    if out is None:
+        out = torch.empty((B, T, H, VALUE), dtype=torch.float32, device=dev)
+    if lse is None:
+        lse = torch.empty((B, T, H), dtype=torch.float32, device=dev)
+    _need(out, "out", torch.float32, (B, T, H, VALUE))
+    _need(lse, "lse", torch.float32, (B, T, H))
+    if idx_out is not None:
+        _need(idx_out, "idx_out", torch.int32, (B, T, k))
+    return (B, T, H_I, d_I, H), c, out, lse
+
+
 def decode_step(cache: PagedCache, q_idx: torch.Tensor, w: torch.Tensor,
                 q: torch.Tensor, k: int, softmax_scale: float,
                 max_seq_len: int, q_pos: Optional[torch.Tensor] = None,
@@ -304,27 +332,12 @@ def decode_step(cache: PagedCache, q_idx: torch.Tensor, w: torch.Tensor,
     w [B, T, H_I] fp32, q [B, T, H, 576] bf16 over a paged cache.  q_pos
     [B, T] int32, or None for T == 1 (the last cached token).
     quantize_queries as for indexer_scores.  Returns (out, lse, idx_out)."""
-    B, T, H_I, d_I = q_idx.shape
-    H = q.shape[2]
-    _need(q_idx, "q_idx", torch.bfloat16)
-    _need(w, "w", torch.float32, (B, T, H_I))
-    _need(q, "q", torch.bfloat16, (B, T, H, LATENT))
-    if q_pos is not None:
-        _need(q_pos, "q_pos", torch.int32, (B, T))
-    c = cache.as_c()
-    dev = q.device
-    if out is None:
-        out = torch.empty((B, T, H, VALUE), dtype=torch.float32, device=dev)
-    if lse is None:
-        lse = torch.empty((B, T, H), dtype=torch.float32, device=dev)
-    _need(out, "out", torch.float32, (B, T, H, VALUE))
-    _need(lse, "lse", torch.float32, (B, T, H))
-    if idx_out is not None:
-        _need(idx_out, "idx_out", torch.int32, (B, T, k))
+    (B, T, H_I, d_I, H), c, out, lse = _decode_args(
+        cache, q_idx, w, q, k, q_pos, out, lse, idx_out)
     ws_bytes = workspace_size(OP_DECODE_STEP, B, T, max_seq_len, H, k)
     if workspace is None:
         workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8,
-                                device=dev)
+                                device=q.device)
     _check(_lib.dsa_decode_step(
         B, T, H_I, d_I, H, k, float(softmax_scale), ctypes.byref(c),
         int(max_seq_len), _ptr(q_idx),

@@ -37,13 +37,13 @@ bool valid_kv_dtype(int d) { return valid_key_dtype(d) || d == DSA_E4M3_T128; }
 
 dsa::CacheView kv_view(const void* data, const void* scale, int dtype,
                        const int32_t* page_table, int max_pages, int L,
-                       uint64_t rows) {
+                       uint64_t rows, int num_pages) {
   const bool fp8 = dtype != DSA_BF16;
   return dsa::CacheView{static_cast<const uint8_t*>(data),
                         static_cast<const uint8_t*>(scale), page_table,
                         max_pages, L, fp8,
                         rows * DSA_LATENT_DIM * (fp8 ? 1 : 2),
-                        dtype == DSA_E4M3_T128};
+                        dtype == DSA_E4M3_T128, num_pages};
 }
 
 // Grid limits: B*T query tokens index a grid dimension capped at 65535.
@@ -200,7 +200,7 @@ dsa_status dsa_sparse_mla_attn(int B, int T, int L, int H, int K,
   dsa::AttnLaunch a{};
   a.B = B; a.T = T; a.H = H; a.K = K;
   a.q = static_cast<const uint16_t*>(q);
-  a.kv = kv_view(kv, kv_scale, kv_dtype, nullptr, 0, L, (uint64_t)B * L);
+  a.kv = kv_view(kv, kv_scale, kv_dtype, nullptr, 0, L, (uint64_t)B * L, 0);
   a.idx = idx;
   a.seq_lens = nullptr;
   a.scale = softmax_scale;
@@ -212,7 +212,11 @@ dsa_status dsa_sparse_mla_attn(int B, int T, int L, int H, int K,
                     "dsa_sparse_mla_attn");
 }
 
-dsa_status dsa_decode_step(int B, int T, int H_I, int d_I, int H, int K,
+}  // extern "C"
+
+namespace {
+
+dsa_status decode_step_impl(int B, int T, int H_I, int d_I, int H, int K,
                            float softmax_scale, const dsa_paged_cache* cache,
                            int max_seq_len, const void* q_idx, int q_mode,
                            const float* w,
@@ -278,7 +282,7 @@ dsa_status dsa_decode_step(int B, int T, int H_I, int d_I, int H, int K,
                            cache->kidx_scale, cache->page_table,
                            cache->max_pages_per_seq, 0, kfp8,
                            (uint64_t)cache->num_pages * DSA_PAGE_SIZE * d_I *
-                               (kfp8 ? 1 : 2), false};
+                               (kfp8 ? 1 : 2), false, cache->num_pages};
   ia.qp = qp;
   ia.scores = scores;
   ia.row_len = max_seq_len;
@@ -308,7 +312,7 @@ dsa_status dsa_decode_step(int B, int T, int H_I, int d_I, int H, int K,
   aa.q = static_cast<const uint16_t*>(q);
   aa.kv = kv_view(cache->kv, cache->kv_scale, cache->kv_dtype,
                   cache->page_table, cache->max_pages_per_seq, 0,
-                  (uint64_t)cache->num_pages * DSA_PAGE_SIZE);
+                  (uint64_t)cache->num_pages * DSA_PAGE_SIZE, cache->num_pages);
   aa.idx = idx;
   aa.seq_lens = cache->seq_lens;
   aa.scale = softmax_scale;
@@ -318,6 +322,22 @@ dsa_status dsa_decode_step(int B, int T, int H_I, int d_I, int H, int K,
   aa.splits = dsa::attn_splits((int)tokens, K);
   return hip_status(dsa::launch_sparse_mla(aa, st),
                     "dsa_decode_step: sparse attention");
+}
+
+}  // namespace
+
+extern "C" {
+
+dsa_status dsa_decode_step(int B, int T, int H_I, int d_I, int H, int K,
+                           float softmax_scale, const dsa_paged_cache* cache,
+                           int max_seq_len, const void* q_idx, int q_mode,
+                           const float* w,
+                           const void* q, const int32_t* q_pos, float* out,
+                           float* lse, int32_t* idx_out, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  return decode_step_impl(B, T, H_I, d_I, H, K, softmax_scale, cache,
+                          max_seq_len, q_idx, q_mode, w, q, q_pos, out, lse,
+                          idx_out, workspace, workspace_bytes, stream);
 }
 
 dsa_status dsa_cache_append(int B, int T, int d_I, int num_pages,

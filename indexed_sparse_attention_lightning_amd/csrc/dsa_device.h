@@ -149,11 +149,14 @@ __device__ __forceinline__ uint2 ld8(const void* p) {
 
 // Physical row index of logical position s of sequence b.
 // page_table == nullptr: contiguous [B, L, ...] storage (row = b*L + s).
+// A page entry outside [0, num_pages) is clamped into it (num_pages > 0):
+// a bad table then reads wrong rows, never memory outside the pool.
 __device__ __forceinline__ int64_t cache_row(const int32_t* page_table,
-                                             int max_pages, int L, int b,
-                                             int s) {
+                                             int max_pages, int num_pages,
+                                             int L, int b, int s) {
   if (page_table == nullptr) return (int64_t)b * L + s;
-  const int pg = page_table[(int64_t)b * max_pages + (s >> 6)];
+  int pg = page_table[(int64_t)b * max_pages + (s >> 6)];
+  if (num_pages > 0) pg = min(max(pg, 0), num_pages - 1);
   return (int64_t)pg * kPage + (s & (kPage - 1));
 }
 

@@ -26,6 +26,8 @@ struct CacheView {
   bool fp8;                   // e4m3 codes + scales, else bf16
   uint64_t bytes;             // size of `data` in bytes
   bool t128;                  // fp8 with fp32 scales per 128-feature tile
+  int num_pages;              // pages in the pool (paged); page entries are
+                              // clamped to [0, num_pages)
 };
 
 // Query positions: q_pos[b*T + t] if given, else seq_lens[b] - 1; with

@@ -95,7 +95,7 @@ __device__ __forceinline__ void stage_load_f8(StageF8<DI>& st,
   int64_t row0;
   bool clamp = false;
   if (kc.page_table != nullptr) {
-    row0 = cache_row(kc.page_table, kc.max_pages, kc.L, b, kbase);
+    row0 = cache_row(kc.page_table, kc.max_pages, kc.num_pages, kc.L, b, kbase);
   } else {
     row0 = (int64_t)b * kc.L + kbase;
     clamp = kbase + kSub > kc.L;
@@ -202,7 +202,7 @@ __device__ __forceinline__ void stage_load(Stage<DI, FP8>& st,
   int64_t row0;
   bool clamp = false;
   if (kc.page_table != nullptr) {
-    row0 = cache_row(kc.page_table, kc.max_pages, kc.L, b, kbase);
+    row0 = cache_row(kc.page_table, kc.max_pages, kc.num_pages, kc.L, b, kbase);
   } else {
     row0 = (int64_t)b * kc.L + kbase;
     clamp = kbase + kSub > kc.L;
@@ -486,7 +486,7 @@ __device__ __forceinline__ void keys_load_q8(KeysQ8<DI>& st,
   int64_t row;
   if (kc.page_table != nullptr) {
     // the 32 keys of a stage share one page (stages are 32-aligned, pages 64)
-    row = cache_row(kc.page_table, kc.max_pages, kc.L, b, kbase) + n;
+    row = cache_row(kc.page_table, kc.max_pages, kc.num_pages, kc.L, b, kbase) + n;
   } else {
     row = (int64_t)b * kc.L + min(kbase + n, kc.L - 1);
   }
@@ -735,7 +735,7 @@ __device__ __forceinline__ void tile_load(TileStage<DI, FP8>& st,
   int64_t row0;
   bool clamp = false;
   if (kc.page_table != nullptr) {
-    row0 = cache_row(kc.page_table, kc.max_pages, kc.L, b, kbase);
+    row0 = cache_row(kc.page_table, kc.max_pages, kc.num_pages, kc.L, b, kbase);
   } else {
     row0 = (int64_t)b * kc.L + kbase;
     clamp = kbase + kStageKeys > kc.L;
@@ -870,7 +870,7 @@ __device__ __forceinline__ void tile_load_q8(TileStageQ8<DI>& st,
   int64_t row0;
   bool clamp = false;
   if (kc.page_table != nullptr) {
-    row0 = cache_row(kc.page_table, kc.max_pages, kc.L, b, kbase);
+    row0 = cache_row(kc.page_table, kc.max_pages, kc.num_pages, kc.L, b, kbase);
   } else {
     row0 = (int64_t)b * kc.L + kbase;
     clamp = kbase + kStageKeys > kc.L;

@@ -18,14 +18,16 @@
 //     features = K), Q held as B operands: 27 of its 36 k-steps in
 //     registers, the last 9 in LDS (registers are the scarce resource: O
 //     takes all 256 accumulation registers);
-//   * softmax in the log2 domain against a per-head reference fixed at the
-//     first valid tile (its max + 64), so O is never rescaled;
+//   * softmax in the log2 domain against a per-head reference fixed for the
+//     pass (the first valid tile's max + 64), so O is never rescaled; a
+//     head whose later logits exceed it by more than 64 sends the workgroup
+//     through a second pass with the true max as the reference (rare);
 //   * O^T += V^T . P^T: P comes straight from the S^T accumulators (its
 //     accumulator layout already is a valid B operand after a k-slot
 //     permutation), V^T is read with the transposing LDS read
 //     (ds_read_b64_tr_b16) using the same row permutation;
 //   * O (128 x 512 fp32 per token) lives in the accumulation registers.
-// Splits write (m, l, O) partials that a combine kernel merges by LSE.
+// Splits write (O/l, log2-sum-exp) partials that a combine kernel merges.
 #include "dsa_device.h"
 #include "dsa_launch.h"
 
@@ -45,8 +47,9 @@ constexpr int kQLdsSteps = kLatent / 16 - kQRegSteps;   // 9 in LDS
 constexpr int kQLdsStride = 2 * kQLdsSteps + 1; // uint4 per head (padded)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
-constexpr float kRef = 64.0f;     // log2 headroom of the fixed softmax reference
-constexpr float kRange = 96.0f;   // largest logit excess (log2) handled exactly
+constexpr float kRef = 64.0f;     // log2 headroom of the first-pass reference
+constexpr float kRange = 64.0f;   // largest logit excess (log2) over the
+                                  // reference that the first pass accepts
 
 // A tile is 36 blocks of 64 slots (1 KB), block (g, rg) holding chunks
 // 8g..8g+7 of rows 8rg..8rg+7: chunk c of row R sits at slot
@@ -61,16 +64,22 @@ __device__ __forceinline__ int kv_slot(int R, int c) {
   return ((c >> 3) * 4 + (R >> 3)) * 64 + (R & 7) * 8 + ((c & 7) ^ kv_swz(R));
 }
 
-__device__ __forceinline__ void wait_vm(int n) {
-  // s_waitcnt vmcnt(n) for the few counts this kernel needs
-  switch (n) {
-    case 0: __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8)); break;
-    case 9: __builtin_amdgcn_s_waitcnt(9 | (7 << 4) | (15 << 8)); break;
-    case 10: __builtin_amdgcn_s_waitcnt(10 | (7 << 4) | (15 << 8)); break;
-    case 18: __builtin_amdgcn_s_waitcnt(2 | (1 << 14) | (7 << 4) | (15 << 8)); break;
-    case 20: __builtin_amdgcn_s_waitcnt(4 | (1 << 14) | (7 << 4) | (15 << 8)); break;
-    default: __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8)); break;
-  }
+// Direct-to-LDS loads per tile: one builtin call = one instruction.  Tile
+// j's loads are known to have landed (for every wave, after the barrier that
+// follows) once each wave waits for vmcnt <= kDma(FP8): the loads of tile j+1,
+// issued later, are exactly that many instructions, so with in-order
+// completion none of tile j's can still be among the outstanding ones.  Any
+// other vector-memory instruction (the FP8 scale loads, or anything the
+// compiler adds) can only make the wait longer, never shorter; issuing the
+// scale loads of a tile before its direct-to-LDS loads keeps it tight.
+constexpr int kDmaBf16 = kSlotsRow / 8;         // 9 blocks of 64 x 16 B
+constexpr int kDmaFp8 = kCodeSegs / 4;          // 5 code blocks per wave
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt field");
+  // s_waitcnt vmcnt(N): low bits [3:0], high bits [15:14]; expcnt and
+  // lgkmcnt at their maxima (not waited for)
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 // Workgroup barrier without the memory fence __syncthreads() implies (that
 // fence would wait for every in-flight direct-to-LDS load).  `lds` also
@@ -111,7 +120,7 @@ __device__ __forceinline__ void dma16(const uint8_t* base,
 template <int G>
 __device__ __forceinline__ void block_loads(__amdgpu_buffer_rsrc_t rsrc,
                                             uint32_t voff, uint4* dst) {
-  if constexpr (G < kSlotsRow / 8) {
+  if constexpr (G < kDmaBf16) {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
         rsrc, (__attribute__((address_space(3))) void*)(dst + G * 4 * kWave),
         16, voff + G * 128, 0, 0, 0);
@@ -179,7 +188,7 @@ __device__ __forceinline__ void issue_bf16(const AttnLaunch& p, const Split& s,
   } else {
     const uint8_t* src = p.kv.data + (uint64_t)(uint32_t)ent * (kLatent * 2) + cpart;
 #pragma unroll
-    for (int g = 0; g < kSlotsRow / 8; ++g)
+    for (int g = 0; g < kDmaBf16; ++g)
       __builtin_amdgcn_global_load_lds(src + g * 128,
                                        dst + (g * 4 + wave) * kWave, 16, 0, 0);
   }
@@ -196,28 +205,17 @@ __device__ __forceinline__ int code_slot(int R, int c) {
   return ((c >> 2) * 2 + (R >> 4)) * 64 + (R & 15) * 4 + ((c & 3) ^ ((R >> 2) & 3));
 }
 
-// FP8: code blocks by DMA; the scales of this lane's conversion slots (row
-// lane%32: MX blocks 4k + wave as e8m0 codes, or 128-feature tile k as fp32
-// bits) into registers.
+// FP8: the scales of this lane's conversion slots (row lane%32: MX blocks
+// 4k + wave as e8m0 codes, or 128-feature tile k as fp32 bits) into
+// registers, then the code blocks by DMA -- in that order (the compiler
+// barrier keeps it), so that the last kDmaFp8 vector-memory instructions of
+// a tile's loads are its code blocks (see wait_vm).
 template <bool BUF, bool T128>
 __device__ __forceinline__ void issue_fp8(const AttnLaunch& p, const Split& s,
                                           __amdgpu_buffer_rsrc_t rsrc, int j,
                                           uint4* dst, uint32_t (&sc)[5],
                                           int wave) {
   const int lane = lane_id();
-  {
-    const int R = 16 * (wave & 1) + (lane >> 2);
-    int ent = s.rows[j * kRowsT + R];
-    ent ^= ent >> 31;   // ~row for masked entries
-    const uint64_t off = (uint64_t)(uint32_t)ent * kLatent +
-                         ((lane & 3) ^ ((R >> 2) & 3)) * 16;
-#pragma unroll
-    for (int k = 0; k < 5; ++k) {
-      const int b = wave + 4 * k;                    // 18, 19: dummies
-      const int cb = (b < 18 ? b : b - 2) >> 1;
-      dma16<BUF>(p.kv.data, rsrc, off + cb * 64, dst + b * kWave);
-    }
-  }
   {
     int ent = s.rows[j * kRowsT + (lane & 31)];
     ent ^= ent >> 31;
@@ -233,6 +231,21 @@ __device__ __forceinline__ void issue_fp8(const AttnLaunch& p, const Split& s,
         const int blk = 4 * k + wave;
         sc[k] = srow[blk < kLatent / 32 ? blk : blk - 4];
       }
+    }
+  }
+  asm volatile("" ::: "memory");
+  {
+    const int R = 16 * (wave & 1) + (lane >> 2);
+    int ent = s.rows[j * kRowsT + R];
+    ent ^= ent >> 31;   // ~row for masked entries
+    const uint64_t off = (uint64_t)(uint32_t)ent * kLatent +
+                         ((lane & 3) ^ ((R >> 2) & 3)) * 16;
+    static_assert(kDmaFp8 * 4 == kCodeSegs, "every wave issues kDmaFp8 blocks");
+#pragma unroll
+    for (int k = 0; k < kDmaFp8; ++k) {
+      const int b = wave + 4 * k;                    // 18, 19: dummies
+      const int cb = (b < 18 ? b : b - 2) >> 1;
+      dma16<BUF>(p.kv.data, rsrc, off + cb * 64, dst + b * kWave);
     }
   }
 }
@@ -286,7 +299,9 @@ struct HeadState {
   uint4 qb[kQRegSteps];     // B operands: this lane's head, 8 features/k-step
   f32x16 o[kValue / 32];    // O^T accumulators, 16 dv tiles of 32
   float m, l;               // softmax reference (log2 units) and partial sum
-  bool bad;                 // a logit exceeded the representable range
+  float* mx;                // LDS: largest logit of each of the wave's 32
+                            // heads (log2 units)
+  int* redo;                // LDS: set when a logit exceeds m by > kRange
 };
 
 __device__ __forceinline__ s16x4 lds_tr16(const char* p) {
@@ -413,6 +428,7 @@ __device__ __forceinline__ void compute_tile(const uint4* tile,
       }
       // one block of the next tile's loads every fourth k-step (k-steps 2,
       // 6, ..., 34), so the address unit drains while the matrix core works
+      static_assert(kS / 4 == kDmaBf16, "one block per four k-steps");
       if ((ks & 3) == 2) loads.block(ks >> 2);
       const uint4 a = aq[ks % (kAhead + 1)], b = bq[ks % (kAhead + 1)];
       f32x16& c = (ks & 1) ? acc1 : acc;
@@ -470,15 +486,20 @@ __device__ __forceinline__ void compute_tile(const uint4* tile,
 #pragma unroll
   for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, acc[r]);
   tmax = fmaxf(tmax, swap_halves(tmax));
-  // The reference max is fixed once per head, at the first tile with a valid
-  // row, 2^64 above that tile's max: later rows stay representable (p <= 2^32
-  // for logits up to 96 above it) and O never needs rescaling.  A logit
-  // beyond that range marks the head as out of range (its LSE becomes NaN).
+  // Per-head reference m (log2 units), fixed for the whole pass so that O
+  // never needs rescaling (a rescale of the 256 accumulation registers
+  // would cost the loop its register allocation): in the first pass, the
+  // first valid tile's max + kRef, so later rows up to kRef + kRange above
+  // that max stay representable (p <= 2^kRange); `mx` tracks the true max.
+  // A head whose logits go past that range is flagged, and the workgroup
+  // runs its rows a second time with m = the true max (p <= 1) -- a rare
+  // path: N(0,1) inputs stay within a few units of the first tile's max.
+  // (Both kept in LDS: the loop has no registers to spare.)
+  __hip_atomic_fetch_max(st.mx + n, tmax, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_WORKGROUP);
   if (st.m == -__builtin_inff() && tmax != -__builtin_inff()) st.m = tmax + kRef;
-  if (tmax > st.m + kRange) st.bad = true;
-  // no reference yet (no valid row so far): subtracting +inf gives p = 0.
-  // The hardware exp2 flushes results below 2^-126, i.e. more than 2^-62
-  // below the largest p of the first valid tile.
+  if (tmax > st.m + kRange) *st.redo = 1;
+  // no reference yet (no valid row so far): subtracting +inf gives p = 0
   const float mref = st.m != -__builtin_inff() ? st.m : __builtin_inff();
   uint4 pb[2];
   float pr[16];
@@ -571,6 +592,8 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_kernel(
   __shared__ int rowcnt[kMaxSplitRows / kThreads][kThreads / kWave];
   __shared__ uint4 qlds[128 * kQLdsStride];
   __shared__ float tmul[T128 ? kTmulRows * 32 : 1];
+  __shared__ int redo;   // some head needs the second softmax pass
+  __shared__ float mxs[128];   // per head: largest logit (log2 units)
   static_assert(32 * kStageRow <= kBufSlots * 16 &&
                     32 * kStageRow <= (FP8 ? kTileSlots : 128 * kQLdsStride) * 16,
                 "epilogue staging regions");
@@ -611,7 +634,7 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_kernel(
   // bounds (their logits are masked)
   const int nvalid = p.seq_lens ? p.seq_lens[s.b] : p.kv.L;
   const int dummy = nvalid > 0 ? (int)cache_row(p.kv.page_table,
-                                                p.kv.max_pages, p.kv.L, s.b, 0)
+                                                p.kv.max_pages, p.kv.num_pages, p.kv.L, s.b, 0)
                                  : 0;
   // all index loads of a thread first, then the query loads (in flight
   // while the page-table lookups run), then the row table
@@ -629,7 +652,8 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_kernel(
   HeadState st;
   st.m = -__builtin_inff();
   st.l = 0.f;
-  st.bad = false;
+  st.mx = &mxs[wave * 32];
+  st.redo = &redo;
 #pragma unroll
   for (int t = 0; t < kValue / 32; ++t) st.o[t] = f32x16{};
   constexpr int kQL = 128 * 2 * kQLdsSteps / kThreads;   // 9 per thread
@@ -674,7 +698,7 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_kernel(
       }
       if (pos[u] >= 0)
         rows[off + __builtin_popcountll(bal[u] & below)] =
-            (int)cache_row(p.kv.page_table, p.kv.max_pages, p.kv.L, s.b, pos[u]);
+            (int)cache_row(p.kv.page_table, p.kv.max_pages, p.kv.num_pages, p.kv.L, s.b, pos[u]);
     }
     s.ntiles = max(1, (base + kRowsT - 1) / kRowsT);
     if (base + tid < s.ntiles * kRowsT) rows[base + tid] = ~dummy;
@@ -686,7 +710,7 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_kernel(
       (int)(BUF ? (uint32_t)p.kv.bytes : 0u), 0x00020000);
   // the first two tiles go out while the queries are still arriving
   uint32_t sc0[5], sc1[5], sc2[5];
-  constexpr int per_tile = FP8 ? 10 : 9;
+  constexpr int per_tile = FP8 ? kDmaFp8 : kDmaBf16;
   auto issue = [&](int j, uint4* dst, uint32_t (&sc)[5]) {
     if constexpr (FP8) issue_fp8<BUF, T128>(p, s, rsrc, j, dst, sc, wave);
     else issue_bf16<BUF>(p, s, rsrc, j, dst, wave);
@@ -705,6 +729,8 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_kernel(
 #pragma unroll
     for (int ks = 0; ks < kQRegSteps; ++ks) st.qb[ks] = make_uint4(0, 0, 0, 0);
   }
+  if (tid == 0) redo = 0;
+  if (tid < 128) mxs[tid] = -__builtin_inff();
   barrier(true);
   const uint4* qrow = qlds + (wave * 32 + n) * kQLdsStride + h;
   const float sl2 = p.scale * kLog2e;
@@ -723,7 +749,7 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_kernel(
     // exact per-buffer waits.
     auto step = [&](int j, uint4* cur, uint4* nxt, uint32_t (&scc)[5],
                     uint32_t (&scn)[5]) {
-      wait_vm(per_tile);
+      wait_vm<per_tile>();
       barrier(false);
       const int jn = min(j + 2, s.ntiles - 1);
       // bf16: a wave that computes this step spreads the loads of tile j+2
@@ -753,12 +779,25 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_kernel(
       }
     };
     const int nsteps = (s.ntiles + 2) / 3 * 3;
-    for (int j = 0; j < nsteps; j += 3) {
-      step(j, buf0, buf2, sc0, sc2);
-      step(j + 1, buf1, buf0, sc1, sc0);
-      step(j + 2, buf2, buf1, sc2, sc1);
+    for (int pass = 0;; ++pass) {
+      for (int j = 0; j < nsteps; j += 3) {
+        step(j, buf0, buf2, sc0, sc2);
+        step(j + 1, buf1, buf0, sc1, sc0);
+        step(j + 2, buf2, buf1, sc2, sc1);
+      }
+      wait_vm<0>();
+      if (pass == 1) break;
+      barrier(true);   // also: every wave is done with the tile buffers
+      if (redo == 0) break;
+      // second pass: every head of the workgroup restarts with its true
+      // max as the reference (all of a tile's loads are shared by the waves)
+#pragma unroll
+      for (int t = 0; t < kValue / 32; ++t) st.o[t] = f32x16{};
+      st.l = 0.f;
+      st.m = st.mx[n];
+      issue(0, buf0, sc0);
+      issue(min(1, s.ntiles - 1), buf1, sc1);
     }
-    wait_vm(0);
   }
   if (!active) return;   // wave-uniform; ended waves leave the barriers
 
@@ -777,9 +816,7 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_kernel(
                         st.o[t][4 * g + 2] * inv, st.o[t][4 * g + 3] * inv);
     if (h == 0)
       p.lse[(int64_t)s.token * p.H + head] =
-          st.bad ? __builtin_nanf("")
-                 : (ltot > 0.f ? (st.m + __builtin_log2f(ltot)) * kLn2
-                               : -__builtin_inff());
+          ltot > 0.f ? (st.m + __builtin_log2f(ltot)) * kLn2 : -__builtin_inff();
   } else {
     // partial of this split: O / l in bf16 (relative rounding 2^-9, well
     // inside the output tolerance) plus (m, l) in fp32
@@ -828,20 +865,24 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_kernel(
       float* ml = reinterpret_cast<float*>(
                       reinterpret_cast<uint16_t*>(p.partial) + nslots * kValue) +
                   2 * slot;
-      ml[0] = st.bad ? __builtin_nanf("") : (ltot > 0.f ? st.m : -__builtin_inff());
-      ml[1] = ltot;
+      // the split's log2-sum-exp: the combine weighs splits by it
+      ml[0] = ltot > 0.f ? st.m + __builtin_log2f(ltot) : -__builtin_inff();
+      ml[1] = 0.f;
     }
   }
 }
 
 // Merge split partials (written and read non-temporal: each is touched once
 // per step; 41.6-42.0 us against 42.9-43.0 us for the attention and the
-// merge together): out = sum_s w_s * (O_s / l_s) / sum_s w_s with
-// w_s = l_s * 2^(m_s - M), M the largest m_s; lse = ln(2^M * sum_s w_s).
-// One wave per (token, head), kCombHeads heads per workgroup; a lane merges
-// 8 consecutive values (16-byte loads).  Every load of a lane (all splits'
-// (m, l), then all splits' partial values) is issued before any is used, so
-// the splits' latencies overlap.
+// merge together).  Split s carries O_s / l_s and its log2-sum-exp
+// g_s = m_s + log2(l_s); with G the largest g_s, out = sum_s w_s * (O_s / l_s)
+// / sum_s w_s, w_s = 2^(g_s - G) in (0, 1], and lse = ln 2 * (G +
+// log2(sum_s w_s)).  The split with the largest sum weighs exactly 1, so no
+// split that matters can underflow, however far apart the splits' softmax
+// references are.  One wave per (token, head), kCombHeads heads per
+// workgroup; a lane merges 8 consecutive values (16-byte loads).  Every
+// load of a lane (all splits' g, then all splits' partial values) is issued
+// before any is used, so the splits' latencies overlap.
 constexpr int kMaxSplits = 16;
 constexpr int kCombHeads = 4;
 __global__ __launch_bounds__(64 * kCombHeads) void combine_kernel(AttnLaunch p,
@@ -854,33 +895,27 @@ __global__ __launch_bounds__(64 * kCombHeads) void combine_kernel(AttnLaunch p,
   const uint16_t* po = reinterpret_cast<const uint16_t*>(p.partial);
   const float* ml = reinterpret_cast<const float*>(po + nslots * kValue);
   const int64_t slot0 = (int64_t)token * splits * p.H + head;
-  float2 mls[kMaxSplits];
+  float g[kMaxSplits];
 #pragma unroll
   for (int sp = 0; sp < kMaxSplits; ++sp)
-    mls[sp] = sp < splits
-                  ? *reinterpret_cast<const float2*>(ml + 2 * (slot0 + (int64_t)sp * p.H))
-                  : make_float2(-__builtin_inff(), 0.f);
+    g[sp] = sp < splits ? ml[2 * (slot0 + (int64_t)sp * p.H)] : -__builtin_inff();
   uint4 v[kMaxSplits];
 #pragma unroll
   for (int sp = 0; sp < kMaxSplits; ++sp)
     v[sp] = sp < splits
                 ? ld16_stream(po + (slot0 + (int64_t)sp * p.H) * kValue + dv)
                 : make_uint4(0u, 0u, 0u, 0u);
-  float M = -__builtin_inff();
+  float G = -__builtin_inff();
 #pragma unroll
-  for (int sp = 0; sp < kMaxSplits; ++sp) {
-    const float m = mls[sp].x;
-    M = (m != m || M != M) ? __builtin_nanf("") : fmaxf(M, m);
-  }
+  for (int sp = 0; sp < kMaxSplits; ++sp)
+    G = (g[sp] != g[sp] || G != G) ? __builtin_nanf("") : fmaxf(G, g[sp]);
   float wsum = 0.f;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  if (M != -__builtin_inff() && M == M) {
+  if (G != -__builtin_inff() && G == G) {
 #pragma unroll
     for (int sp = 0; sp < kMaxSplits; ++sp) {
-      const float m = mls[sp].x, l = mls[sp].y;
-      // splits without rows (m = -inf) or beyond `splits` weigh nothing
-      const float f = (m == -__builtin_inff() || !(l > 0.f)) ? 0.f
-                                                             : l * exp2f(m - M);
+      // splits without rows (g = -inf) or beyond `splits` weigh nothing
+      const float f = g[sp] == -__builtin_inff() ? 0.f : exp2f(g[sp] - G);
       wsum += f;
       if (f > 0.f) {   // a skipped split's values are never read
         const uint32_t w[4] = {v[sp].x, v[sp].y, v[sp].z, v[sp].w};
@@ -898,8 +933,8 @@ __global__ __launch_bounds__(64 * kCombHeads) void combine_kernel(AttnLaunch p,
   o[1] = make_float4(acc[4] * inv, acc[5] * inv, acc[6] * inv, acc[7] * inv);
   if ((threadIdx.x & 63) == 0)
     p.lse[(int64_t)token * p.H + head] =
-        M != M ? M
-               : (wsum > 0.f ? (M + __builtin_log2f(wsum)) * kLn2
+        G != G ? G
+               : (wsum > 0.f ? (G + __builtin_log2f(wsum)) * kLn2
                              : -__builtin_inff());
 }
 

@@ -16,6 +16,18 @@ OUT_REL_TOL = 1e-2    # max|out - oracle| <= 1e-2 * max|oracle out|
 LSE_ABS_TOL = 1e-3    # max|lse - oracle lse| <= 1e-3
 
 
+def prefill_rows(T=4096, seed=77, n_random=32):
+    """Sampled query rows of a prefill chunk: the first and the last eight
+    (every position of the query-tiled indexer's 8-query tile, at both ends),
+    the 16 around T/2 (for the 4096-query chunk at 61440..65535 these straddle
+    position 63488, a multiple of 2048), and n_random seeded others: 64 rows
+    for the full chunk."""
+    ts = set(range(8)) | set(range(T - 8, T)) | set(range(T // 2 - 8, T // 2 + 8))
+    rng = np.random.default_rng(seed)
+    others = [t for t in rng.permutation(T) if t not in ts][:n_random]
+    return [(0, int(t)) for t in sorted(ts | set(others))]
+
+
 def paged_cache(d) -> dsa.PagedCache:
     return dsa.PagedCache(kidx=d["kidx"], kv=d["kv"], page_table=d["page_table"],
                           seq_lens=d["seq_lens"], kidx_scale=d["kidx_scale"],

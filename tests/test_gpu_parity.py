@@ -14,7 +14,7 @@ import workloads as wk
 from workloads.device import to_device
 
 from gpu_helpers import (assert_attn_close, assert_idx_equal, check_workload,
-                         run_decode_step, run_separate_ops)
+                         prefill_rows, run_decode_step, run_separate_ops)
 
 pytestmark = pytest.mark.gpu
 
@@ -149,8 +149,11 @@ def test_full_decode_fp8():
 
 
 def test_full_prefill_sampled_rows():
-    """4096 queries at 61440..65535 of a 65536 context; rows sampled."""
-    rows = [(0, t) for t in (0, 1, 777, 2048, 3001, 4094, 4095)]
+    """4096 queries at 61440..65535 of a 65536 context; 64 rows sampled:
+    every position of the 8-query tile at both ends of the chunk, the rows
+    around a multiple of 2048, and seeded others."""
+    rows = prefill_rows()
+    assert len(rows) == 64
     check_workload(W["prefill"], rows=rows, separate=True)
 
 
@@ -239,3 +242,69 @@ def test_indexer_long_wave_ranges():
         want[:qp + 1] = oracle.indexer_scores_row(q_i[b, 0], w[b, 0],
                                                   k_i[b, :qp + 1])
         assert np.array_equal(sc[b, 0].astype(np.float64), want), b
+
+
+# ------------------------------------------- softmax over a wide logit range
+
+def _wide_range_inputs(B, T, H, K, seed):
+    """Queries and latent rows whose logits (log2 units) spread over several
+    hundred units across the selected rows, rising within every run of 128
+    rows (the first 32-row tile of each run lowest, so a reference taken from
+    a run's first tile is far below its later maxima) and with a permuted
+    offset per run (runs end far apart in their sums).  q[h] is a_h times a
+    vector of ones (a_h in 1..1.875, exact in bf16), row s is b_s times ones
+    plus N(0, 0.5) noise, b_s = off[run] + 3 * (s mod 128) / 127 - 2."""
+    rng = np.random.default_rng(seed)
+    L = K
+    a = 1.0 + (np.arange(H) % 8) / 8.0
+    q = np.broadcast_to(a[None, None, :, None], (B, T, H, 576)).astype(np.float32)
+    runs = (L + 127) // 128
+    off = rng.permutation(np.linspace(-1.5, 1.5, runs))
+    s = np.arange(L)
+    b = off[s // 128] + 3.0 * (s % 128) / 127.0 - 2.0
+    kv = (b[None, :, None] + 0.5 * rng.standard_normal((B, L, 576))).astype(np.float32)
+    idx = np.broadcast_to(np.arange(K, dtype=np.int32), (B, T, K)).copy()
+    return wk.f32_to_bf16_bits(q), kv, idx
+
+
+@pytest.mark.parametrize("B,T,H,K,fmt", [
+    (2, 1, 128, 2048, "bf16"),     # 16 splits per token, combined by LSE
+    (2, 1, 128, 2048, "mx32"),
+    (1, 256, 64, 128, "bf16"),     # one split per token: no combine
+])
+def test_wide_logit_range(B, T, H, K, fmt):
+    """Logits spread far beyond the first tile's max (well past the range a
+    reference fixed at the first tile covers, so the second softmax pass
+    runs) and across the splits of a token (whose partial sums then differ
+    by far more than the fp32 exponent range): out and LSE against the
+    oracle's fp64 softmax, element by element, and nothing NaN."""
+    scale = 1.0 / np.sqrt(192.0)
+    q_bits, kv_f, idx = _wide_range_inputs(B, T, H, K, seed=31 + T)
+    q = torch.from_numpy(q_bits.view(np.int16)).view(torch.bfloat16).cuda()
+    if fmt == "bf16":
+        kv_bits = wk.f32_to_bf16_bits(kv_f)
+        kv_ref = oracle.decode_bf16(kv_bits)
+        kv = torch.from_numpy(kv_bits.view(np.int16)).view(torch.bfloat16).cuda()
+        kv_scale = None
+    else:
+        codes, sc = wk.mx32_quantize(kv_f)
+        kv_ref = oracle.dequant_mx32(codes, sc)
+        kv = torch.from_numpy(codes).cuda()
+        kv_scale = torch.from_numpy(sc).cuda()
+    out, lse = dsa.sparse_mla_attn(q, kv, torch.from_numpy(idx).cuda(), scale,
+                                   kv_scale=kv_scale)
+    torch.cuda.synchronize()
+    out, lse = out.cpu().numpy(), lse.cpu().numpy()
+    qf = oracle.decode_bf16(q_bits)
+    ref_o = np.empty((B, T, H, 512))
+    ref_l = np.empty((B, T, H))
+    for bb in range(B):
+        for t in range(T):
+            ref_o[bb, t], ref_l[bb, t] = oracle.sparse_mla_row(
+                qf[bb, t], kv_ref[bb, idx[bb, t]], scale)
+    z = (qf[0, 0] @ kv_ref[0].T) * scale / np.log(2.0)
+    assert z.max() - z.min() > 200.0   # the spread this test is about
+    assert np.all(np.isfinite(out)) and np.all(np.isfinite(lse))
+    err = np.abs(out - ref_o).max()
+    assert err <= 1e-2 * np.abs(ref_o).max(), err
+    assert np.abs(lse - ref_l).max() <= 1e-3

@@ -13,7 +13,7 @@ import pytest
 import oracle
 import workloads as wk
 
-from gpu_helpers import check_workload
+from gpu_helpers import check_workload, prefill_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -49,12 +49,11 @@ def test_quantised_indexer_matches_oracle(name):
 
 
 def test_quantised_indexer_full_decode_fp8():
-    """The FP8 decode batch at full size (32 x 32768), sampled rows."""
+    """The FP8 decode batch at full size (32 x 32768), every row."""
     wl = W["decode_fp8"]
     q = wk.eighths(1001, (wl.B, wl.T, wl.H_I, wl.d_I))
     print("q8 full decode_fp8", flush=True)
-    check_workload(wl, rows=[(0, 0), (13, 0), (31, 0)], q_idx=q,
-                   quantize_queries=True)
+    check_workload(wl, q_idx=q, quantize_queries=True)
 
 
 def test_quantised_indexer_full_prefill_chunk():
@@ -63,6 +62,4 @@ def test_quantised_indexer_full_prefill_chunk():
     wl = wk.scaled(W["prefill"], quantized=True)
     q = wk.eighths(1002, (wl.B, wl.T, wl.H_I, wl.d_I))
     print("q8 full prefill chunk", flush=True)
-    check_workload(wl, rows=[(0, 0), (0, 1), (0, 7), (0, 8), (0, 2047),
-                             (0, 4090), (0, 4095)], q_idx=q,
-                   quantize_queries=True)
+    check_workload(wl, rows=prefill_rows(), q_idx=q, quantize_queries=True)
