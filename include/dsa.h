@@ -22,7 +22,8 @@
  * - Tensor pointers are DEVICE pointers, 16-byte aligned, row-major and
  *   densely packed in the layouts stated per argument.  Scalars are host
  *   values.  The caller owns every buffer; the library never allocates,
- *   frees or synchronises.
+ *   frees or synchronises (dsa_decode_step_static works in the library's
+ *   own static device scratch instead of a caller workspace).
  * - bf16 tensors hold IEEE bfloat16 bit patterns (uint16).  FP8 tensors hold
  *   OCP e4m3fn codes (uint8) with one OCP e8m0 scale code per 32 consecutive
  *   features of a row (the "MX block-32" layout: page "Optimizing Inference
@@ -101,6 +102,8 @@ typedef enum dsa_op {
 #define DSA_PAGE_SIZE 64
 #define DSA_MAX_TOPK 2048
 #define DSA_MAX_CONTEXT 131072   /* longest score row / sequence */
+/* Bytes of device scratch that dsa_decode_step_static owns on each GPU. */
+#define DSA_STATIC_SCRATCH_BYTES (64ull << 20)
 
 /*
  * One layer's paged cache: indexer keys and latent KV in two page pools that
@@ -234,6 +237,27 @@ dsa_status dsa_decode_step(int B, int T, int H_I, int d_I, int H, int K,
                            const void* q, const int32_t* q_pos, float* out,
                            float* lse, int32_t* idx_out, void* workspace,
                            size_t workspace_bytes, void* stream);
+
+/*
+ * dsa_decode_step without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation): the workspace is the library's
+ * own static device scratch of DSA_STATIC_SCRATCH_BYTES per GPU, held from
+ * the first call on a device until the process ends.  Arguments and results
+ * as for dsa_decode_step.  Sizes whose workspace
+ * (dsa_workspace_size(DSA_OP_DECODE_STEP, ...)) exceeds the scratch return
+ * DSA_ERR_WORKSPACE before any launch.  The call itself allocates nothing;
+ * its first call on a device looks up the scratch's address there.  All
+ * calls on one GPU share that scratch: calls that may overlap on one GPU
+ * (different streams, or different threads without ordering) race.
+ */
+dsa_status dsa_decode_step_static(int B, int T, int H_I, int d_I, int H, int K,
+                                  float softmax_scale,
+                                  const dsa_paged_cache* cache,
+                                  int max_seq_len, const void* q_idx,
+                                  int q_mode, const float* w, const void* q,
+                                  const int32_t* q_pos, float* out, float* lse,
+                                  int32_t* idx_out, void* stream);
 
 /*
  * Store new tokens' indexer keys and latent rows into the paged pools -- the

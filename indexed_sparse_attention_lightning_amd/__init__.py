@@ -13,6 +13,8 @@ Entry points (same names as the C ABI, without the ``dsa_`` prefix):
 * ``topk``            per-row Top-K (ties to the lower position), ascending
 * ``sparse_mla_attn`` absorbed-MLA attention over selected latent rows
 * ``decode_step``     indexer -> Top-K -> attention over a paged cache
+* ``decode_step_static``  the same in the library's static device scratch
+                      (no workspace: for callers that cannot allocate)
 * ``cache_append``    store new tokens' key / latent rows into the paged
                       pools, quantised to each pool's format
 """
@@ -29,7 +31,8 @@ import torch
 __all__ = [
     "DSA_BF16", "DSA_E4M3_MX32", "DSA_E4M3_T128", "DSA_Q_BF16", "DSA_Q_MX32",
     "DsaError", "PagedCache",
-    "cache_append", "decode_step", "indexer_scores", "library_path",
+    "cache_append", "decode_step", "decode_step_static", "indexer_scores",
+    "library_path", "STATIC_SCRATCH_BYTES",
     "sparse_mla_attn", "topk", "workspace_size",
 ]
 
@@ -40,6 +43,7 @@ T128_TILES = 5
 DSA_Q_BF16, DSA_Q_MX32 = 0, 1
 OP_INDEXER_SCORES, OP_TOPK, OP_SPARSE_MLA, OP_DECODE_STEP = 0, 1, 2, 3
 LATENT, VALUE, PAGE = 576, 512, 64
+STATIC_SCRATCH_BYTES = 64 << 20   # DSA_STATIC_SCRATCH_BYTES
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libdsa.so")
@@ -78,6 +82,9 @@ def _load():
         "dsa_sparse_mla_attn": [I, I, I, I, I, P, P, I, P, P, F, P, P, P, S, P],
         "dsa_decode_step": [I, I, I, I, I, I, F, ctypes.POINTER(_PagedCacheC),
                             I, P, I, P, P, P, P, P, P, P, S, P],
+        "dsa_decode_step_static": [I, I, I, I, I, I, F,
+                                   ctypes.POINTER(_PagedCacheC),
+                                   I, P, I, P, P, P, P, P, P, P],
         "dsa_cache_append": [I, I, I, I, I, P, P, P, I, P, P, P, I, P, P, P],
         "dsa_workspace_size": [I, I, I, I, I, I],
         "dsa_status_string": [I],
@@ -87,7 +94,8 @@ def _load():
         fn = getattr(lib, name)
         fn.argtypes = args
     for name in ("dsa_indexer_scores", "dsa_topk", "dsa_sparse_mla_attn",
-                 "dsa_decode_step", "dsa_cache_append"):
+                 "dsa_decode_step", "dsa_decode_step_static",
+                 "dsa_cache_append"):
         getattr(lib, name).restype = ctypes.c_int
     lib.dsa_workspace_size.restype = ctypes.c_size_t
     lib.dsa_status_string.restype = ctypes.c_char_p
@@ -345,6 +353,29 @@ def decode_step(cache: PagedCache, q_idx: torch.Tensor, w: torch.Tensor,
         _ptr(q_pos),
         _ptr(out), _ptr(lse), _ptr(idx_out), _ptr(workspace),
         workspace.numel(), _stream()), "dsa_decode_step")
+    return out, lse, idx_out
+
+
+def decode_step_static(cache: PagedCache, q_idx: torch.Tensor,
+                       w: torch.Tensor, q: torch.Tensor, k: int,
+                       softmax_scale: float, max_seq_len: int,
+                       q_pos: Optional[torch.Tensor] = None,
+                       out: Optional[torch.Tensor] = None,
+                       lse: Optional[torch.Tensor] = None,
+                       idx_out: Optional[torch.Tensor] = None,
+                       quantize_queries: bool = False):
+    """decode_step without a workspace: the library's static device scratch
+    (STATIC_SCRATCH_BYTES per GPU) holds the intermediates, and the library
+    call allocates nothing (pass out / lse to allocate nothing here either).
+    Calls that overlap on one GPU share that scratch and race."""
+    (B, T, H_I, d_I, H), c, out, lse = _decode_args(
+        cache, q_idx, w, q, k, q_pos, out, lse, idx_out)
+    _check(_lib.dsa_decode_step_static(
+        B, T, H_I, d_I, H, k, float(softmax_scale), ctypes.byref(c),
+        int(max_seq_len), _ptr(q_idx),
+        DSA_Q_MX32 if quantize_queries else DSA_Q_BF16, _ptr(w), _ptr(q),
+        _ptr(q_pos), _ptr(out), _ptr(lse), _ptr(idx_out), _stream()),
+        "dsa_decode_step_static")
     return out, lse, idx_out
 
 

@@ -8,6 +8,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "dsa_launch.h"
 
@@ -93,6 +94,38 @@ dsa_status check_q_mode(int q_mode, bool mx_keys) {
 dsa_status hip_status(hipError_t e, const char* what) {
   if (e == hipSuccess) return ok();
   return fail(DSA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// Scratch of dsa_decode_step_static: device memory of the library itself, one
+// copy per GPU, held until the process ends.  In host code `scratch` only
+// names the symbol; its device address (different on every GPU) comes from
+// hipGetSymbolAddress with that GPU current, looked up once per device and
+// kept in g_scratch.  Nothing in it needs to start at zero: every byte a
+// decode step reads from its workspace was written earlier in the same step.
+constexpr size_t kScratchBytes = DSA_STATIC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices] = {};
+
+dsa_status static_scratch_ptr(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "dsa_decode_step_static: hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(DSA_ERR_UNSUPPORTED, "device %d beyond the %d the library tracks",
+                dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return hip_status(e != hipSuccess ? e : hipErrorInvalidSymbol,
+                        "dsa_decode_step_static: hipGetSymbolAddress(scratch)");
+    g_scratch[dev] = p;
+  }
+  *out = g_scratch[dev];
+  return DSA_OK;
 }
 
 }  // namespace
@@ -222,7 +255,8 @@ dsa_status decode_step_impl(int B, int T, int H_I, int d_I, int H, int K,
                            const float* w,
                            const void* q, const int32_t* q_pos, float* out,
                            float* lse, int32_t* idx_out, void* workspace,
-                           size_t workspace_bytes, void* stream) {
+                           size_t workspace_bytes, void* stream,
+                           bool static_scratch) {
   if (!cache || !q_idx || !w || !q || !out || !lse)
     return fail(DSA_ERR_NULL, "dsa_decode_step: NULL pointer");
   if (!cache->kidx || !cache->kv || !cache->page_table || !cache->seq_lens)
@@ -253,6 +287,15 @@ dsa_status decode_step_impl(int B, int T, int H_I, int d_I, int H, int K,
   if (cache->kv_dtype != DSA_BF16 && !cache->kv_scale)
     return fail(DSA_ERR_NULL, "FP8 KV needs kv_scale");
   const size_t need = decode_ws(B, T, max_seq_len, H, K);
+  if (static_scratch) {
+    if (need > kScratchBytes)
+      return fail(DSA_ERR_WORKSPACE,
+                  "dsa_decode_step_static: these sizes need %zu bytes of "
+                  "scratch, the library's static scratch holds %zu",
+                  need, kScratchBytes);
+    if (dsa_status st = static_scratch_ptr(&workspace)) return st;
+    workspace_bytes = kScratchBytes;
+  }
   if (!workspace || workspace_bytes < need)
     return fail(DSA_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", need,
                 workspace ? workspace_bytes : (size_t)0);
@@ -337,7 +380,19 @@ dsa_status dsa_decode_step(int B, int T, int H_I, int d_I, int H, int K,
                            size_t workspace_bytes, void* stream) {
   return decode_step_impl(B, T, H_I, d_I, H, K, softmax_scale, cache,
                           max_seq_len, q_idx, q_mode, w, q, q_pos, out, lse,
-                          idx_out, workspace, workspace_bytes, stream);
+                          idx_out, workspace, workspace_bytes, stream, false);
+}
+
+dsa_status dsa_decode_step_static(int B, int T, int H_I, int d_I, int H, int K,
+                                  float softmax_scale,
+                                  const dsa_paged_cache* cache,
+                                  int max_seq_len, const void* q_idx,
+                                  int q_mode, const float* w, const void* q,
+                                  const int32_t* q_pos, float* out, float* lse,
+                                  int32_t* idx_out, void* stream) {
+  return decode_step_impl(B, T, H_I, d_I, H, K, softmax_scale, cache,
+                          max_seq_len, q_idx, q_mode, w, q, q_pos, out, lse,
+                          idx_out, nullptr, 0, stream, true);
 }
 
 dsa_status dsa_cache_append(int B, int T, int d_I, int num_pages,

@@ -169,3 +169,25 @@ def test_workspace_sizes():
     # scores + indices at least
     assert d >= 32 * 32768 * 4 + 32 * 2048 * 4
     assert dsa.workspace_size(99, 1, 1, 1, 1, 1) == 0
+
+
+def test_decode_step_static_validation():
+    """The static-scratch decode step validates like dsa_decode_step and
+    refuses sizes whose workspace exceeds its scratch before any HIP call."""
+    c = dsa._PagedCacheC(64, 10, 2048, 0, 0, 0x1000, None, 0x1000, None,
+                         0x1000, 0x1000)
+
+    def f(cache=c, **kw):
+        a = dict(B=2, T=1, H_I=64, d_I=128, H=128, K=64, msl=256, qp=None)
+        a.update(kw)
+        return lib.dsa_decode_step_static(
+            a["B"], a["T"], a["H_I"], a["d_I"], a["H"], a["K"], 0.07,
+            ctypes.byref(cache) if cache else None, a["msl"], FAKE, 0, FAKE,
+            FAKE, a["qp"], FAKE, FAKE, None, None)
+    assert f(cache=None) == NULL
+    assert f(H=129) == UNSUP
+    big = dict(B=200, msl=131072)
+    assert dsa.workspace_size(dsa.OP_DECODE_STEP, 200, 1, 131072, 128,
+                              64) > dsa.STATIC_SCRATCH_BYTES
+    assert f(**big) == WS
+    assert b"static scratch" in lib.dsa_last_error()
