@@ -30,11 +30,26 @@ __device__ __forceinline__ f32x16 mfma32(const uint4& a, const uint4& b,
 }
 
 // Value held by lane (l ^ 32): the two wave halves exchange registers.
-__device__ __forceinline__ float swap_halves(float x) {
+// (Only one of the instruction's two results is taken per lane: the
+// compiler treats the two results of a swap of a register with itself as
+// equal, which folds an expression that uses both.)
+__device__ __forceinline__ float swap_halves(float x, int lane) {
   auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(int, x),
                                             __builtin_bit_cast(int, x), false,
                                             false);
-  return __builtin_bit_cast(float, lane_id() < 32 ? r[1] : r[0]);
+  return __builtin_bit_cast(float, lane < 32 ? r[1] : r[0]);
+}
+__device__ __forceinline__ float swap_halves(float x) {
+  return swap_halves(x, lane_id());
+}
+
+// The lane index computed afresh (the compiler cannot reuse an earlier
+// value): after a long loop, values derived from it need not stay live.
+__device__ __forceinline__ int fresh_lane_id() {
+  int l;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0"
+               : "=v"(l));
+  return l;
 }
 
 // Two fp32 -> packed bf16x2 (round to nearest even).

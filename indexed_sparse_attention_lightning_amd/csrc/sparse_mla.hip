@@ -45,6 +45,8 @@ constexpr int kStageRow = kValue + 16;   // staged half partial row (bytes)
 constexpr int kQRegSteps = 27;                  // Q k-steps kept in registers
 constexpr int kQLdsSteps = kLatent / 16 - kQRegSteps;   // 9 in LDS
 constexpr int kQLdsStride = 2 * kQLdsSteps + 1; // uint4 per head (padded)
+constexpr int kQMaxSlot = 2 * kQLdsSteps;        // the padding slot: the
+                                                // head's largest logit
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kRef = 64.0f;     // log2 headroom of the first-pass reference
@@ -299,8 +301,6 @@ struct HeadState {
   uint4 qb[kQRegSteps];     // B operands: this lane's head, 8 features/k-step
   f32x16 o[kValue / 32];    // O^T accumulators, 16 dv tiles of 32
   float m, l;               // softmax reference (log2 units) and partial sum
-  float* mx;                // LDS: largest logit of each of the wave's 32
-                            // heads (log2 units)
   int* redo;                // LDS: set when a logit exceeds m by > kRange
 };
 
@@ -312,14 +312,15 @@ __device__ __forceinline__ s16x4 lds_tr16(const char* p) {
 
 // S^T accumulation in VGPRs.  The O accumulator fills all 256 AGPRs, so the
 // S^T chain uses the VGPR form of the 32x32x16 bf16 MFMA, issued directly:
-// the first starts from a zero accumulator, the chained ones accumulate into
+// the first starts from a zero accumulator (its result registers may not
+// overlap its operands: early clobber), the chained ones accumulate into
 // exactly the same registers (back-to-back dependent accumulation, which the
 // hardware forwards), and the last is followed by enough wait states before
 // any VALU instruction reads the result.
 __device__ __forceinline__ void mfma32_vgpr_first(f32x16& c, const uint4& a,
                                                   const uint4& b) {
   asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0"
-               : "=v"(c)
+               : "=&v"(c)
                : "v"(__builtin_bit_cast(bf16x8, a)),
                  "v"(__builtin_bit_cast(bf16x8, b)));
 }
@@ -494,9 +495,13 @@ __device__ __forceinline__ void compute_tile(const uint4* tile,
   // A head whose logits go past that range is flagged, and the workgroup
   // runs its rows a second time with m = the true max (p <= 1) -- a rare
   // path: N(0,1) inputs stay within a few units of the first tile's max.
-  // (Both kept in LDS: the loop has no registers to spare.)
-  __hip_atomic_fetch_max(st.mx + n, tmax, __ATOMIC_RELAXED,
-                         __HIP_MEMORY_SCOPE_WORKGROUP);
+  // (Both kept in LDS: the loop has no registers to spare.  The max sits
+  // in the padding slot of the head's query row in LDS, so the lanes of
+  // the first half reach it at a fixed offset from their query pointer.)
+  if (h == 0)
+    __hip_atomic_fetch_max(reinterpret_cast<float*>(
+                               const_cast<uint4*>(qrow) + kQMaxSlot),
+                           tmax, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
   if (st.m == -__builtin_inff() && tmax != -__builtin_inff()) st.m = tmax + kRef;
   if (tmax > st.m + kRange) *st.redo = 1;
   // no reference yet (no valid row so far): subtracting +inf gives p = 0
@@ -593,7 +598,6 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_kernel(
   __shared__ uint4 qlds[128 * kQLdsStride];
   __shared__ float tmul[T128 ? kTmulRows * 32 : 1];
   __shared__ int redo;   // some head needs the second softmax pass
-  __shared__ float mxs[128];   // per head: largest logit (log2 units)
   static_assert(32 * kStageRow <= kBufSlots * 16 &&
                     32 * kStageRow <= (FP8 ? kTileSlots : 128 * kQLdsStride) * 16,
                 "epilogue staging regions");
@@ -652,7 +656,6 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_kernel(
   HeadState st;
   st.m = -__builtin_inff();
   st.l = 0.f;
-  st.mx = &mxs[wave * 32];
   st.redo = &redo;
 #pragma unroll
   for (int t = 0; t < kValue / 32; ++t) st.o[t] = f32x16{};
@@ -730,7 +733,9 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_kernel(
     for (int ks = 0; ks < kQRegSteps; ++ks) st.qb[ks] = make_uint4(0, 0, 0, 0);
   }
   if (tid == 0) redo = 0;
-  if (tid < 128) mxs[tid] = -__builtin_inff();
+  if (tid < 128)
+    *reinterpret_cast<float*>(qlds + tid * kQLdsStride + kQMaxSlot) =
+        -__builtin_inff();
   barrier(true);
   const uint4* qrow = qlds + (wave * 32 + n) * kQLdsStride + h;
   const float sl2 = p.scale * kLog2e;
@@ -791,22 +796,38 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_kernel(
       if (redo == 0) break;
       // second pass: every head of the workgroup restarts with its true
       // max as the reference (all of a tile's loads are shared by the waves)
+      const int lane = fresh_lane_id();
+      const int n = lane & 31, h = lane >> 5;
+      const int head = wave * 32 + n;
 #pragma unroll
       for (int t = 0; t < kValue / 32; ++t) st.o[t] = f32x16{};
       st.l = 0.f;
-      st.m = st.mx[n];
+      st.m = *reinterpret_cast<const float*>(qlds + head * kQLdsStride + kQMaxSlot);
+      // the query operands are loaded again rather than kept live across
+      // the end of the first pass (registers: the loop has none to spare)
+      {
+        const uint16_t* qh =
+            p.q + ((int64_t)s.token * p.H + min(head, p.H - 1)) * kLatent;
+#pragma unroll
+        for (int ks = 0; ks < kQRegSteps; ++ks)
+          st.qb[ks] = head < p.H ? ld16(qh + ks * 16 + h * 8) : make_uint4(0, 0, 0, 0);
+      }
       issue(0, buf0, sc0);
       issue(min(1, s.ntiles - 1), buf1, sc1);
     }
   }
   if (!active) return;   // wave-uniform; ended waves leave the barriers
 
-  const float ltot = st.l + swap_halves(st.l);
-  const int dvb = 4 * h;   // first of this lane's 4 consecutive dv per group
+  // lane-derived values afresh: keeping them across the loop costs spills
+  const int lane2 = fresh_lane_id();
+  const int n2 = lane2 & 31, h2 = lane2 >> 5;
+  const int head2 = wave * 32 + n2;
+  const float ltot = st.l + swap_halves(st.l, lane2);
+  const int dvb = 4 * h2;   // first of this lane2's 4 consecutive dv per group
   if (gridDim.x == 1) {
-    if (head >= p.H) return;
+    if (head2 >= p.H) return;
     const float inv = ltot > 0.f ? 1.0f / ltot : 0.f;
-    float* o = p.out + ((int64_t)s.token * p.H + head) * kValue;
+    float* o = p.out + ((int64_t)s.token * p.H + head2) * kValue;
 #pragma unroll
     for (int t = 0; t < kValue / 32; ++t)
 #pragma unroll
@@ -814,8 +835,8 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_kernel(
         *reinterpret_cast<float4*>(o + 32 * t + 8 * g + dvb) =
             make_float4(st.o[t][4 * g] * inv, st.o[t][4 * g + 1] * inv,
                         st.o[t][4 * g + 2] * inv, st.o[t][4 * g + 3] * inv);
-    if (h == 0)
-      p.lse[(int64_t)s.token * p.H + head] =
+    if (h2 == 0)
+      p.lse[(int64_t)s.token * p.H + head2] =
           ltot > 0.f ? (st.m + __builtin_log2f(ltot)) * kLn2 : -__builtin_inff();
   } else {
     // partial of this split: O / l in bf16 (relative rounding 2^-9, well
@@ -831,12 +852,12 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_kernel(
     const float inv = ltot > 0.f ? 1.0f / ltot : 0.f;
     const int64_t slot0 = ((int64_t)s.token * gridDim.x + split) * p.H + wave * 32;
     uint16_t* const o0 = reinterpret_cast<uint16_t*>(p.partial) + slot0 * kValue;
-    const int rr = lane >> 5;   // row of the pair a read instruction covers
+    const int rr = lane2 >> 5;   // row of the pair a read instruction covers
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
       {
-        char* const wr = stg + n * kStageRow;
-        const int sx = (n >> 4) << 3;
+        char* const wr = stg + n2 * kStageRow;
+        const int sx = (n2 >> 4) << 3;
 #pragma unroll
         for (int t = 0; t < kValue / 64; ++t)
 #pragma unroll
@@ -850,17 +871,17 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_kernel(
 #pragma unroll 4
       for (int r0 = 0; r0 < 32; r0 += 2) {
         const int r = r0 + rr;
-        uint4 v = *reinterpret_cast<const uint4*>(stg + r * kStageRow + (lane & 31) * 16);
+        uint4 v = *reinterpret_cast<const uint4*>(stg + r * kStageRow + (lane2 & 31) * 16);
         if (r >= 16) v = make_uint4(v.z, v.w, v.x, v.y);
         if (wave * 32 + r < p.H)
-          st16_stream(o0 + (int64_t)r * kValue + half * (kValue / 2) + (lane & 31) * 8,
+          st16_stream(o0 + (int64_t)r * kValue + half * (kValue / 2) + (lane2 & 31) * 8,
                       v);
       }
       // a wave's LDS accesses run in order: the second half may overwrite
       // the first once its reads are issued
     }
-    const int64_t slot = slot0 + n;
-    if (h == 0 && head < p.H) {
+    const int64_t slot = slot0 + n2;
+    if (h2 == 0 && head2 < p.H) {
       const int64_t nslots = (int64_t)gridDim.y * gridDim.x * p.H;
       float* ml = reinterpret_cast<float*>(
                       reinterpret_cast<uint16_t*>(p.partial) + nslots * kValue) +

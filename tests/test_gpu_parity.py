@@ -308,3 +308,20 @@ def test_wide_logit_range(B, T, H, K, fmt):
     err = np.abs(out - ref_o).max()
     assert err <= 1e-2 * np.abs(ref_o).max(), err
     assert np.abs(lse - ref_l).max() <= 1e-3
+
+
+@pytest.mark.parametrize("case", ["few_values", "all_equal"])
+def test_decode_split_topk_ties(case):
+    """Decode rows of 32768 positions whose scores take few distinct values,
+    through the decode step's split selection: with one indexer head
+    reading one key feature, the scores are w * max(0, k) (five values), so
+    the threshold digit holds thousands of equal keys (the finishing
+    workgroup resolves them from the list, ties to the lower position);
+    with all queries zero every score is 0 and the threshold digit holds
+    the whole row (more than the list takes: the finishing workgroup
+    selects from the whole row)."""
+    wl = wk.scaled(W["decode"], B=3, top_k=2048, H=32, seed=41)
+    q = np.zeros((wl.B, wl.T, wl.H_I, wl.d_I), dtype=np.float32)
+    if case == "few_values":
+        q[:, :, 0, 0] = 1.0
+    check_workload(wl, q_idx=wk.f32_to_bf16_bits(q), separate=False)
