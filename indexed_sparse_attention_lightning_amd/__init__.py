@@ -203,11 +203,9 @@ def topk(scores: torch.Tensor, q_pos: torch.Tensor, k: int,
          out: Optional[torch.Tensor] = None,
          workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
     """idx [B, T, k] int32: the min(k, q_pos+1) best positions of each row
-    (ties to the lower position), ascending, then -1.  Rows of one query
-    per sequence past 8192 positions, and rows past 65536, use a workspace
-    of workspace_size(OP_TOPK, ...) bytes for the selection over many
-    workgroups (allocated here when not given; an empty tensor selects the
-    one-workgroup-per-row path)."""
+    (ties to the lower position), ascending, then -1.  Rows longer than
+    65536 use a workspace of workspace_size(OP_TOPK, ...) bytes (allocated
+    here when not given; an empty tensor selects the one-workgroup path)."""
     B, T, L = scores.shape
     _need(scores, "scores", torch.float32)
     _need(q_pos, "q_pos", torch.int32, (B, T))

@@ -77,7 +77,7 @@ size_t decode_ws(int B, int T, int L, int H, int K) {
   const size_t tokens = (size_t)B * T;
   return align_up(tokens * (size_t)L * sizeof(float)) +
          align_up(tokens * (size_t)K * sizeof(int32_t)) +
-         align_up(dsa::topk_workspace_bytes((int)tokens, T, L, K)) +
+         align_up(dsa::topk_workspace_bytes((int)tokens, L, K)) +
          align_up(dsa::attn_workspace_bytes((int)tokens, H, K)) +
          align_up(tokens * dsa::kSpanMax * 2 * sizeof(uint32_t));
 }
@@ -150,7 +150,7 @@ size_t dsa_workspace_size(int op, int B, int T, int L, int H, int K) {
   if (B < 1 || T < 1 || L < 1 || H < 1 || K < 1) return 0;
   switch (op) {
     case DSA_OP_INDEXER_SCORES: return 0;
-    case DSA_OP_TOPK: return dsa::topk_workspace_bytes(B * T, T, L, K);
+    case DSA_OP_TOPK: return dsa::topk_workspace_bytes(B * T, L, K);
     case DSA_OP_SPARSE_MLA: return dsa::attn_workspace_bytes(B * T, H, K);
     case DSA_OP_DECODE_STEP: return decode_ws(B, T, L, H, K);
     default: return 0;
@@ -307,7 +307,7 @@ dsa_status decode_step_impl(int B, int T, int H_I, int d_I, int H, int K,
   int32_t* idx = reinterpret_cast<int32_t*>(ws);
   ws += align_up(tokens * (size_t)K * sizeof(int32_t));
   void* topk_ws = ws;
-  const size_t topk_bytes = dsa::topk_workspace_bytes((int)tokens, T, max_seq_len, K);
+  const size_t topk_bytes = dsa::topk_workspace_bytes((int)tokens, max_seq_len, K);
   ws += align_up(topk_bytes);
   float* partial = reinterpret_cast<float*>(ws);
   ws += align_up(dsa::attn_workspace_bytes((int)tokens, H, K));

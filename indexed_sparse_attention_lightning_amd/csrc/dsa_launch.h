@@ -76,27 +76,21 @@ struct TopkLaunch {
   const float* scores;
   QueryPos qp;
   int32_t* idx;            // [rows, K]
+  int nchunks, chunk;      // long rows: chunks per row, positions per chunk
+  int32_t* cand;           // long rows: [rows, nchunks, K] candidate lists
   int keys_in;             // scores holds score_key bit patterns already
-  const uint32_t* span;    // per-row key ranges (rows of kSpanMax (min, max)
-  int span_kpw;            // pairs), one per span_kpw positions (entries past
-                           // a row's causal positions unused), or nullptr
-  // split selection (workspace; set by launch_topk)
-  int schunks, mwords;     // chunks per row, bitmap words per row
-  uint16_t* shist;         // [rows, schunks, 2048] chunk histograms
-  uint32_t* smask;         // [rows, mwords] keys above the threshold digit
-  uint2* scand;            // [rows, cap] (position, relative key) of the
-                           // threshold digit's keys
-  uint32_t* srec;          // [rows, 8] the row's threshold record
+  const uint32_t* span;    // keys_in rows only, or nullptr: the indexer's
+  int span_kpw;            // per-row key ranges, one per span_kpw positions
+                           // (entries past a row's causal positions unused)
 };
 // One workgroup per row.
 hipError_t launch_topk(const TopkLaunch& a, hipStream_t stream);
-// Decode rows (T == 1) past 8192 positions and every row past 64K positions
-// go through the split selection (many workgroups a row) when the workspace
-// holds topk_workspace_bytes(); otherwise as above.
+// Rows longer than 64K positions go through per-chunk candidate lists when
+// the workspace holds topk_workspace_bytes(); otherwise as above.
 hipError_t launch_topk(const TopkLaunch& a, void* workspace,
                        size_t workspace_bytes, hipStream_t stream);
-bool topk_split(int T, int L);
-size_t topk_workspace_bytes(int rows, int T, int L, int K);
+int topk_chunks(int L);
+size_t topk_workspace_bytes(int rows, int L, int K);
 
 struct AttnLaunch {
   int B, T, H, K;

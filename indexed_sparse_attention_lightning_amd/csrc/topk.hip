@@ -13,12 +13,11 @@
 // [w*KPT*64, (w+1)*KPT*64), lane l position w*KPT*64 + j*64 + l of step j,
 // so one compare-and-ballot covers 64 consecutive positions.  Rows of up to
 // 64K positions keep their keys in registers for the whole selection.
-// A decode batch has few rows: one workgroup each would leave most of the
-// chip idle.  Its rows (one query per sequence, past 8192 positions) and
-// every row past 64K positions take the first digit over many workgroups
-// instead (the split kernels below: one workgroup per 4096-position chunk
-// histograms, then thresholds and classifies its chunk), and one workgroup
-// per row finishes on the few keys of the threshold digit.
+// Longer rows, given a workspace, go in two launches: one workgroup per
+// 16K-position chunk selects the chunk's own Top-K into a candidate list,
+// then one workgroup per row selects from its chunks' lists (the row's Top-K
+// lies in their union, and list order is position order); without the
+// workspace one workgroup streams the whole row through each pass.
 //
 // The exact K-th largest key `thr` is found digit by digit, with the digits
 // cut from the row's own key range [min, max] rather than from fixed bit
@@ -44,19 +43,6 @@ constexpr int kBinsPerThread = kMaxBins / kThreads;   // 8
 
 constexpr int kSlab = 512;                  // candidates a wave may keep
 constexpr int kMaxWords = 131072 / 32;      // bitmap words of the longest row
-
-// Split selection of a row over many workgroups (see the split kernels):
-// chunks of kSplitC positions, a first digit of up to kSplitBits bits.
-constexpr int kSplitC = 4096;
-constexpr int kSplitThreads = 256;
-constexpr int kSplitKPT = kSplitC / kSplitThreads;   // 16 keys a thread
-constexpr int kSplitBits = 11;
-constexpr int kSplitBins = 1 << kSplitBits;
-constexpr int kSplitCap = kWaves * kSlab;     // threshold-digit keys a row's
-                                              // finishing workgroup takes
-// the split kernels' per-row record
-constexpr int kRecKmin = 0, kRecShift = 1, kRecDigit = 2, kRecAbove = 3,
-              kRecCount = 4, kRecRem = 5, kRecCand = 6, kRecWords = 8;
 
 struct alignas(16) TopkShared {
   uint32_t hist[kMaxBins + 4];   // hist[d]: keys with digit d; the slot past
@@ -270,45 +256,58 @@ struct RowKeys {
 
 // What one workgroup selects from:
 //   kRow     a whole score row (positions 0..n-1, n from the query position);
+//   kChunk   chunk c of a row (its positions c*chunk ..), writing the chunk's
+//            own Top-K as row positions (-1 padded) to the candidate lists;
+//   kGather  a row's candidate lists (nchunks * K slots of positions in
+//            ascending order, -1 holes), each slot's key read from the row
+//            at its position.  A row's Top-K lies in the union of its chunks'
+//            Top-Ks (an entry of the row's Top-K has fewer than K entries
+//            above it in its own chunk), and slot order is position order,
+//            so ties still go to the lower position.
 //   kRowSpan as kRow, for rows whose keys the indexer wrote together with
 //            each of its waves' (min, max) key: the row's range is known
 //            before the keys arrive, so the first histogram counts each key
 //            step as its load completes (no pass and barrier for the range)
-//   kFinish  a row whose first digit the split kernels below already took
-//            over many workgroups: the keys in digits above the threshold
-//            digit arrive as a bitmap and the keys of the threshold digit as
-//            a (position, relative key) list, and the remaining digits run on
-//            that list only; a row whose threshold digit holds more keys than
-//            the lists take runs as kRow
-enum TopkMode { kRow = 0, kRowSpan = 3, kFinish = 4 };
+enum TopkMode { kRow = 0, kChunk = 1, kGather = 2, kRowSpan = 3 };
 
 template <int KPT, bool RES, int MODE = kRow>
 __global__ __launch_bounds__(kThreads, 1) void topk_kernel(TopkLaunch p) {
   __shared__ TopkShared sm;
   const int tid = threadIdx.x, lane = lane_id();
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
-  const int r = blockIdx.x;
+  const int r = MODE == kChunk ? blockIdx.x / p.nchunks : blockIdx.x;
   const int b = r / p.T, t = r % p.T;
   const int qpos = query_pos(p.qp, b, t);
-  const int n = max(0, min(qpos + 1, p.L));   // causal candidates of the row
-  const int kk = min(p.K, n);
+  const int nrow = max(0, min(qpos + 1, p.L));   // causal candidates of the row
+  int n, kk, pbase = 0;
   const float* rowp = p.scores + (int64_t)r * p.L;
-  int32_t* const out = p.idx + (int64_t)r * p.K;
+  const int32_t* cand = nullptr;
+  int32_t* out;
+  if constexpr (MODE == kRow || MODE == kRowSpan) {
+    n = nrow;
+    kk = min(p.K, n);
+    out = p.idx + (int64_t)r * p.K;
+  } else if constexpr (MODE == kChunk) {
+    const int c = blockIdx.x % p.nchunks;
+    pbase = c * p.chunk;
+    n = max(0, min(nrow - pbase, p.chunk));
+    kk = min(p.K, n);
+    rowp += pbase;
+    out = p.cand + (int64_t)blockIdx.x * p.K;
+  } else {
+    n = p.nchunks * p.K;   // candidate slots
+    kk = min(p.K, nrow);
+    cand = p.cand + (int64_t)r * n;
+    out = p.idx + (int64_t)r * p.K;
+  }
 
   for (int i = kk + tid; i < p.K; i += kThreads) out[i] = -1;
   if (kk == n) {  // every candidate is selected
-    for (int i = tid; i < n; i += kThreads) out[i] = i;
+    for (int i = tid; i < n; i += kThreads)
+      out[i] = MODE == kGather ? cand[i] : pbase + i;
     return;
   }
-  // kFinish: the split kernels' record of this row (uniform)
-  bool fast = false;
-  uint32_t rec[kRecWords] = {};
-  if constexpr (MODE == kFinish) {
-#pragma unroll
-    for (int i = 0; i < kRecWords; ++i)
-      rec[i] = __builtin_amdgcn_readfirstlane(p.srec[(int64_t)r * kRecWords + i]);
-    fast = rec[kRecCount] <= (uint32_t)kSplitCap;
-  }
+  if (MODE == kGather && kk == 0) return;
 
   // the row's key range from the indexer's span entries 0 .. ns-1 (those
   // that cover its causal positions 0 .. n-1), loaded before the keys: the
@@ -335,17 +334,40 @@ __global__ __launch_bounds__(kThreads, 1) void topk_kernel(TopkLaunch p) {
   const int nsteps =
       min(KPT, max(0, (n - wave * KPT * kWave + kWave - 1) / kWave));
 
-  uint32_t rem = (uint32_t)kk, d0 = 0, cnt0 = 0, blo = 0;
-  int nsh = 0;
-  if (!fast) {
-    // ---- load; min / max over the candidates; clear histogram and bitmap
-    uint32_t mn = 0xffffffffu, mx = 0u;   // min taken over key - 1
-    if constexpr (RES) {
-      // buffer loads bounded by the candidate count: positions past n read 0
-      // without branches, and all loads share one offset register
+  // ---- load; min / max over the candidates; clear histogram and bitmap
+  uint32_t mn = 0xffffffffu, mx = 0u;   // min taken over key - 1
+  if constexpr (RES) {
+    // buffer loads bounded by the candidate count: positions past n read 0
+    // without branches, and all loads share one offset register
+    if constexpr (MODE == kGather) {
+      // slot positions first (slots past n are holes), then the scores at
+      // those positions (a hole's offset is out of the row's range: the
+      // bounded load reads 0 without touching memory); a hole gets key 0
+      const __amdgpu_buffer_rsrc_t cs = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<int32_t*>(cand), 0, n * 4, 0x00020000);
+      int32_t ps[KPT];
+#pragma unroll
+      for (int j = 0; j < KPT; ++j) {
+        const int32_t v = __builtin_amdgcn_raw_buffer_load_b32(
+            cs, (keys.wbase + lane) * 4, j * kWave * 4, 0);
+        ps[j] = keys.valid(j) ? v : -1;
+      }
+      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<float*>(keys.row), 0, nrow * 4, 0x00020000);
+#pragma unroll
+      for (int j = 0; j < KPT; ++j)
+        keys.k[j] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(
+            rs, (uint32_t)ps[j] * 4u, 0, 0);
+#pragma unroll
+      for (int j = 0; j < KPT; ++j) {
+        keys.k[j] = ps[j] >= 0 ? as_key(keys.k[j], keys.keys_in) : 0u;
+        mn = min(mn, keys.k[j] - 1u);
+        mx = max(mx, keys.k[j]);
+      }
+    } else {
       const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
           const_cast<float*>(keys.row), 0, n * 4, 0x00020000);
-  #pragma unroll
+#pragma unroll
       for (int j = 0; j < KPT; ++j)
         keys.k[j] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(
             rs, (keys.wbase + lane) * 4, j * kWave * 4, 0);
@@ -358,223 +380,197 @@ __global__ __launch_bounds__(kThreads, 1) void topk_kernel(TopkLaunch p) {
         const bool padded = keys.wbase + KPT * kWave > n;   // wave-uniform
         const bool kin = keys.keys_in;
         if (padded) {
-  #pragma unroll
+#pragma unroll
           for (int j = 0; j < KPT; ++j)
             keys.k[j] = keys.valid(j) ? as_key(keys.k[j], kin) : 0u;
         } else if (!kin) {
-  #pragma unroll
+#pragma unroll
           for (int j = 0; j < KPT; ++j)
             keys.k[j] = score_key(__builtin_bit_cast(float, keys.k[j]));
         }
-  #pragma unroll
+#pragma unroll
         for (int j = 0; j < KPT; ++j) {
           mn = min(mn, keys.k[j] - 1u);
           mx = max(mx, keys.k[j]);
         }
       }
-
-    } else {
-      // kmin is still 0: absolute keys, 0 past n
-      keys.stream(nsteps, [&](int, uint32_t k) {
-        mn = min(mn, k - 1u);
-        mx = max(mx, k);
-      });
     }
-    {
-      uint4* h = reinterpret_cast<uint4*>(sm.hist);
-      for (int i = tid; i < (kMaxBins + 4) / 4; i += kThreads)
-        h[i] = make_uint4(0, 0, 0, 0);
-      uint4* e = reinterpret_cast<uint4*>(sm.eqw);
-      for (int i = tid; i < kMaxWords / 4; i += kThreads)
-        e[i] = make_uint4(0, 0, 0, 0);
-      if (tid == 0) sm.overflow = 0u;
-    }
-    uint32_t kmin, kmax;
-    if constexpr (MODE == kRowSpan) {
-      // every wave reduces the span entries itself: no exchange
-      kmin = smn != 0xffffffffu ? smn - 1u : 0xffffffffu;
-      kmax = smx;
-      wave_minmax(kmin, kmax);
-      __syncthreads();   // the cleared histogram and bitmap
-    } else {
-      wave_minmax(mn, mx);
-      if (lane == 0) {
-        sm.wmin[wave] = mn;
-        sm.wmax[wave] = mx;
-      }
-      __syncthreads();
-      kmin = lane < kWaves ? sm.wmin[lane] : 0xffffffffu;
-      kmax = lane < kWaves ? sm.wmax[lane] : 0u;
-      wave_minmax(kmin, kmax);
-    }
-    // some lane holds a candidate (n >= 2 here).  kmin is the smallest
-    // candidate key minus one: candidates have relative keys >= 1 and lanes
-    // past n (or holes between candidate slots) the relative key 0, which no
-    // histogram, candidate list or bitmap takes.
-    keys.kmin = kmin;
-    if constexpr (RES && MODE != kRowSpan) {   // kRowSpan: in the first count
-  #pragma unroll
-      for (int j = 0; j < KPT; ++j)
-        keys.k[j] = keys.k[j] ? keys.k[j] - kmin : 0u;
-    }
-
-    // ---- first digit over all keys: digit(r) = r >> nsh, r <= range
-    const uint32_t range = kmax - kmin;
-    const int sh0 = 32 - __builtin_clz(range);   // range >= 1, < 2^sh0
-    if (sh0 > 0) {
-      const int np = (sh0 + kDigitBits - 1) / kDigitBits;
-      const int nbits = (sh0 + np - 1) / np;
-      nsh = sh0 - nbits;
-      const int nb = 1 << nbits;
-      const auto count = [&](int j, uint32_t rk) {
-        (void)j;
-        if (rk != 0u) atomicAdd(&sm.hist[rk >> nsh], 1u);   // rk <= range < 2^sh0
-      };
-      // only waves that reach past n (or hold candidate-slot holes) have
-      // keys to skip; the others count without the test
-      const bool padded = keys.wbase + KPT * kWave > n;
-      if constexpr (MODE == kRowSpan) {
-        // each key step is made relative and counted as its load completes
-        if (padded) {
-  #pragma unroll
-          for (int j = 0; j < KPT; ++j) {
-            const uint32_t k = keys.k[j];
-            const uint32_t rk = k ? k - kmin : 0u;
-            keys.k[j] = rk;
-            if (rk != 0u) atomicAdd(&sm.hist[rk >> nsh], 1u);
-            TOPK_STEP_FENCE(j);
-          }
-        } else {
-  #pragma unroll
-          for (int j = 0; j < KPT; ++j) {
-            const uint32_t rk = keys.k[j] - kmin;   // keys >= 1 > kmin
-            keys.k[j] = rk;
-            atomicAdd(&sm.hist[rk >> nsh], 1u);
-            TOPK_STEP_FENCE(j);
-          }
-        }
-      } else if constexpr (RES) {
-        if (padded) {
-  #pragma unroll
-          for (int j = 0; j < KPT; ++j) {
-            count(j, keys.k[j]);
-            TOPK_STEP_FENCE(j);
-          }
-        } else {
-  #pragma unroll
-          for (int j = 0; j < KPT; ++j) {
-            atomicAdd(&sm.hist[keys.k[j] >> nsh], 1u);
-            TOPK_STEP_FENCE(j);
-          }
-        }
-      } else {
-        keys.stream(nsteps, count);
-      }
-      __syncthreads();
-      uint32_t above;
-      pick_digit(sm.hist, nb, rem, sm, 0, tid, lane, wave, d0, above, cnt0);
-      rem -= above;
-    }
-    // digit d0 spans relative keys [blo, bhi]; blo1 leaves out the key 0 of
-    // lanes past n
-    blo = d0 << nsh;
-    const uint32_t bhi = blo | ((1u << nsh) - 1u);
-    const uint32_t blo1 = blo > 1u ? blo : 1u;
-
-    // ---- sweep: bitmap of keys in larger digits; keys in digit d0 are
-    // final (nsh == 0: they all equal the threshold) or go to the wave's
-    // candidate list, in position order
-    uint32_t ns = 0;
-    // resident rows gather the wave's 2*KPT mask words in registers (word i
-    // in lane i % 64 of register i / 64) and store them once
-    constexpr int kMaskRegs = RES ? (2 * KPT + kWave - 1) / kWave : 1;
-    uint32_t gwr[kMaskRegs], ewr[kMaskRegs];
-  #pragma unroll
-    for (int i = 0; i < kMaskRegs; ++i) gwr[i] = ewr[i] = 0u;
-    const auto sweep = [&](int j, uint32_t rk) {
-      const bool in = rk >= blo1 && rk <= bhi;
-      const uint64_t g = __ballot(rk > bhi);
-      const uint64_t c = __ballot(in);
-      if constexpr (RES) {
-        const int i0 = (2 * j) / kWave, l0 = (2 * j) % kWave;
-        gwr[i0] = writelane(gwr[i0], (uint32_t)g, l0);
-        gwr[i0] = writelane(gwr[i0], (uint32_t)(g >> 32), l0 + 1);
-        if (nsh == 0) {
-          ewr[i0] = writelane(ewr[i0], (uint32_t)c, l0);
-          ewr[i0] = writelane(ewr[i0], (uint32_t)(c >> 32), l0 + 1);
-        }
-      } else {
-        const int wd = 2 * (wave * KPT + j);
-        if (lane == 0) {
-          sm.gtw[wd] = (uint32_t)g;
-          sm.gtw[wd + 1] = (uint32_t)(g >> 32);
-          if (nsh == 0) {
-            sm.eqw[wd] = (uint32_t)c;
-            sm.eqw[wd + 1] = (uint32_t)(c >> 32);
-          }
-        }
-      }
-      if (nsh != 0 && c != 0ull) {
-        const uint32_t at = ns + lanes_below(c);
-        if (in && at < (uint32_t)kSlab)
-          sm.slab[wave][at] = make_uint2((uint32_t)keys.pos(j), rk);
-        ns += __builtin_popcountll(c);
-      }
-    };
-    if constexpr (RES) {
-  #pragma unroll
-      for (int j = 0; j < KPT; ++j) {
-        sweep(j, keys.k[j]);
-        TOPK_STEP_FENCE(j);
-      }
-    } else {
-      keys.stream(nsteps, sweep);
-    }
-    if constexpr (RES) {
-  #pragma unroll
-      for (int i = 0; i < kMaskRegs; ++i) {
-        const int wd = i * kWave + lane;
-        if (wd < 2 * KPT) {
-          sm.gtw[2 * wave * KPT + wd] = gwr[i];
-          if (nsh == 0) sm.eqw[2 * wave * KPT + wd] = ewr[i];
-        }
-      }
-    }
-    if (lane == 0) {
-      sm.scnt[wave] = min(ns, (uint32_t)kSlab);
-      if (ns > (uint32_t)kSlab) sm.overflow = 1u;
-    }
-    __syncthreads();
   } else {
-    // ---- kFinish: the first digit was taken by the split kernels; the
-    // keys in larger digits arrive as a bitmap, the threshold digit's keys
-    // as a (position, relative key) list that the waves share out
-    nsh = (int)rec[kRecShift];
-    d0 = rec[kRecDigit];
-    cnt0 = rec[kRecCount];
-    rem = rec[kRecRem];
-    blo = d0 << nsh;
-    const int nw = (n + 31) / 32;
-    const uint32_t* mrow = p.smask + (int64_t)r * p.mwords;
-    for (int i = tid; i < nw; i += kThreads) {
-      sm.gtw[i] = mrow[i];
-      sm.eqw[i] = 0u;
-    }
-    const int per = (int)((cnt0 + kWaves - 1) / kWaves);   // <= kSlab
-    const int e0 = min((int)cnt0, wave * per), e1 = min((int)cnt0, e0 + per);
-    const uint2* crow = p.scand + (int64_t)r * kSplitCap;
-    for (int e = e0 + lane; e < e1; e += kWave) sm.slab[wave][e - e0] = crow[e];
-    if (lane == 0) sm.scnt[wave] = (uint32_t)(e1 - e0);
+    // kmin is still 0: absolute keys, 0 past n
+    keys.stream(nsteps, [&](int, uint32_t k) {
+      mn = min(mn, k - 1u);
+      mx = max(mx, k);
+    });
+  }
+  {
+    uint4* h = reinterpret_cast<uint4*>(sm.hist);
+    for (int i = tid; i < (kMaxBins + 4) / 4; i += kThreads)
+      h[i] = make_uint4(0, 0, 0, 0);
+    uint4* e = reinterpret_cast<uint4*>(sm.eqw);
+    for (int i = tid; i < kMaxWords / 4; i += kThreads)
+      e[i] = make_uint4(0, 0, 0, 0);
     if (tid == 0) sm.overflow = 0u;
+  }
+  uint32_t kmin, kmax;
+  if constexpr (MODE == kRowSpan) {
+    // every wave reduces the span entries itself: no exchange
+    kmin = smn != 0xffffffffu ? smn - 1u : 0xffffffffu;
+    kmax = smx;
+    wave_minmax(kmin, kmax);
+    __syncthreads();   // the cleared histogram and bitmap
+  } else {
+    wave_minmax(mn, mx);
+    if (lane == 0) {
+      sm.wmin[wave] = mn;
+      sm.wmax[wave] = mx;
+    }
     __syncthreads();
-    if (nsh == 0) {   // the threshold digit is the whole key: all equal
-      for (int e = e0 + lane; e < e1; e += kWave) {
-        const uint32_t ps = sm.slab[wave][e - e0].x;
-        atomicOr(&sm.eqw[ps >> 5], 1u << (ps & 31));
+    kmin = lane < kWaves ? sm.wmin[lane] : 0xffffffffu;
+    kmax = lane < kWaves ? sm.wmax[lane] : 0u;
+    wave_minmax(kmin, kmax);
+  }
+  // some lane holds a candidate (n >= 2 here).  kmin is the smallest
+  // candidate key minus one: candidates have relative keys >= 1 and lanes
+  // past n (or holes between candidate slots) the relative key 0, which no
+  // histogram, candidate list or bitmap takes.
+  keys.kmin = kmin;
+  if constexpr (RES && MODE != kRowSpan) {   // kRowSpan: in the first count
+#pragma unroll
+    for (int j = 0; j < KPT; ++j)
+      keys.k[j] = keys.k[j] ? keys.k[j] - kmin : 0u;
+  }
+
+  // ---- first digit over all keys: digit(r) = r >> nsh, r <= range
+  const uint32_t range = kmax - kmin;
+  const int sh0 = 32 - __builtin_clz(range);   // range >= 1, < 2^sh0
+  uint32_t rem = (uint32_t)kk;
+  uint32_t d0 = 0, cnt0 = 0;
+  int nsh = 0;
+  if (sh0 > 0) {
+    const int np = (sh0 + kDigitBits - 1) / kDigitBits;
+    const int nbits = (sh0 + np - 1) / np;
+    nsh = sh0 - nbits;
+    const int nb = 1 << nbits;
+    const auto count = [&](int j, uint32_t rk) {
+      (void)j;
+      if (rk != 0u) atomicAdd(&sm.hist[rk >> nsh], 1u);   // rk <= range < 2^sh0
+    };
+    // only waves that reach past n (or hold candidate-slot holes) have
+    // keys to skip; the others count without the test
+    const bool padded = MODE == kGather || keys.wbase + KPT * kWave > n;
+    if constexpr (MODE == kRowSpan) {
+      // each key step is made relative and counted as its load completes
+      if (padded) {
+#pragma unroll
+        for (int j = 0; j < KPT; ++j) {
+          const uint32_t k = keys.k[j];
+          const uint32_t rk = k ? k - kmin : 0u;
+          keys.k[j] = rk;
+          if (rk != 0u) atomicAdd(&sm.hist[rk >> nsh], 1u);
+          TOPK_STEP_FENCE(j);
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < KPT; ++j) {
+          const uint32_t rk = keys.k[j] - kmin;   // keys >= 1 > kmin
+          keys.k[j] = rk;
+          atomicAdd(&sm.hist[rk >> nsh], 1u);
+          TOPK_STEP_FENCE(j);
+        }
       }
-      __syncthreads();
+    } else if constexpr (RES) {
+      if (padded) {
+#pragma unroll
+        for (int j = 0; j < KPT; ++j) {
+          count(j, keys.k[j]);
+          TOPK_STEP_FENCE(j);
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < KPT; ++j) {
+          atomicAdd(&sm.hist[keys.k[j] >> nsh], 1u);
+          TOPK_STEP_FENCE(j);
+        }
+      }
+    } else {
+      keys.stream(nsteps, count);
+    }
+    __syncthreads();
+    uint32_t above;
+    pick_digit(sm.hist, nb, rem, sm, 0, tid, lane, wave, d0, above, cnt0);
+    rem -= above;
+  }
+  // digit d0 spans relative keys [blo, bhi]; blo1 leaves out the key 0 of
+  // lanes past n
+  const uint32_t blo = d0 << nsh;
+  const uint32_t bhi = blo | ((1u << nsh) - 1u);
+  const uint32_t blo1 = blo > 1u ? blo : 1u;
+
+  // ---- sweep: bitmap of keys in larger digits; keys in digit d0 are
+  // final (nsh == 0: they all equal the threshold) or go to the wave's
+  // candidate list, in position order
+  uint32_t ns = 0;
+  // resident rows gather the wave's 2*KPT mask words in registers (word i
+  // in lane i % 64 of register i / 64) and store them once
+  constexpr int kMaskRegs = RES ? (2 * KPT + kWave - 1) / kWave : 1;
+  uint32_t gwr[kMaskRegs], ewr[kMaskRegs];
+#pragma unroll
+  for (int i = 0; i < kMaskRegs; ++i) gwr[i] = ewr[i] = 0u;
+  const auto sweep = [&](int j, uint32_t rk) {
+    const bool in = rk >= blo1 && rk <= bhi;
+    const uint64_t g = __ballot(rk > bhi);
+    const uint64_t c = __ballot(in);
+    if constexpr (RES) {
+      const int i0 = (2 * j) / kWave, l0 = (2 * j) % kWave;
+      gwr[i0] = writelane(gwr[i0], (uint32_t)g, l0);
+      gwr[i0] = writelane(gwr[i0], (uint32_t)(g >> 32), l0 + 1);
+      if (nsh == 0) {
+        ewr[i0] = writelane(ewr[i0], (uint32_t)c, l0);
+        ewr[i0] = writelane(ewr[i0], (uint32_t)(c >> 32), l0 + 1);
+      }
+    } else {
+      const int wd = 2 * (wave * KPT + j);
+      if (lane == 0) {
+        sm.gtw[wd] = (uint32_t)g;
+        sm.gtw[wd + 1] = (uint32_t)(g >> 32);
+        if (nsh == 0) {
+          sm.eqw[wd] = (uint32_t)c;
+          sm.eqw[wd + 1] = (uint32_t)(c >> 32);
+        }
+      }
+    }
+    if (nsh != 0 && c != 0ull) {
+      const uint32_t at = ns + lanes_below(c);
+      if (in && at < (uint32_t)kSlab)
+        sm.slab[wave][at] = make_uint2((uint32_t)keys.pos(j), rk);
+      ns += __builtin_popcountll(c);
+    }
+  };
+  if constexpr (RES) {
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+      sweep(j, keys.k[j]);
+      TOPK_STEP_FENCE(j);
+    }
+  } else {
+    keys.stream(nsteps, sweep);
+  }
+  if constexpr (RES) {
+#pragma unroll
+    for (int i = 0; i < kMaskRegs; ++i) {
+      const int wd = i * kWave + lane;
+      if (wd < 2 * KPT) {
+        sm.gtw[2 * wave * KPT + wd] = gwr[i];
+        if (nsh == 0) sm.eqw[2 * wave * KPT + wd] = ewr[i];
+      }
     }
   }
+  if (lane == 0) {
+    sm.scnt[wave] = min(ns, (uint32_t)kSlab);
+    if (ns > (uint32_t)kSlab) sm.overflow = 1u;
+  }
+  __syncthreads();
+
   uint32_t thr = blo;            // relative threshold
   uint32_t eq_total = cnt0;
   if (nsh > 0) {
@@ -706,251 +702,9 @@ __global__ __launch_bounds__(kThreads, 1) void topk_kernel(TopkLaunch p) {
       const int bit = __builtin_ctz(m);
       m &= m - 1;
       if (slot < (uint32_t)kk)
-        out[slot] = w * 32 + bit;
+        out[slot] = MODE == kGather ? cand[w * 32 + bit] : pbase + w * 32 + bit;
       ++slot;
     }
-  }
-}
-
-// ---- Split selection: a decode row's first digit over many workgroups.
-//
-// One workgroup per chunk of kSplitC positions of a row, in three launches
-// instead of one 1024-thread workgroup per row (which leaves most of the
-// chip idle while a decode batch's few rows are selected):
-//   topk_hist_kernel    the chunk's histogram of the first digit, cut from
-//                       the row's key range (its span entries, from the
-//                       indexer or topk_span_kernel);
-//   topk_thresh_kernel  every chunk sums its row's histograms, finds the
-//                       digit holding the K-th key (the same in every
-//                       chunk), writes the chunk's bitmap of keys in larger
-//                       digits and appends its keys of that digit to the
-//                       row's list;
-//   topk_kernel<kFinish> one workgroup per row runs the remaining digits on
-//                       that list and emits the positions in order.
-// A row whose threshold digit holds more than kSplitCap keys (heavy ties)
-// writes no list, and its finishing workgroup selects from the whole row.
-
-struct SplitRow {
-  int r, n, kk, p0;
-  uint32_t kmin;   // smallest candidate key - 1: candidates have keys > kmin
-  int nsh, nb;     // digit = (key - kmin) >> nsh, nb bins
-};
-
-__device__ __forceinline__ int row_candidates(const TopkLaunch& p, int r) {
-  const int qpos = query_pos(p.qp, r / p.T, r % p.T);
-  return max(0, min(qpos + 1, p.L));
-}
-
-// The row's key range from its span entries 0 .. ns-1 (those covering its
-// causal positions), reduced inside each wave: no exchange.
-__device__ __forceinline__ void split_digit(const TopkLaunch& p, SplitRow& s,
-                                            int lane) {
-  const int ns = (s.n + p.span_kpw - 1) / p.span_kpw;   // <= kSpanMax
-  uint32_t mn = 0xffffffffu, mx = 0u;
-  if (lane < ns) {
-    const uint2 v =
-        reinterpret_cast<const uint2*>(p.span)[(int64_t)s.r * kSpanMax + lane];
-    mn = v.x;
-    mx = v.y;
-  }
-  uint32_t kmin = mn != 0xffffffffu ? mn - 1u : 0xffffffffu, kmax = mx;
-  wave_minmax(kmin, kmax);
-  const uint32_t range = kmax - kmin;   // >= 1
-  const int sh0 = 32 - __builtin_clz(range);
-  const int nbits = min(sh0, kSplitBits);
-  s.kmin = kmin;
-  s.nsh = sh0 - nbits;
-  s.nb = 1 << nbits;
-}
-
-// The chunk's keys, kSplitKPT a thread (position p0 + j*256 + tid), 0 past
-// the row's candidates (bounded buffer loads).
-__device__ __forceinline__ void split_load(const TopkLaunch& p, const SplitRow& s,
-                                           int tid, uint32_t (&k)[kSplitKPT]) {
-  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<float*>(p.scores + (int64_t)s.r * p.L), 0, s.n * 4, 0x00020000);
-  // the whole offset in the lane's offset register, which the bounds
-  // check covers
-#pragma unroll
-  for (int j = 0; j < kSplitKPT; ++j)
-    k[j] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(
-        rs, (uint32_t)(s.p0 + j * kSplitThreads + tid) * 4, 0, 0);
-  if (!p.keys_in) {
-#pragma unroll
-    for (int j = 0; j < kSplitKPT; ++j)
-      k[j] = s.p0 + j * kSplitThreads + tid < s.n
-                 ? score_key(__builtin_bit_cast(float, k[j]))
-                 : 0u;
-  }
-}
-
-// The chunk's first-digit bin of key k, or -1 for a lane past the row.
-__device__ __forceinline__ int split_bin(const SplitRow& s, uint32_t k) {
-  return k > s.kmin ? (int)min((k - s.kmin) >> s.nsh, (uint32_t)s.nb - 1u) : -1;
-}
-
-// (min, max) key of each chunk of kSplitC positions, as span entries, for
-// rows whose indexer left none.
-__global__ __launch_bounds__(kSplitThreads) void topk_span_kernel(TopkLaunch p) {
-  __shared__ uint32_t wmn[kSplitThreads / kWave], wmx[kSplitThreads / kWave];
-  const int tid = threadIdx.x, lane = lane_id();
-  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
-  SplitRow s{};
-  s.r = blockIdx.y;
-  s.n = row_candidates(p, s.r);
-  s.p0 = blockIdx.x * kSplitC;
-  if (s.p0 >= s.n) return;
-  uint32_t k[kSplitKPT];
-  split_load(p, s, tid, k);
-  uint32_t mn = 0xffffffffu, mx = 0u;
-#pragma unroll
-  for (int j = 0; j < kSplitKPT; ++j)
-    if (k[j] != 0u) {   // keys of candidates are >= 1
-      mn = min(mn, k[j]);
-      mx = max(mx, k[j]);
-    }
-  wave_minmax(mn, mx);
-  if (lane == 0) {
-    wmn[wave] = mn;
-    wmx[wave] = mx;
-  }
-  __syncthreads();
-  if (tid == 0) {
-#pragma unroll
-    for (int w = 1; w < kSplitThreads / kWave; ++w) {
-      mn = min(mn, wmn[w]);
-      mx = max(mx, wmx[w]);
-    }
-    reinterpret_cast<uint2*>(const_cast<uint32_t*>(p.span))[(int64_t)s.r * kSpanMax + blockIdx.x] =
-        make_uint2(mn, mx);
-  }
-}
-
-__global__ __launch_bounds__(kSplitThreads) void topk_hist_kernel(TopkLaunch p) {
-  __shared__ uint32_t hist[kSplitBins];
-  const int tid = threadIdx.x, lane = lane_id();
-  SplitRow s{};
-  s.r = blockIdx.y;
-  s.n = row_candidates(p, s.r);
-  s.kk = min(p.K, s.n);
-  s.p0 = blockIdx.x * kSplitC;
-  if (s.p0 >= s.n || s.kk == s.n) return;
-  uint32_t k[kSplitKPT];
-  split_load(p, s, tid, k);
-  split_digit(p, s, lane);
-#pragma unroll
-  for (int i = 0; i < kSplitBins / kSplitThreads; ++i)
-    hist[i * kSplitThreads + tid] = 0u;
-  __syncthreads();
-#pragma unroll
-  for (int j = 0; j < kSplitKPT; ++j) {
-    const int d = split_bin(s, k[j]);
-    if (d >= 0) atomicAdd(&hist[d], 1u);
-  }
-  __syncthreads();
-  // bins 8t .. 8t+7 as uint16 counts (a chunk holds at most 4096 keys)
-  constexpr int kPer = kSplitBins / kSplitThreads;
-  static_assert(kPer == 8 && kSplitC < 65536, "uint16 counts, 16-byte rows");
-  uint32_t w[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-    w[i] = hist[kPer * tid + 2 * i] | (hist[kPer * tid + 2 * i + 1] << 16);
-  reinterpret_cast<uint4*>(p.shist + ((int64_t)s.r * p.schunks + blockIdx.x) *
-                                         kSplitBins)[tid] =
-      make_uint4(w[0], w[1], w[2], w[3]);
-  if (blockIdx.x == 0 && tid == 0)
-    p.srec[(int64_t)s.r * kRecWords + kRecCand] = 0u;   // list length
-}
-
-__global__ __launch_bounds__(kSplitThreads) void topk_thresh_kernel(TopkLaunch p) {
-  __shared__ uint32_t wsum[kSplitThreads / kWave];
-  __shared__ uint32_t pick[3];
-  const int tid = threadIdx.x, lane = lane_id();
-  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
-  SplitRow s{};
-  s.r = blockIdx.y;
-  s.n = row_candidates(p, s.r);
-  s.kk = min(p.K, s.n);
-  s.p0 = blockIdx.x * kSplitC;
-  if (s.p0 >= s.n || s.kk == s.n) return;
-  uint32_t k[kSplitKPT];
-  split_load(p, s, tid, k);
-  split_digit(p, s, lane);
-  // the row's histogram, summed over its chunks: thread t owns the digits
-  // nb-1-8t .. nb-8-8t, c[u] the count of digit nb-1-8t-u
-  const int nvc = (s.n + kSplitC - 1) / kSplitC;
-  const int top = s.nb - 8 * tid;
-  uint32_t c[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
-  const uint16_t* hrow = p.shist + (int64_t)s.r * p.schunks * kSplitBins;
-  if (top >= 8) {
-    for (int ch = 0; ch < nvc; ++ch) {
-      const uint4 v = *reinterpret_cast<const uint4*>(hrow + ch * kSplitBins + top - 8);
-      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {   // bins top-8+2i (low), top-7+2i (high)
-        c[7 - 2 * i] += w[i] & 0xffffu;
-        c[6 - 2 * i] += w[i] >> 16;
-      }
-    }
-  } else if (top > 0) {
-    for (int ch = 0; ch < nvc; ++ch)
-#pragma unroll
-      for (int u = 0; u < 8; ++u)
-        if (top - 1 - u >= 0) c[u] += hrow[ch * kSplitBins + top - 1 - u];
-  }
-  uint32_t sum = 0;
-#pragma unroll
-  for (int u = 0; u < 8; ++u) sum += c[u];
-  const uint32_t incl = wave_incl_scan(sum, lane);
-  if (lane == kWave - 1) wsum[wave] = incl;
-  __syncthreads();
-  uint32_t base = 0;
-#pragma unroll
-  for (int w = 0; w < kSplitThreads / kWave; ++w) base += w < wave ? wsum[w] : 0u;
-  uint32_t run = base + incl - sum;
-  const uint32_t kk = (uint32_t)s.kk;
-#pragma unroll
-  for (int u = 0; u < 8; ++u) {
-    if (c[u] && run < kk && kk <= run + c[u]) {
-      pick[0] = (uint32_t)(top - 1 - u);
-      pick[1] = run;
-      pick[2] = c[u];
-    }
-    run += c[u];
-  }
-  __syncthreads();
-  const int dstar = (int)pick[0];
-  const uint32_t above = pick[1], cnt = pick[2];
-  const bool list = cnt <= (uint32_t)kSplitCap;   // same in every chunk
-  uint32_t* mrow = p.smask + (int64_t)s.r * p.mwords;
-  uint32_t* nlist = p.srec + (int64_t)s.r * kRecWords + kRecCand;
-  uint2* crow = p.scand + (int64_t)s.r * kSplitCap;
-#pragma unroll
-  for (int j = 0; j < kSplitKPT; ++j) {
-    const int d = split_bin(s, k[j]);
-    const uint64_t gt = __ballot(d > dstar);
-    const uint64_t eq = __ballot(d == dstar);
-    const int pos0 = s.p0 + j * kSplitThreads + wave * kWave;   // 64-aligned
-    if (lane == 0) {
-      mrow[pos0 >> 5] = (uint32_t)gt;
-      mrow[(pos0 >> 5) + 1] = (uint32_t)(gt >> 32);
-    }
-    if (list && eq != 0ull) {
-      uint32_t at = 0;
-      if (lane == 0) at = atomicAdd(nlist, (uint32_t)__builtin_popcountll(eq));
-      at = __builtin_amdgcn_readfirstlane(at);
-      if (d == dstar)
-        crow[at + lanes_below(eq)] = make_uint2((uint32_t)(pos0 + lane), k[j] - s.kmin);
-    }
-  }
-  if (blockIdx.x == 0 && tid == 0) {
-    uint32_t* rec = p.srec + (int64_t)s.r * kRecWords;
-    rec[kRecKmin] = s.kmin;
-    rec[kRecShift] = (uint32_t)s.nsh;
-    rec[kRecDigit] = (uint32_t)dstar;
-    rec[kRecAbove] = above;
-    rec[kRecCount] = cnt;
-    rec[kRecRem] = kk - above;
   }
 }
 
@@ -960,82 +714,43 @@ void launch_kpt(const TopkLaunch& p, hipStream_t stream) {
                      dim3(kThreads), 0, stream, p);
 }
 
-template <int MODE>
-void launch_by_length(const TopkLaunch& p, hipStream_t stream) {
-  // positions per row a workgroup covers: 1024 * KPT
-  if (p.L <= 4 * kThreads)
-    launch_kpt<4, true, MODE>(p, stream);
-  else if (p.L <= 16 * kThreads)
-    launch_kpt<16, true, MODE>(p, stream);
-  else if (p.L <= 32 * kThreads)
-    launch_kpt<32, true, MODE>(p, stream);
-  else if (p.L <= 64 * kThreads)
-    launch_kpt<64, true, MODE>(p, stream);
-  else
-    launch_kpt<128, false, MODE>(p, stream);
-}
-
-size_t align256(size_t x) { return (x + 255) / 256 * 256; }
-
-struct SplitLayout {
-  int nch;
-  size_t hist, mask, cand, rec, span, total;   // byte offsets, total size
-};
-
-SplitLayout split_layout(int rows, int L) {
-  SplitLayout l{};
-  l.nch = (L + kSplitC - 1) / kSplitC;
-  const size_t R = (size_t)rows;
-  l.hist = 0;
-  l.mask = l.hist + align256(R * l.nch * kSplitBins * sizeof(uint16_t));
-  l.cand = l.mask + align256(R * l.nch * (kSplitC / 32) * sizeof(uint32_t));
-  l.rec = l.cand + align256(R * kSplitCap * sizeof(uint2));
-  l.span = l.rec + align256(R * kRecWords * sizeof(uint32_t));
-  l.total = l.span + align256(R * kSpanMax * sizeof(uint2));
-  return l;
-}
+constexpr int kChunkLen = 16 * kThreads;   // positions per chunk workgroup
 
 }  // namespace
 
-// Rows the split selection takes: one query per sequence (a decode batch,
-// few rows) longer than 8192 positions, and every row longer than 64K
-// positions (more than one workgroup holds in registers).
-bool topk_split(int T, int L) {
-  return L > 64 * kThreads || (T == 1 && L > 2 * kSplitC);
+int topk_chunks(int L) {
+  return L > 64 * kThreads ? (L + kChunkLen - 1) / kChunkLen : 0;
 }
 
-size_t topk_workspace_bytes(int rows, int T, int L, int K) {
-  (void)K;
-  return topk_split(T, L) ? split_layout(rows, L).total : 0;
+size_t topk_workspace_bytes(int rows, int L, int K) {
+  return (size_t)rows * topk_chunks(L) * K * sizeof(int32_t);
 }
 
 hipError_t launch_topk(const TopkLaunch& p0, void* workspace,
                        size_t workspace_bytes, hipStream_t stream) {
-  const SplitLayout l = split_layout(p0.rows, p0.L);
-  if (!topk_split(p0.T, p0.L) || !workspace || workspace_bytes < l.total)
-    return launch_topk(p0, stream);
-  TopkLaunch p = p0;
-  char* ws = static_cast<char*>(workspace);
-  p.schunks = l.nch;
-  p.mwords = l.nch * (kSplitC / 32);
-  p.shist = reinterpret_cast<uint16_t*>(ws + l.hist);
-  p.smask = reinterpret_cast<uint32_t*>(ws + l.mask);
-  p.scand = reinterpret_cast<uint2*>(ws + l.cand);
-  p.srec = reinterpret_cast<uint32_t*>(ws + l.rec);
-  const dim3 grid(l.nch, p.rows);
-  // the rows' key ranges: the indexer's per-wave entries when it wrote
-  // keys with them, else one entry per chunk
-  const bool spans = p.span != nullptr && p.keys_in && p.span_kpw > 0 &&
-                     (p.L + p.span_kpw - 1) / p.span_kpw <= kSpanMax;
-  if (!spans) {
-    p.span = reinterpret_cast<const uint32_t*>(ws + l.span);
-    p.span_kpw = kSplitC;
-    hipLaunchKernelGGL(topk_span_kernel, grid, dim3(kSplitThreads), 0, stream, p);
+  // Rows past 64K positions: one workgroup per 16K-position chunk selects
+  // the chunk's Top-K (keys in registers), then one workgroup per row
+  // selects from the chunks' candidates.  Without the workspace for the
+  // candidate lists, one workgroup streams the whole row.
+  const int nch = topk_chunks(p0.L);
+  const size_t need = topk_workspace_bytes(p0.rows, p0.L, p0.K);
+  if (nch > 0 && workspace && workspace_bytes >= need) {
+    TopkLaunch p = p0;
+    p.nchunks = nch;
+    p.chunk = kChunkLen;
+    p.cand = static_cast<int32_t*>(workspace);
+    hipLaunchKernelGGL((topk_kernel<16, true, kChunk>), dim3(p.rows * nch),
+                       dim3(kThreads), 0, stream, p);
+    const int slots = nch * p.K;   // <= 8 * 2048
+    if (slots <= 4 * kThreads)
+      hipLaunchKernelGGL((topk_kernel<4, true, kGather>), dim3(p.rows),
+                         dim3(kThreads), 0, stream, p);
+    else
+      hipLaunchKernelGGL((topk_kernel<16, true, kGather>), dim3(p.rows),
+                         dim3(kThreads), 0, stream, p);
+    return hipGetLastError();
   }
-  hipLaunchKernelGGL(topk_hist_kernel, grid, dim3(kSplitThreads), 0, stream, p);
-  hipLaunchKernelGGL(topk_thresh_kernel, grid, dim3(kSplitThreads), 0, stream, p);
-  launch_by_length<kFinish>(p, stream);
-  return hipGetLastError();
+  return launch_topk(p0, stream);
 }
 
 hipError_t launch_topk(const TopkLaunch& p, hipStream_t stream) {
@@ -1052,7 +767,16 @@ hipError_t launch_topk(const TopkLaunch& p, hipStream_t stream) {
       launch_kpt<64, true, kRowSpan>(p, stream);
     return hipGetLastError();
   }
-  launch_by_length<kRow>(p, stream);
+  if (p.L <= 4 * kThreads)
+    launch_kpt<4, true>(p, stream);
+  else if (p.L <= 16 * kThreads)
+    launch_kpt<16, true>(p, stream);
+  else if (p.L <= 32 * kThreads)
+    launch_kpt<32, true>(p, stream);
+  else if (p.L <= 64 * kThreads)
+    launch_kpt<64, true>(p, stream);
+  else
+    launch_kpt<128, false>(p, stream);
   return hipGetLastError();
 }
 

@@ -311,15 +311,13 @@ def test_wide_logit_range(B, T, H, K, fmt):
 
 
 @pytest.mark.parametrize("case", ["few_values", "all_equal"])
-def test_decode_split_topk_ties(case):
+def test_decode_topk_heavy_ties(case):
     """Decode rows of 32768 positions whose scores take few distinct values,
-    through the decode step's split selection: with one indexer head
-    reading one key feature, the scores are w * max(0, k) (five values), so
-    the threshold digit holds thousands of equal keys (the finishing
-    workgroup resolves them from the list, ties to the lower position);
-    with all queries zero every score is 0 and the threshold digit holds
-    the whole row (more than the list takes: the finishing workgroup
-    selects from the whole row)."""
+    through the decode step (the Top-K takes each row's key range from the
+    indexer): with one indexer head reading one key feature, the scores are
+    w * max(0, k), five values, so the K-th largest score is shared by
+    thousands of positions and the lowest of them must be taken; with all
+    queries zero every score is 0 and the first K positions are taken."""
     wl = wk.scaled(W["decode"], B=3, top_k=2048, H=32, seed=41)
     q = np.zeros((wl.B, wl.T, wl.H_I, wl.d_I), dtype=np.float32)
     if case == "few_values":
