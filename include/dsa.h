@@ -195,6 +195,7 @@ dsa_status dsa_topk(int B, int T, int L, int K, const float* scores,
  *   kv_scale [B, L, 18] e8m0 (MX32), [B, L, 5] fp32 (T128); NULL for bf16
  *   idx      [B, T, K] int32        selected positions; -1 entries skipped;
  *                                   valid entries must lie in [0, L)
+ *   softmax_scale > 0, finite (else DSA_ERR_SHAPE)
  *   out      [B, T, H, 512] fp32    softmax-weighted sum of value rows
  *   lse      [B, T, H] fp32         natural-log sum of exp(scale * q.k);
  *                                   a row with no valid index gets out = 0,

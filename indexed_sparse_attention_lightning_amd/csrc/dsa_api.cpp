@@ -219,6 +219,8 @@ dsa_status dsa_sparse_mla_attn(int B, int T, int L, int H, int K,
   if (!q || !kv || !idx || !out || !lse)
     return fail(DSA_ERR_NULL, "dsa_sparse_mla_attn: NULL tensor pointer");
   if (dsa_status s = check_attn_dims(B, T, H, K)) return s;
+  if (!(softmax_scale > 0.f) || softmax_scale == __builtin_inff())
+    return fail(DSA_ERR_SHAPE, "softmax_scale must be positive and finite");
   if (L < 1) return fail(DSA_ERR_SHAPE, "L must be >= 1");
   if ((long long)B * L > 0x7fffffffLL)
     return fail(DSA_ERR_UNSUPPORTED, "B*L must fit in int32");
@@ -263,6 +265,8 @@ dsa_status decode_step_impl(int B, int T, int H_I, int d_I, int H, int K,
     return fail(DSA_ERR_NULL, "dsa_decode_step: NULL cache pointer");
   if (dsa_status s = check_indexer_dims(B, T, H_I, d_I)) return s;
   if (dsa_status s = check_attn_dims(B, T, H, K)) return s;
+  if (!(softmax_scale > 0.f) || softmax_scale == __builtin_inff())
+    return fail(DSA_ERR_SHAPE, "softmax_scale must be positive and finite");
   if (!q_pos && T != 1)
     return fail(DSA_ERR_NULL, "q_pos may be NULL only when T == 1");
   if (cache->page_size != DSA_PAGE_SIZE)

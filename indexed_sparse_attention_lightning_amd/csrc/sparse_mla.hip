@@ -47,6 +47,11 @@ constexpr int kQLdsSteps = kLatent / 16 - kQRegSteps;   // 9 in LDS
 constexpr int kQLdsStride = 2 * kQLdsSteps + 1; // uint4 per head (padded)
 constexpr int kQMaxSlot = 2 * kQLdsSteps;        // the padding slot: the
                                                 // head's largest logit
+// S^T accumulation chains of the bf16 and MX kernels: 3 and 4 chains (no
+// spills in bf16) measured the same as 2 (decode attention 45.2 vs 44.9 us
+// with the merge, prefill chunk 2.51 vs 2.51 ms): the chains' latency is not
+// what bounds the tile loop
+constexpr int kSChains = 2;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kRef = 64.0f;     // log2 headroom of the first-pass reference
@@ -409,17 +414,20 @@ __device__ __forceinline__ void compute_tile(const uint4* tile,
       return ks < kQRegSteps ? st.qb[ks < kQRegSteps ? ks : 0]
                              : qrow[(ks - kQRegSteps) * 2];
     };
-    // two independent accumulation chains (even / odd k-steps) and operands
-    // fetched three k-steps ahead keep the matrix core fed
+    // independent accumulation chains (k-step ks feeds chain ks % kChains;
+    // T128: two, even / odd) and operands fetched three k-steps ahead keep
+    // the matrix core fed
     constexpr int kS = kLatent / 16;   // 36 k-steps
     constexpr int kAhead = 3;
+    constexpr int kChains = T128 ? 2 : kSChains;
+    static_assert(kS % kChains == 0, "whole chains");
     uint4 aq[kAhead + 1], bq[kAhead + 1];
 #pragma unroll
     for (int i = 0; i < kAhead; ++i) {
       aq[i] = a_at(i);
       bq[i] = b_at(i);
     }
-    f32x16 acc1;
+    f32x16 accs[kChains - 1];   // chains 1.. (chain 0 is acc)
     uint4 ap, bp;   // T128: the even operands of a pair issued together
 #pragma unroll
     for (int ks = 0; ks < kS; ++ks) {
@@ -432,11 +440,12 @@ __device__ __forceinline__ void compute_tile(const uint4* tile,
       static_assert(kS / 4 == kDmaBf16, "one block per four k-steps");
       if ((ks & 3) == 2) loads.block(ks >> 2);
       const uint4 a = aq[ks % (kAhead + 1)], b = bq[ks % (kAhead + 1)];
-      f32x16& c = (ks & 1) ? acc1 : acc;
+      f32x16& c = (ks % kChains) ? accs[(ks % kChains) - 1] : acc;
       // T128: the first and last k-step pairs of each 128-feature tile
       const bool pair_first = T128 && ks >= 8 && (ks & 7) < 2;
       const bool pair_last = T128 && ((ks & 7) >= 6 || ks >= kS - 2);
       if (pair_first || pair_last) {
+        f32x16& acc1 = accs[0];
         if ((ks & 1) == 0) {
           ap = a;
           bp = b;
@@ -454,11 +463,11 @@ __device__ __forceinline__ void compute_tile(const uint4* tile,
             }
           }
         }
-      } else if (ks < 2) {
+      } else if (ks < kChains) {
         mfma32_vgpr_first(c, a, b);
-      } else if (T128 || ks + 2 < kS) {
+      } else if (T128 || ks + 1 < kS) {
         mfma32_vgpr(c, a, b);
-      } else {
+      } else {   // the last product: wait states before the VALU reads
         mfma32_vgpr_last(c, a, b);
       }
     }
@@ -466,27 +475,28 @@ __device__ __forceinline__ void compute_tile(const uint4* tile,
       float f[16];
       tile_factors(tmul, 4, h, f);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[r] = (acc[r] + acc1[r]) * f[r];
+      for (int r = 0; r < 16; ++r) acc[r] = (acc[r] + accs[0][r]) * f[r];
     } else {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[r] += acc1[r];
+      for (int k = 0; k < kChains - 1; ++k)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[r] += accs[k][r];
     }
   }
-  // ---- online softmax (lane: head n, rows 8(r/4) + 4h + r%4 of the tile)
-  if (vmask == 0xffffffffu) {   // every row of the tile is selected (uniform)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) acc[r] *= sl2;
-  } else {
+  // ---- online softmax (lane: head n, rows 8(r/4) + 4h + r%4 of the tile).
+  // The scale (> 0) is applied once to the max and folded into the exp2
+  // argument, fma(s, sl2, -m): masked rows are -inf before scaling.
+  if (vmask != 0xffffffffu) {   // some row of the tile is not selected
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int R = 8 * (r >> 2) + 4 * h + (r & 3);
-      acc[r] = ((vmask >> R) & 1u) ? acc[r] * sl2 : -__builtin_inff();
+      acc[r] = ((vmask >> R) & 1u) ? acc[r] : -__builtin_inff();
     }
   }
   float tmax = -__builtin_inff();
 #pragma unroll
   for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, acc[r]);
-  tmax = fmaxf(tmax, swap_halves(tmax));
+  tmax = fmaxf(tmax, swap_halves(tmax)) * sl2;
   // Per-head reference m (log2 units), fixed for the whole pass so that O
   // never needs rescaling (a rescale of the 256 accumulation registers
   // would cost the loop its register allocation): in the first pass, the
@@ -513,7 +523,7 @@ __device__ __forceinline__ void compute_tile(const uint4* tile,
     float* p = pr + 8 * kk;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      p[e] = __builtin_amdgcn_exp2f(acc[8 * kk + e] - mref);
+      p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(acc[8 * kk + e], sl2, -mref));
       st.l += p[e];
     }
     if constexpr (!T128)

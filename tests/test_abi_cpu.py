@@ -84,8 +84,13 @@ def test_sparse_mla_validation():
         a = dict(B=1, T=1, L=64, H=128, K=64, kd=0, ks=None, ws=None, wsb=0)
         a.update(kw)
         return lib.dsa_sparse_mla_attn(a["B"], a["T"], a["L"], a["H"], a["K"],
-                                       FAKE, FAKE, a["kd"], a["ks"], FAKE, 0.1,
+                                       FAKE, FAKE, a["kd"], a["ks"], FAKE,
+                                       a.get("scale", 0.1),
                                        FAKE, FAKE, a["ws"], a["wsb"], None)
+    assert f(scale=0.0) == SHAPE                # the softmax scale must be > 0
+    assert f(scale=-0.1) == SHAPE
+    assert f(scale=float("inf")) == SHAPE
+    assert f(scale=float("nan")) == SHAPE
     assert f(H=129) == UNSUP
     assert f(K=0) == UNSUP
     assert f(kd=1) == NULL
