@@ -29,6 +29,14 @@ __device__ __forceinline__ f32x16 mfma32(const uint4& a, const uint4& b,
       0);
 }
 
+// max(x, 0) as one integer max on the bit pattern: the same value as
+// fmaxf(x, 0) for every x that is not a NaN (negative values and -0 give
+// +0, +inf stays).  fmaxf on a matrix-core result costs two instructions
+// (the operand is first canonicalised for IEEE NaN rules).
+__device__ __forceinline__ float relu(float x) {
+  return __builtin_bit_cast(float, max(__builtin_bit_cast(int, x), 0));
+}
+
 // Value held by lane (l ^ 32): the two wave halves exchange registers.
 // (Only one of the instruction's two results is taken per lane: the
 // compiler treats the two results of a swap of a register with itself as
@@ -133,6 +141,17 @@ __device__ __forceinline__ uint32_t split_scale(uint32_t s_bits, float& m) {
   m = s_bits == 0 ? 1.0f : __builtin_bit_cast(float, s_bits) * 0x1p126f;
   return 0x00800000u;
 }
+
+// A raw buffer resource over `bytes` bytes at `base`: a load at an offset
+// past `bytes` returns zeros and makes no memory access.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t span_rsrc(const void* base,
+                                                         uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0,
+                                           (int)bytes, 0x00020000);
+}
+// Cache-policy operand of a buffer load that streams (non-temporal, as
+// ld16_stream below).
+constexpr int kBufStream = 2;
 
 // 128-bit non-temporal-hint-free global load / LDS access helpers.
 __device__ __forceinline__ uint4 ld16(const void* p) {

@@ -73,51 +73,67 @@ struct StageF8 {
 };
 
 // Past-the-end stages (a wave issues the same loads every step, so its last
-// steps load stages beyond its range, whose scores are dropped) read their
-// code or key bytes from `park` instead: the first mask + 1 bytes of the
-// wave's own query row, which the plain query loads left in L2.  Re-reading the last
-// real stage would go to HBM again, since the key stream's non-temporal
-// loads do not keep it in the caches.
-struct Park {
-  const uint8_t* at;   // nullptr: a real stage
-  int mask;            // a power of two minus one, within the query row
-};
+// steps load stages beyond its range, whose scores are dropped) load through
+// an empty buffer range: the loads return zeros and read no memory.
+// A stage's loads go through one buffer resource over its 32 key rows (the
+// rows of a stage are consecutive: stages are 32-aligned and pages hold 64
+// positions), so a lane's offset is the same every stage and the per-load
+// address arithmetic is a scalar base per stage; in the contiguous layout
+// the range stops at the cache's last row (the rows past it read zeros).
+template <int ROWB>
+__device__ __forceinline__ void stage_rows(const CacheView& kc, int b,
+                                           int kbase, bool parked,
+                                           const uint8_t*& base,
+                                           uint32_t& rows, int64_t& row0) {
+  rows = 0;
+  row0 = 0;
+  if (parked) {
+    base = kc.data;
+    return;
+  }
+  if (kc.page_table != nullptr) {
+    row0 = cache_row(kc.page_table, kc.max_pages, kc.num_pages, kc.L, b, kbase);
+    rows = kSub;
+  } else {
+    row0 = (int64_t)b * kc.L + kbase;
+    rows = (uint32_t)max(0, min(kSub, kc.L - kbase));
+  }
+  base = kc.data + row0 * ROWB;
+  // the resource must be wave-uniform (a divergent one costs a loop of
+  // single-value loads per instruction)
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  base = reinterpret_cast<const uint8_t*>(
+      ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(a >> 32)) << 32) |
+      (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a));
+  rows = (uint32_t)__builtin_amdgcn_readfirstlane((int)rows);
+}
 
 template <int DI>
 __device__ __forceinline__ void stage_load_f8(StageF8<DI>& st,
                                               const CacheView& kc, int b,
-                                              int kbase, int lane, Park park) {
+                                              int kbase, int lane,
+                                              bool parked) {
   using CL = CodeLayout<DI>;
   // wave-uniform: the page-table lookup is then a scalar load (a vector one
   // would be waited for with every key load in flight)
   b = __builtin_amdgcn_readfirstlane(b);
   kbase = __builtin_amdgcn_readfirstlane(kbase);
+  const uint8_t* base;
+  uint32_t rows;
   int64_t row0;
-  bool clamp = false;
-  if (kc.page_table != nullptr) {
-    row0 = cache_row(kc.page_table, kc.max_pages, kc.num_pages, kc.L, b, kbase);
-  } else {
-    row0 = (int64_t)b * kc.L + kbase;
-    clamp = kbase + kSub > kc.L;
-  }
+  stage_rows<DI>(kc, b, kbase, parked, base, rows, row0);
+  const auto codes = span_rsrc(base, rows * DI);
 #pragma unroll
-  for (int i = 0; i < CL::kLoads; ++i) {
-    const int id = i * kWave + lane;
-    const int n = id / CL::kChunks, c = id % CL::kChunks;
-    int64_t row = row0 + n;
-    if (clamp) row = (int64_t)b * kc.L + min(kbase + n, kc.L - 1);
-    st.v[i] = ld16_stream(park.at ? park.at + ((id * 16) & park.mask)
-                                  : kc.data + row * DI + c * 16);
-  }
-  {
-    const int n = lane & 31;
-    int64_t row = row0 + n;
-    if (clamp) row = (int64_t)b * kc.L + min(kbase + n, kc.L - 1);
-    if constexpr (DI == 128)
-      st.sc = *reinterpret_cast<const uint32_t*>(kc.scale + row * 4);
-    else
-      st.sc = *reinterpret_cast<const uint16_t*>(kc.scale + row * 2);
-  }
+  for (int i = 0; i < CL::kLoads; ++i)
+    st.v[i] = __builtin_bit_cast(
+        uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                   codes, (uint32_t)(i * kWave + lane) * 16, 0, kBufStream));
+  const auto scales = span_rsrc(kc.scale + row0 * (DI / 32), rows * (DI / 32));
+  const uint32_t n = lane & 31;
+  if constexpr (DI == 128)
+    st.sc = __builtin_amdgcn_raw_buffer_load_b32(scales, n * 4, 0, 0);
+  else
+    st.sc = __builtin_amdgcn_raw_buffer_load_b16(scales, n * 2, 0, 0);
 }
 
 // The codes go to the wave's LDS tile and the scale words to `scl` (one per
@@ -170,7 +186,7 @@ __device__ __forceinline__ float tile_scores_f8(const uint4* tile,
 #pragma unroll
   for (int m = 0; m < MB; ++m)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) s += wv[m][r] * fmaxf(acc[m][r], 0.f);
+    for (int r = 0; r < 16; ++r) s += wv[m][r] * relu(acc[m][r]);
   return s + swap_halves(s);
 }
 
@@ -180,69 +196,44 @@ __device__ __forceinline__ float out_val(const IndexerLaunch& p, float sc) {
   return p.keys_out ? __builtin_bit_cast(float, score_key(sc)) : sc + 0.0f;
 }
 
-// Registers holding one 32-key stage on its way from HBM to LDS.
-template <int DI, bool FP8>
+// Registers holding one 32-key bf16 stage on its way from HBM to LDS.
+template <int DI>
 struct Stage {
-  static constexpr int N = FP8 ? KeyLayout<DI>::kLoadsFp8
-                               : KeyLayout<DI>::kLoadsBf16;
+  static constexpr int N = KeyLayout<DI>::kLoadsBf16;
   uint4 v[N];
-  uint32_t sc[FP8 ? N : 1];
 };
 
-template <int DI, bool FP8>
-__device__ __forceinline__ void stage_load(Stage<DI, FP8>& st,
-                                           const CacheView& kc, int b,
-                                           int kbase, int lane, Park park) {
-  using KL = KeyLayout<DI>;
+template <int DI>
+__device__ __forceinline__ void stage_load(Stage<DI>& st, const CacheView& kc,
+                                           int b, int kbase, int lane,
+                                           bool parked) {
   // wave-uniform: the page-table lookup is then a scalar load (a vector one
   // would be waited for with every key load in flight)
   b = __builtin_amdgcn_readfirstlane(b);
   kbase = __builtin_amdgcn_readfirstlane(kbase);
-  // the 32 keys of a stage share one page (stages are 32-aligned, pages 64)
+  const uint8_t* base;
+  uint32_t rows;
   int64_t row0;
-  bool clamp = false;
-  if (kc.page_table != nullptr) {
-    row0 = cache_row(kc.page_table, kc.max_pages, kc.num_pages, kc.L, b, kbase);
-  } else {
-    row0 = (int64_t)b * kc.L + kbase;
-    clamp = kbase + kSub > kc.L;
-  }
+  stage_rows<DI * 2>(kc, b, kbase, parked, base, rows, row0);
+  const auto keys = span_rsrc(base, rows * (DI * 2));
+  // lane l of load i takes bytes 16*(64i + l) of the stage's rows:
+  // key (64i + l) / chunks, chunk (64i + l) % chunks
 #pragma unroll
-  for (int i = 0; i < Stage<DI, FP8>::N; ++i) {
-    const int id = i * kWave + lane;
-    if constexpr (!FP8) {
-      const int n = id / KL::kChunks, c = id % KL::kChunks;
-      int64_t row = row0 + n;
-      if (clamp) row = (int64_t)b * kc.L + min(kbase + n, kc.L - 1);
-      st.v[i] = ld16_stream(park.at ? park.at + ((id * 16) & park.mask)
-                                    : kc.data + row * (DI * 2) + c * 16);
-    } else {
-      const int n = id / KL::kCodeChunks, c = id % KL::kCodeChunks;
-      int64_t row = row0 + n;
-      if (clamp) row = (int64_t)b * kc.L + min(kbase + n, kc.L - 1);
-      st.v[i] = ld16(kc.data + row * DI + c * 16);
-      st.sc[i] = kc.scale[row * (DI / 32) + (c >> 1)];
-    }
-  }
+  for (int i = 0; i < Stage<DI>::N; ++i)
+    st.v[i] = __builtin_bit_cast(
+        uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                   keys, (uint32_t)(i * kWave + lane) * 16, 0, kBufStream));
 }
 
-template <int DI, bool FP8>
-__device__ __forceinline__ void stage_store(const Stage<DI, FP8>& st,
-                                            uint4* tile, int lane) {
+template <int DI>
+__device__ __forceinline__ void stage_store(const Stage<DI>& st, uint4* tile,
+                                            int lane) {
   using KL = KeyLayout<DI>;
 #pragma unroll
-  for (int i = 0; i < Stage<DI, FP8>::N; ++i) {
+  for (int i = 0; i < Stage<DI>::N; ++i) {
     const int id = i * kWave + lane;
-    if constexpr (!FP8) {
-      const int n = id / KL::kChunks, c = id % KL::kChunks;
-      tile[n * KL::kChunks + KL::slot(n, c)] = st.v[i];
-    } else {
-      const int n = id / KL::kCodeChunks, c = id % KL::kCodeChunks;
-      const uint4 lo = dequant8_e4m3(make_uint2(st.v[i].x, st.v[i].y), st.sc[i]);
-      const uint4 hi = dequant8_e4m3(make_uint2(st.v[i].z, st.v[i].w), st.sc[i]);
-      tile[n * KL::kChunks + KL::slot(n, 2 * c)] = lo;
-      tile[n * KL::kChunks + KL::slot(n, 2 * c + 1)] = hi;
-    }
+    const int n = id / KL::kChunks, c = id % KL::kChunks;
+    tile[n * KL::kChunks + KL::slot(n, c)] = st.v[i];
   }
 }
 
@@ -269,7 +260,7 @@ __device__ __forceinline__ float tile_scores(const uint4* tile,
 #pragma unroll
   for (int m = 0; m < MB; ++m)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) s += wv[m][r] * fmaxf(acc[m][r], 0.f);
+    for (int r = 0; r < 16; ++r) s += wv[m][r] * relu(acc[m][r]);
   return s + swap_halves(s);
 }
 
@@ -363,14 +354,9 @@ __global__ __launch_bounds__(256, 2) void indexer_stream_kernel(
 
   uint4* tile = lds[wave];
   uint32_t* scl = sscale[wave];
-  const int qbytes = p.H_I * DI * 2;
-  const Park parked{reinterpret_cast<const uint8_t*>(p.q_idx + qrow * p.H_I * DI),
-                    (1 << (31 - __builtin_clz(qbytes))) - 1};
-  const auto park_if = [&](int stage) {
-    return stage > nsub - 1 ? parked : Park{nullptr, 0};
-  };
+  const auto park_if = [&](int stage) { return stage > nsub - 1; };
   // Every iteration issues the same loads and stores (stages past the end
-  // read the parked query row and their scores are dropped), so the
+  // read zeros through an empty range and their scores are dropped), so the
   // compiler can count them and wait only for the stage it consumes.
   const int last = nsub - 1;
   float* sb = sbuf[wave];
@@ -411,20 +397,20 @@ __global__ __launch_bounds__(256, 2) void indexer_stream_kernel(
         flush(k0 + (i + 4) * kSub - kFlush, k0 + (i + 4) * kSub);
     }
   } else {
-    Stage<DI, FP8> s0, s1;
-    stage_load<DI, FP8>(s0, p.keys, b, k0, lane, park_if(0));
-    stage_load<DI, FP8>(s1, p.keys, b, k0 + min(1, last) * kSub, lane,
+    Stage<DI> s0, s1;
+    stage_load<DI>(s0, p.keys, b, k0, lane, park_if(0));
+    stage_load<DI>(s1, p.keys, b, k0 + min(1, last) * kSub, lane,
                         park_if(1));
     for (int i = 0; i < nsub; i += 2) {
-      stage_store<DI, FP8>(s0, tile, lane);
-      stage_load<DI, FP8>(s0, p.keys, b, k0 + min(i + 2, last) * kSub, lane,
+      stage_store<DI>(s0, tile, lane);
+      stage_load<DI>(s0, p.keys, b, k0 + min(i + 2, last) * kSub, lane,
                           park_if(i + 2));
       {
         const float sc = tile_scores<DI, MB>(tile, a, wv, lane);
         if (lane < 32) sb[(i * kSub + lane) % kFlush] = out_val(p, sc);
       }
-      stage_store<DI, FP8>(s1, tile, lane);
-      stage_load<DI, FP8>(s1, p.keys, b, k0 + min(i + 3, last) * kSub, lane,
+      stage_store<DI>(s1, tile, lane);
+      stage_load<DI>(s1, p.keys, b, k0 + min(i + 3, last) * kSub, lane,
                           park_if(i + 3));
       {
         const float sc = tile_scores<DI, MB>(tile, a, wv, lane);
@@ -594,7 +580,7 @@ __device__ __forceinline__ float scores_q8(const KeysQ8<DI>& st,
 #pragma unroll
   for (int m = 0; m < MB; ++m)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) s += wv[m][r] * fmaxf(acc[m][r], 0.f);
+    for (int r = 0; r < 16; ++r) s += wv[m][r] * relu(acc[m][r]);
   return s + swap_halves(s);
 }
 
@@ -941,7 +927,7 @@ __device__ __forceinline__ float tile_scores_q8(const uint4* tile,
 #pragma unroll
   for (int m = 0; m < MB; ++m)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) s += wv[m][r] * fmaxf(acc[m][r], 0.f);
+    for (int r = 0; r < 16; ++r) s += wv[m][r] * relu(acc[m][r]);
   return s + swap_halves(s);
 }
 
