@@ -194,6 +194,22 @@ __device__ __forceinline__ int64_t cache_row(const int32_t* page_table,
   return (int64_t)pg * kPage + (s & (kPage - 1));
 }
 
+// cache_row for a wave-uniform (b, s): the page-table entry is read through
+// the scalar cache (the table is read-only for a launch).  A plain load of a
+// uniform address becomes a vector load wherever a store precedes it in a
+// loop (the compiler cannot rule out aliasing), and waiting for that one
+// waits for every vector load in flight.
+__device__ __forceinline__ int64_t cache_row_uniform(const int32_t* page_table,
+                                                     int max_pages,
+                                                     int num_pages, int L,
+                                                     int b, int s) {
+  if (page_table == nullptr) return (int64_t)b * L + s;
+  typedef const __attribute__((address_space(4))) int32_t ConstI32;
+  int pg = ((ConstI32*)page_table)[(int64_t)b * max_pages + (s >> 6)];
+  if (num_pages > 0) pg = min(max(pg, 0), num_pages - 1);
+  return (int64_t)pg * kPage + (s & (kPage - 1));
+}
+
 // Order-preserving map float -> uint32: larger float <=> larger key.
 // -0 is folded onto +0 and every NaN onto key 1 (below all numbers, whose
 // keys start at 0x007fffff for -inf); key 0 is left free as a "no position"

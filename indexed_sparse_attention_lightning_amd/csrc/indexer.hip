@@ -92,7 +92,7 @@ __device__ __forceinline__ void stage_rows(const CacheView& kc, int b,
     return;
   }
   if (kc.page_table != nullptr) {
-    row0 = cache_row(kc.page_table, kc.max_pages, kc.num_pages, kc.L, b, kbase);
+    row0 = cache_row_uniform(kc.page_table, kc.max_pages, kc.num_pages, kc.L, b, kbase);
     rows = kSub;
   } else {
     row0 = (int64_t)b * kc.L + kbase;
@@ -472,7 +472,7 @@ __device__ __forceinline__ void keys_load_q8(KeysQ8<DI>& st,
   int64_t row;
   if (kc.page_table != nullptr) {
     // the 32 keys of a stage share one page (stages are 32-aligned, pages 64)
-    row = cache_row(kc.page_table, kc.max_pages, kc.num_pages, kc.L, b, kbase) + n;
+    row = cache_row_uniform(kc.page_table, kc.max_pages, kc.num_pages, kc.L, b, kbase) + n;
   } else {
     row = (int64_t)b * kc.L + min(kbase + n, kc.L - 1);
   }
@@ -718,10 +718,14 @@ __device__ __forceinline__ void tile_load(TileStage<DI, FP8>& st,
                                           const CacheView& kc, int b,
                                           int kbase, int tid) {
   using KL = KeyLayout<DI>;
+  // wave-uniform: the page-table lookup is then a scalar load (a vector one
+  // is waited for together with the other stage's key loads in flight)
+  b = __builtin_amdgcn_readfirstlane(b);
+  kbase = __builtin_amdgcn_readfirstlane(kbase);
   int64_t row0;
   bool clamp = false;
   if (kc.page_table != nullptr) {
-    row0 = cache_row(kc.page_table, kc.max_pages, kc.num_pages, kc.L, b, kbase);
+    row0 = cache_row_uniform(kc.page_table, kc.max_pages, kc.num_pages, kc.L, b, kbase);
   } else {
     row0 = (int64_t)b * kc.L + kbase;
     clamp = kbase + kStageKeys > kc.L;
@@ -853,10 +857,13 @@ __device__ __forceinline__ void tile_load_q8(TileStageQ8<DI>& st,
                                              const CacheView& kc, int b,
                                              int kbase, int tid) {
   using CL = CodeLayout<DI>;
+  // wave-uniform (a scalar page-table lookup, as in tile_load)
+  b = __builtin_amdgcn_readfirstlane(b);
+  kbase = __builtin_amdgcn_readfirstlane(kbase);
   int64_t row0;
   bool clamp = false;
   if (kc.page_table != nullptr) {
-    row0 = cache_row(kc.page_table, kc.max_pages, kc.num_pages, kc.L, b, kbase);
+    row0 = cache_row_uniform(kc.page_table, kc.max_pages, kc.num_pages, kc.L, b, kbase);
   } else {
     row0 = (int64_t)b * kc.L + kbase;
     clamp = kbase + kStageKeys > kc.L;
