@@ -13,13 +13,16 @@
 // cores (heads form the MFMA M dimension, keys the N dimension, the key
 // features the K dimension).  Per wave:
 //   * the query's q_I (all heads) sits in registers as MFMA A operands;
-//   * keys arrive in 32-key stages: coalesced 16-byte global loads into
-//     registers (two stages in flight), then a swizzled write into a
-//     wave-private LDS tile and MFMA-layout reads out of it (the transpose a
-//     row-major key cache needs; the XOR swizzle keeps both sides free of LDS
-//     bank conflicts);
-//   * FP8 keys are dequantised on the way into LDS (e4m3 x 2^(e8m0-127) is
-//     exact in bf16), so the MFMA path is the same for both cache formats;
+//   * keys arrive in 32-key stages: coalesced 16-byte buffer loads into
+//     registers (two bf16 stages in flight, four of FP8 codes), then a
+//     swizzled write into a wave-private LDS tile and MFMA-layout reads out
+//     of it (the transpose a row-major key cache needs; the XOR swizzle keeps
+//     both sides free of LDS bank conflicts);
+//   * FP8 keys go to LDS as codes and are dequantised when read as operands
+//     (e4m3 x 2^(e8m0-127) is exact in bf16), so the products are the bf16
+//     ones for both cache formats (the prefill tile kernel dequantises on the
+//     way into LDS instead; the quantised kernels further down feed the codes
+//     to the scaled FP8 matrix cores as they are);
 //   * the ReLU and head-weighted sum run on the accumulators, and the two wave
 //     halves combine with one cross-half swap.
 // Exactness: integer-valued bf16 inputs with power-of-two weights make every
