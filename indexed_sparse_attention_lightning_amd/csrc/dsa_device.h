@@ -144,8 +144,8 @@ __device__ __forceinline__ uint32_t split_scale(uint32_t s_bits, float& m) {
 
 // A raw buffer resource over `bytes` bytes at `base`: a load at an offset
 // past `bytes` returns zeros and makes no memory access.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t span_rsrc(const void* base,
-                                                         uint32_t bytes) {
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t bytes_rsrc(const void* base,
+                                                          uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0,
                                            (int)bytes, 0x00020000);
 }

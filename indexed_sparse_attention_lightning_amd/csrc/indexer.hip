@@ -125,13 +125,13 @@ __device__ __forceinline__ void stage_load_f8(StageF8<DI>& st,
   uint32_t rows;
   int64_t row0;
   stage_rows<DI>(kc, b, kbase, parked, base, rows, row0);
-  const auto codes = span_rsrc(base, rows * DI);
+  const auto codes = bytes_rsrc(base, rows * DI);
 #pragma unroll
   for (int i = 0; i < CL::kLoads; ++i)
     st.v[i] = __builtin_bit_cast(
         uint4, __builtin_amdgcn_raw_buffer_load_b128(
                    codes, (uint32_t)(i * kWave + lane) * 16, 0, kBufStream));
-  const auto scales = span_rsrc(kc.scale + row0 * (DI / 32), rows * (DI / 32));
+  const auto scales = bytes_rsrc(kc.scale + row0 * (DI / 32), rows * (DI / 32));
   const uint32_t n = lane & 31;
   if constexpr (DI == 128)
     st.sc = __builtin_amdgcn_raw_buffer_load_b32(scales, n * 4, 0, 0);
@@ -218,7 +218,7 @@ __device__ __forceinline__ void stage_load(Stage<DI>& st, const CacheView& kc,
   uint32_t rows;
   int64_t row0;
   stage_rows<DI * 2>(kc, b, kbase, parked, base, rows, row0);
-  const auto keys = span_rsrc(base, rows * (DI * 2));
+  const auto keys = bytes_rsrc(base, rows * (DI * 2));
   // lane l of load i takes bytes 16*(64i + l) of the stage's rows:
   // key (64i + l) / chunks, chunk (64i + l) % chunks
 #pragma unroll
@@ -372,10 +372,8 @@ __global__ __launch_bounds__(256, 2) void indexer_stream_kernel(
     for (int s = from + lane; s < to; s += kWave) {
       const float v = sb[(s - k0) % kFlush];
       srow[s] = v;
-      if constexpr (!FP8) {   // (the FP8 kernel keeps no ranges: no registers)
-        kmn = min(kmn, __builtin_bit_cast(uint32_t, v));
-        kmx = max(kmx, __builtin_bit_cast(uint32_t, v));
-      }
+      kmn = min(kmn, __builtin_bit_cast(uint32_t, v));
+      kmx = max(kmx, __builtin_bit_cast(uint32_t, v));
     }
   };
   if constexpr (FP8) {
@@ -425,7 +423,7 @@ __global__ __launch_bounds__(256, 2) void indexer_stream_kernel(
   }
   const int done = (nsub - 1) / (kFlush / kSub) * kFlush;   // flushed so far
   flush(k0 + done, kend);
-  if (!FP8 && p.span) span_store(p.span, qrow, k0 / kpw, kmn, kmx, lane);
+  if (p.span) span_store(p.span, qrow, k0 / kpw, kmn, kmx, lane);
 }
 
 // ------------------------------------------------ quantised indexer (MX32)
@@ -1116,9 +1114,7 @@ hipError_t launch_indexer(const IndexerLaunch& p, hipStream_t stream) {
 }
 
 int indexer_span_kpw(const IndexerLaunch& p) {
-  // the FP8 stream kernel (MX keys, bf16 queries) keeps no key ranges
-  const bool fp8_stream = p.keys.fp8 && !p.q8;
-  return p.T >= kTileQ || fp8_stream ? 0 : stream_kpw(p);
+  return p.T >= kTileQ ? 0 : stream_kpw(p);
 }
 
 }  // namespace dsa
