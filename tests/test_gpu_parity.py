@@ -54,6 +54,14 @@ SMALL = {
     # causal skipping of whole stages, rows shorter than K
     "prefill_from_start": wk.scaled(W["prefill"], T=130, L=640, first_pos=0,
                                     top_k=64, H=16, seed=109),
+    # query-tiled indexer over scattered pages (its per-stage page lookups)
+    "prefill_paged_scattered": wk.scaled(W["prefill"], T=24, L=1500,
+                                         first_pos=1300, top_k=256, H=32,
+                                         paged_random=True, seed=112),
+    "prefill_paged_scattered_fp8": wk.scaled(W["prefill"], T=21, L=1300,
+                                             first_pos=1100, top_k=200, H=16,
+                                             quantized=True,
+                                             paged_random=True, seed=113),
 }
 
 
