@@ -57,6 +57,9 @@ struct alignas(16) TopkShared {
   uint32_t overflow;
 };
 
+// Unsigned compare predicates of __builtin_amdgcn_uicmpl (LLVM's ICmp codes).
+constexpr int kCmpUgt = 34, kCmpUge = 35, kCmpUle = 37;
+
 template <int CTRL>
 __device__ __forceinline__ uint32_t dpp(uint32_t x) {
   return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, 0xf, 0xf,
@@ -517,9 +520,11 @@ __global__ __launch_bounds__(kThreads, 1) void topk_kernel(TopkLaunch p) {
 #pragma unroll
   for (int i = 0; i < kMaskRegs; ++i) gwr[i] = ewr[i] = 0u;
   const auto sweep = [&](int j, uint32_t rk) {
-    const bool in = rk >= blo1 && rk <= bhi;
-    const uint64_t g = __ballot(rk > bhi);
-    const uint64_t c = __ballot(in);
+    // lane masks straight from the compares (a ballot of a flag is lowered
+    // through a vector register: two more instructions every step)
+    const uint64_t g = __builtin_amdgcn_uicmpl(rk, bhi, kCmpUgt);
+    const uint64_t c = __builtin_amdgcn_uicmpl(rk, blo1, kCmpUge) &
+                       __builtin_amdgcn_uicmpl(rk, bhi, kCmpUle);
     if constexpr (RES) {
       const int i0 = (2 * j) / kWave, l0 = (2 * j) % kWave;
       gwr[i0] = writelane(gwr[i0], (uint32_t)g, l0);
@@ -539,9 +544,9 @@ __global__ __launch_bounds__(kThreads, 1) void topk_kernel(TopkLaunch p) {
         }
       }
     }
-    if (nsh != 0 && c != 0ull) {
+    if (nsh != 0 && c != 0ull) {   // (the digit test again: rarely taken)
       const uint32_t at = ns + lanes_below(c);
-      if (in && at < (uint32_t)kSlab)
+      if (rk >= blo1 && rk <= bhi && at < (uint32_t)kSlab)
         sm.slab[wave][at] = make_uint2((uint32_t)keys.pos(j), rk);
       ns += __builtin_popcountll(c);
     }
