@@ -521,10 +521,18 @@ __global__ __launch_bounds__(kThreads, 1) void topk_kernel(TopkLaunch p) {
   for (int i = 0; i < kMaskRegs; ++i) gwr[i] = ewr[i] = 0u;
   const auto sweep = [&](int j, uint32_t rk) {
     // lane masks straight from the compares (a ballot of a flag is lowered
-    // through a vector register: two more instructions every step)
-    const uint64_t g = __builtin_amdgcn_uicmpl(rk, bhi, kCmpUgt);
-    const uint64_t c = __builtin_amdgcn_uicmpl(rk, blo1, kCmpUge) &
-                       __builtin_amdgcn_uicmpl(rk, bhi, kCmpUle);
+    // through a vector register: two more instructions every step); the
+    // 64-step kernel, short of registers, spills more with them and keeps
+    // the ballots
+    uint64_t g, c;
+    if constexpr (KPT <= 32) {
+      g = __builtin_amdgcn_uicmpl(rk, bhi, kCmpUgt);
+      c = __builtin_amdgcn_uicmpl(rk, blo1, kCmpUge) &
+          __builtin_amdgcn_uicmpl(rk, bhi, kCmpUle);
+    } else {
+      g = __ballot(rk > bhi);
+      c = __ballot(rk >= blo1 && rk <= bhi);
+    }
     if constexpr (RES) {
       const int i0 = (2 * j) / kWave, l0 = (2 * j) % kWave;
       gwr[i0] = writelane(gwr[i0], (uint32_t)g, l0);
