@@ -41,7 +41,6 @@ constexpr int kTileSlots = kRowsT * kSlotsRow;  // 2304
 constexpr int kCodeSegs = 20;                   // 18 code blocks + 2 dummies
 constexpr int kStageSlots = kCodeSegs * kWave;  // 1280
 constexpr int kMaxSplitRows = 2048;
-constexpr int kStageRow = kValue + 16;   // staged half partial row (bytes)
 constexpr int kQRegSteps = 27;                  // Q k-steps kept in registers
 constexpr int kQLdsSteps = kLatent / 16 - kQRegSteps;   // 9 in LDS
 constexpr int kQLdsStride = 2 * kQLdsSteps + 1; // uint4 per head (padded)
@@ -608,9 +607,6 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_kernel(
   __shared__ uint4 qlds[128 * kQLdsStride];
   __shared__ float tmul[T128 ? kTmulRows * 32 : 1];
   __shared__ int redo;   // some head needs the second softmax pass
-  static_assert(32 * kStageRow <= kBufSlots * 16 &&
-                    32 * kStageRow <= (FP8 ? kTileSlots : 128 * kQLdsStride) * 16,
-                "epilogue staging regions");
 
   const int tid = threadIdx.x, lane = lane_id();
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
@@ -850,49 +846,31 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_kernel(
           ltot > 0.f ? (st.m + __builtin_log2f(ltot)) * kLn2 : -__builtin_inff();
   } else {
     // partial of this split: O / l in bf16 (relative rounding 2^-9, well
-    // inside the output tolerance) plus (m, l) in fp32
-    // The wave's 32 rows go through LDS, half a row (256 values) at a time,
-    // so that each store writes whole 512-byte row halves.  Staged rows are
-    // kStageRow bytes apart; rows 16..31 swap the 8-byte halves of every 16
-    // bytes, so the 32 lanes of a write cycle (one column of rows 0..31) hit
-    // distinct banks.  Each wave stages in a buffer of its own.
-    barrier(true);   // every wave is done reading the tiles and Q
-    char* const stg = reinterpret_cast<char*>(
-        wave == 0 ? buf0 : wave == 1 ? buf1 : wave == 2 ? buf2 : (FP8 ? ftile : qlds));
+    // inside the output tolerance) plus (m, l) in fp32.  The values stay in
+    // the accumulator layout: lane (n, h2) writes its 16 values of value
+    // block t as two 16-byte pieces, piece q = rows 8q..8q+7, at slot
+    // (t, q, lane) of the wave's 32-head block, so every store instruction
+    // writes 1 KB contiguous and no LDS staging or barrier is needed; the
+    // combine reads the same layout.  Head blocks are 32 heads (padded).
+    const int Hp = (p.H + 31) & ~31;
     const float inv = ltot > 0.f ? 1.0f / ltot : 0.f;
-    const int64_t slot0 = ((int64_t)s.token * gridDim.x + split) * p.H + wave * 32;
-    uint16_t* const o0 = reinterpret_cast<uint16_t*>(p.partial) + slot0 * kValue;
-    const int rr = lane2 >> 5;   // row of the pair a read instruction covers
+    const int64_t slot0 = ((int64_t)s.token * gridDim.x + split) * Hp + wave * 32;
+    uint4* const o0 = reinterpret_cast<uint4*>(
+        reinterpret_cast<uint16_t*>(p.partial) + slot0 * kValue);
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      {
-        char* const wr = stg + n2 * kStageRow;
-        const int sx = (n2 >> 4) << 3;
+    for (int t = 0; t < kValue / 32; ++t)
 #pragma unroll
-        for (int t = 0; t < kValue / 64; ++t)
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const f32x16& ot = st.o[half * (kValue / 64) + t];
-            *reinterpret_cast<uint2*>(wr + (((32 * t + 8 * g + dvb) * 2) ^ sx)) =
-                make_uint2(pack_bf16x2(ot[4 * g] * inv, ot[4 * g + 1] * inv),
-                           pack_bf16x2(ot[4 * g + 2] * inv, ot[4 * g + 3] * inv));
-          }
+      for (int q = 0; q < 2; ++q) {
+        const f32x16& ot = st.o[t];
+        st16_stream(o0 + (t * 2 + q) * kWave + lane2,
+                    make_uint4(pack_bf16x2(ot[8 * q] * inv, ot[8 * q + 1] * inv),
+                               pack_bf16x2(ot[8 * q + 2] * inv, ot[8 * q + 3] * inv),
+                               pack_bf16x2(ot[8 * q + 4] * inv, ot[8 * q + 5] * inv),
+                               pack_bf16x2(ot[8 * q + 6] * inv, ot[8 * q + 7] * inv)));
       }
-#pragma unroll 4
-      for (int r0 = 0; r0 < 32; r0 += 2) {
-        const int r = r0 + rr;
-        uint4 v = *reinterpret_cast<const uint4*>(stg + r * kStageRow + (lane2 & 31) * 16);
-        if (r >= 16) v = make_uint4(v.z, v.w, v.x, v.y);
-        if (wave * 32 + r < p.H)
-          st16_stream(o0 + (int64_t)r * kValue + half * (kValue / 2) + (lane2 & 31) * 8,
-                      v);
-      }
-      // a wave's LDS accesses run in order: the second half may overwrite
-      // the first once its reads are issued
-    }
     const int64_t slot = slot0 + n2;
     if (h2 == 0 && head2 < p.H) {
-      const int64_t nslots = (int64_t)gridDim.y * gridDim.x * p.H;
+      const int64_t nslots = (int64_t)gridDim.y * gridDim.x * Hp;
       float* ml = reinterpret_cast<float*>(
                       reinterpret_cast<uint16_t*>(p.partial) + nslots * kValue) +
                   2 * slot;
@@ -904,65 +882,88 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_kernel(
 }
 
 // Merge split partials (written and read non-temporal: each is touched once
-// per step; 41.6-42.0 us against 42.9-43.0 us for the attention and the
-// merge together).  Split s carries O_s / l_s and its log2-sum-exp
+// per step).  Split s carries O_s / l_s and its log2-sum-exp
 // g_s = m_s + log2(l_s); with G the largest g_s, out = sum_s w_s * (O_s / l_s)
 // / sum_s w_s, w_s = 2^(g_s - G) in (0, 1], and lse = ln 2 * (G +
 // log2(sum_s w_s)).  The split with the largest sum weighs exactly 1, so no
 // split that matters can underflow, however far apart the splits' softmax
-// references are.  One wave per (token, head), kCombHeads heads per
-// workgroup; a lane merges 8 consecutive values (16-byte loads).  Every
-// load of a lane (all splits' g, then all splits' partial values) is issued
+// references are.  The partials are in the attention kernel's accumulator
+// layout; one wave merges value block t of a 32-head group of a token, lane
+// (n, h) the 16 values of head 32g + n at features 32t + 8(r/4) + 4h + r%4,
+// r = 0..15, each split's two 16-byte pieces read as 1 KB per instruction.
+// Every load of a lane (all splits' g, then all splits' pieces) is issued
 // before any is used, so the splits' latencies overlap.
 constexpr int kMaxSplits = 16;
-constexpr int kCombHeads = 4;
-__global__ __launch_bounds__(64 * kCombHeads) void combine_kernel(AttnLaunch p,
-                                                                  int splits) {
-  const int token = blockIdx.x;
-  const int head = blockIdx.y * kCombHeads + (int)(threadIdx.x / 64);
-  if (head >= p.H) return;
-  const int dv = (threadIdx.x & 63) * 8;
-  const int64_t nslots = (int64_t)gridDim.x * splits * p.H;
+constexpr int kCombBlocks = 4;   // value blocks (waves) per workgroup
+// MAXS: the split count bound the registers are sized for (8 covers the
+// decode batches and keeps twice the waves resident)
+template <int MAXS>
+__global__ __launch_bounds__(64 * kCombBlocks) void combine_kernel(AttnLaunch p,
+                                                                   int splits) {
+  const int token = blockIdx.x, grp = blockIdx.y;
+  const int wave = (int)(threadIdx.x / 64), lane = (int)(threadIdx.x & 63);
+  const int t = blockIdx.z * kCombBlocks + wave;   // value block
+  const int n = lane & 31, h = lane >> 5;
+  const int head = grp * 32 + n;
+  const int Hp = (p.H + 31) & ~31;
+  const int64_t nslots = (int64_t)gridDim.x * splits * Hp;
   const uint16_t* po = reinterpret_cast<const uint16_t*>(p.partial);
   const float* ml = reinterpret_cast<const float*>(po + nslots * kValue);
-  const int64_t slot0 = (int64_t)token * splits * p.H + head;
-  float g[kMaxSplits];
+  // slot of (token, split 0, first head of the group)
+  const int64_t slot0 = (int64_t)token * splits * Hp + grp * 32;
+  const bool live = head < p.H;
+  float g[MAXS];
 #pragma unroll
-  for (int sp = 0; sp < kMaxSplits; ++sp)
-    g[sp] = sp < splits ? ml[2 * (slot0 + (int64_t)sp * p.H)] : -__builtin_inff();
-  uint4 v[kMaxSplits];
+  for (int sp = 0; sp < MAXS; ++sp)
+    g[sp] = sp < splits && live ? ml[2 * (slot0 + (int64_t)sp * Hp + n)]
+                                : -__builtin_inff();
+  uint4 v[MAXS][2];
 #pragma unroll
-  for (int sp = 0; sp < kMaxSplits; ++sp)
-    v[sp] = sp < splits
-                ? ld16_stream(po + (slot0 + (int64_t)sp * p.H) * kValue + dv)
-                : make_uint4(0u, 0u, 0u, 0u);
+  for (int sp = 0; sp < MAXS; ++sp) {
+    const uint4* blk = reinterpret_cast<const uint4*>(
+        po + (slot0 + (int64_t)sp * Hp) * kValue);
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+      v[sp][q] = sp < splits ? ld16_stream(blk + (t * 2 + q) * kWave + lane)
+                             : make_uint4(0u, 0u, 0u, 0u);
+  }
   float G = -__builtin_inff();
 #pragma unroll
-  for (int sp = 0; sp < kMaxSplits; ++sp)
+  for (int sp = 0; sp < MAXS; ++sp)
     G = (g[sp] != g[sp] || G != G) ? __builtin_nanf("") : fmaxf(G, g[sp]);
   float wsum = 0.f;
-  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  float acc[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) acc[r] = 0.f;
   if (G != -__builtin_inff() && G == G) {
 #pragma unroll
-    for (int sp = 0; sp < kMaxSplits; ++sp) {
+    for (int sp = 0; sp < MAXS; ++sp) {
       // splits without rows (g = -inf) or beyond `splits` weigh nothing
       const float f = g[sp] == -__builtin_inff() ? 0.f : exp2f(g[sp] - G);
       wsum += f;
       if (f > 0.f) {   // a skipped split's values are never read
-        const uint32_t w[4] = {v[sp].x, v[sp].y, v[sp].z, v[sp].w};
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          acc[2 * i] += f * __builtin_bit_cast(float, w[i] << 16);
-          acc[2 * i + 1] += f * __builtin_bit_cast(float, w[i] & 0xffff0000u);
+        for (int q = 0; q < 2; ++q) {
+          const uint32_t w[4] = {v[sp][q].x, v[sp][q].y, v[sp][q].z, v[sp][q].w};
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            acc[8 * q + 2 * i] += f * __builtin_bit_cast(float, w[i] << 16);
+            acc[8 * q + 2 * i + 1] +=
+                f * __builtin_bit_cast(float, w[i] & 0xffff0000u);
+          }
         }
       }
     }
   }
+  if (!live) return;
   const float inv = wsum > 0.f ? 1.0f / wsum : 0.f;
-  float4* o = reinterpret_cast<float4*>(p.out + ((int64_t)token * p.H + head) * kValue + dv);
-  o[0] = make_float4(acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv);
-  o[1] = make_float4(acc[4] * inv, acc[5] * inv, acc[6] * inv, acc[7] * inv);
-  if ((threadIdx.x & 63) == 0)
+  float* o = p.out + ((int64_t)token * p.H + head) * kValue + 32 * t + 4 * h;
+#pragma unroll
+  for (int r4 = 0; r4 < 4; ++r4)
+    *reinterpret_cast<float4*>(o + 8 * r4) =
+        make_float4(acc[4 * r4] * inv, acc[4 * r4 + 1] * inv,
+                    acc[4 * r4 + 2] * inv, acc[4 * r4 + 3] * inv);
+  if (t == 0 && h == 0)
     p.lse[(int64_t)token * p.H + head] =
         G != G ? G
                : (wsum > 0.f ? (G + __builtin_log2f(wsum)) * kLn2
@@ -983,7 +984,8 @@ int attn_splits(int tokens, int K) {
 size_t attn_workspace_bytes(int tokens, int H, int K) {
   const int s = attn_splits(tokens, K);
   if (s <= 1) return 0;
-  return (size_t)tokens * s * H * (kValue * sizeof(uint16_t) + 2 * sizeof(float));
+  const int Hp = (H + 31) & ~31;   // partials in whole 32-head blocks
+  return (size_t)tokens * s * Hp * (kValue * sizeof(uint16_t) + 2 * sizeof(float));
 }
 
 hipError_t launch_sparse_mla(const AttnLaunch& p, hipStream_t stream) {
@@ -1011,9 +1013,13 @@ hipError_t launch_sparse_mla(const AttnLaunch& p, hipStream_t stream) {
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || used == 1) return e;
-  hipLaunchKernelGGL(combine_kernel,
-                     dim3(tokens, (p.H + kCombHeads - 1) / kCombHeads),
-                     dim3(64 * kCombHeads), 0, stream, p, used);
+  const dim3 cgrid(tokens, (p.H + 31) / 32, kValue / 32 / kCombBlocks);
+  if (used <= 8)
+    hipLaunchKernelGGL(combine_kernel<8>, cgrid, dim3(64 * kCombBlocks), 0,
+                       stream, p, used);
+  else
+    hipLaunchKernelGGL(combine_kernel<kMaxSplits>, cgrid,
+                       dim3(64 * kCombBlocks), 0, stream, p, used);
   return hipGetLastError();
 }
 
