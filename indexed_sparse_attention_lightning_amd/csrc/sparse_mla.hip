@@ -607,6 +607,10 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_kernel(
   __shared__ uint4 qlds[128 * kQLdsStride];
   __shared__ float tmul[T128 ? kTmulRows * 32 : 1];
   __shared__ int redo;   // some head needs the second softmax pass
+  static_assert(32 * (128 * 4 + 16) <= kBufSlots * 16 &&
+                    32 * (128 * 4 + 16) <=
+                        (FP8 ? kTileSlots : 128 * kQLdsStride) * 16,
+                "epilogue staging regions");
 
   const int tid = threadIdx.x, lane = lane_id();
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
@@ -831,17 +835,41 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_kernel(
   const float ltot = st.l + swap_halves(st.l, lane2);
   const int dvb = 4 * h2;   // first of this lane2's 4 consecutive dv per group
   if (gridDim.x == 1) {
-    if (head2 >= p.H) return;
+    // The output rows (fp32) go through LDS a quarter (128 values) at a
+    // time, so that every store instruction writes two heads' 512-byte row
+    // quarters, whole cache lines (straight from the accumulator layout a
+    // store wrote 32 bytes of each of 32 rows).  Each wave stages in a
+    // buffer of its own, rows 16 bytes apart beyond their length.
+    barrier(true);   // every wave is done reading the tiles and Q
+    char* const stg = reinterpret_cast<char*>(
+        wave == 0 ? buf0 : wave == 1 ? buf1 : wave == 2 ? buf2 : (FP8 ? ftile : qlds));
+    constexpr int kRowQ = 128 * 4 + 16;   // staged row quarter (bytes)
     const float inv = ltot > 0.f ? 1.0f / ltot : 0.f;
-    float* o = p.out + ((int64_t)s.token * p.H + head2) * kValue;
+    float* const o0 = p.out + ((int64_t)s.token * p.H + wave * 32) * kValue;
 #pragma unroll
-    for (int t = 0; t < kValue / 32; ++t)
+    for (int k = 0; k < 4; ++k) {
 #pragma unroll
-      for (int g = 0; g < 4; ++g)
-        *reinterpret_cast<float4*>(o + 32 * t + 8 * g + dvb) =
-            make_float4(st.o[t][4 * g] * inv, st.o[t][4 * g + 1] * inv,
-                        st.o[t][4 * g + 2] * inv, st.o[t][4 * g + 3] * inv);
-    if (h2 == 0)
+      for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const f32x16& ot = st.o[4 * k + tt];
+          *reinterpret_cast<float4*>(stg + n2 * kRowQ + (32 * tt + 8 * g + dvb) * 4) =
+              make_float4(ot[4 * g] * inv, ot[4 * g + 1] * inv,
+                          ot[4 * g + 2] * inv, ot[4 * g + 3] * inv);
+        }
+      // a wave's LDS accesses run in order: the next quarter may overwrite
+      // this one once its reads are issued
+#pragma unroll 4
+      for (int i = 0; i < 16; ++i) {
+        const int r = 2 * i + (lane2 >> 5);
+        const float4 v =
+            *reinterpret_cast<const float4*>(stg + r * kRowQ + (lane2 & 31) * 16);
+        if (wave * 32 + r < p.H)
+          *reinterpret_cast<float4*>(o0 + (int64_t)r * kValue + 128 * k +
+                                     (lane2 & 31) * 4) = v;
+      }
+    }
+    if (h2 == 0 && head2 < p.H)
       p.lse[(int64_t)s.token * p.H + head2] =
           ltot > 0.f ? (st.m + __builtin_log2f(ltot)) * kLn2 : -__builtin_inff();
   } else {
