@@ -922,15 +922,18 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_kernel(
 // Every load of a lane (all splits' g, then all splits' pieces) is issued
 // before any is used, so the splits' latencies overlap.
 constexpr int kMaxSplits = 16;
-constexpr int kCombBlocks = 4;   // value blocks (waves) per workgroup
-// MAXS: the split count bound the registers are sized for (8 covers the
-// decode batches and keeps twice the waves resident)
-template <int MAXS>
-__global__ __launch_bounds__(64 * kCombBlocks) void combine_kernel(AttnLaunch p,
-                                                                   int splits) {
+constexpr int kCombWaves = 4;   // waves per workgroup
+// MAXS: the split count bound the registers are sized for; QPL: 16-byte
+// pieces per lane (2: a wave merges a whole value block of its 32 heads;
+// 1: half of one, twice the waves -- for many splits over few tokens)
+template <int MAXS, int QPL>
+__global__ __launch_bounds__(64 * kCombWaves) void combine_kernel(AttnLaunch p,
+                                                                  int splits) {
   const int token = blockIdx.x, grp = blockIdx.y;
   const int wave = (int)(threadIdx.x / 64), lane = (int)(threadIdx.x & 63);
-  const int t = blockIdx.z * kCombBlocks + wave;   // value block
+  const int unit = blockIdx.z * kCombWaves + wave;   // (block, piece) unit
+  const int t = unit / (2 / QPL);                    // value block
+  const int q0 = (unit % (2 / QPL)) * QPL;           // first piece
   const int n = lane & 31, h = lane >> 5;
   const int head = grp * 32 + n;
   const int Hp = (p.H + 31) & ~31;
@@ -945,14 +948,14 @@ __global__ __launch_bounds__(64 * kCombBlocks) void combine_kernel(AttnLaunch p,
   for (int sp = 0; sp < MAXS; ++sp)
     g[sp] = sp < splits && live ? ml[2 * (slot0 + (int64_t)sp * Hp + n)]
                                 : -__builtin_inff();
-  uint4 v[MAXS][2];
+  uint4 v[MAXS][QPL];
 #pragma unroll
   for (int sp = 0; sp < MAXS; ++sp) {
     const uint4* blk = reinterpret_cast<const uint4*>(
         po + (slot0 + (int64_t)sp * Hp) * kValue);
 #pragma unroll
-    for (int q = 0; q < 2; ++q)
-      v[sp][q] = sp < splits ? ld16_stream(blk + (t * 2 + q) * kWave + lane)
+    for (int q = 0; q < QPL; ++q)
+      v[sp][q] = sp < splits ? ld16_stream(blk + (t * 2 + q0 + q) * kWave + lane)
                              : make_uint4(0u, 0u, 0u, 0u);
   }
   float G = -__builtin_inff();
@@ -960,9 +963,9 @@ __global__ __launch_bounds__(64 * kCombBlocks) void combine_kernel(AttnLaunch p,
   for (int sp = 0; sp < MAXS; ++sp)
     G = (g[sp] != g[sp] || G != G) ? __builtin_nanf("") : fmaxf(G, g[sp]);
   float wsum = 0.f;
-  float acc[16];
+  float acc[8 * QPL];
 #pragma unroll
-  for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+  for (int r = 0; r < 8 * QPL; ++r) acc[r] = 0.f;
   if (G != -__builtin_inff() && G == G) {
 #pragma unroll
     for (int sp = 0; sp < MAXS; ++sp) {
@@ -971,7 +974,7 @@ __global__ __launch_bounds__(64 * kCombBlocks) void combine_kernel(AttnLaunch p,
       wsum += f;
       if (f > 0.f) {   // a skipped split's values are never read
 #pragma unroll
-        for (int q = 0; q < 2; ++q) {
+        for (int q = 0; q < QPL; ++q) {
           const uint32_t w[4] = {v[sp][q].x, v[sp][q].y, v[sp][q].z, v[sp][q].w};
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
@@ -985,13 +988,17 @@ __global__ __launch_bounds__(64 * kCombBlocks) void combine_kernel(AttnLaunch p,
   }
   if (!live) return;
   const float inv = wsum > 0.f ? 1.0f / wsum : 0.f;
+  // piece q holds accumulator rows 8q..8q+7: features 32t + 8(2q + j) + 4h
+  // + 0..3 for j = 0, 1
   float* o = p.out + ((int64_t)token * p.H + head) * kValue + 32 * t + 4 * h;
 #pragma unroll
-  for (int r4 = 0; r4 < 4; ++r4)
-    *reinterpret_cast<float4*>(o + 8 * r4) =
-        make_float4(acc[4 * r4] * inv, acc[4 * r4 + 1] * inv,
-                    acc[4 * r4 + 2] * inv, acc[4 * r4 + 3] * inv);
-  if (t == 0 && h == 0)
+  for (int q = 0; q < QPL; ++q)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+      *reinterpret_cast<float4*>(o + 8 * (2 * (q0 + q) + j)) =
+          make_float4(acc[8 * q + 4 * j] * inv, acc[8 * q + 4 * j + 1] * inv,
+                      acc[8 * q + 4 * j + 2] * inv, acc[8 * q + 4 * j + 3] * inv);
+  if (t == 0 && q0 == 0 && h == 0)
     p.lse[(int64_t)token * p.H + head] =
         G != G ? G
                : (wsum > 0.f ? (G + __builtin_log2f(wsum)) * kLn2
@@ -1041,13 +1048,16 @@ hipError_t launch_sparse_mla(const AttnLaunch& p, hipStream_t stream) {
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || used == 1) return e;
-  const dim3 cgrid(tokens, (p.H + 31) / 32, kValue / 32 / kCombBlocks);
+  // units of (value block, pieces): 16 blocks x 2 / QPL, kCombWaves a group
+  const int groups = (p.H + 31) / 32;
   if (used <= 8)
-    hipLaunchKernelGGL(combine_kernel<8>, cgrid, dim3(64 * kCombBlocks), 0,
-                       stream, p, used);
+    hipLaunchKernelGGL((combine_kernel<8, 2>),
+                       dim3(tokens, groups, kValue / 32 / kCombWaves),
+                       dim3(64 * kCombWaves), 0, stream, p, used);
   else
-    hipLaunchKernelGGL(combine_kernel<kMaxSplits>, cgrid,
-                       dim3(64 * kCombBlocks), 0, stream, p, used);
+    hipLaunchKernelGGL((combine_kernel<kMaxSplits, 1>),
+                       dim3(tokens, groups, 2 * kValue / 32 / kCombWaves),
+                       dim3(64 * kCombWaves), 0, stream, p, used);
   return hipGetLastError();
 }
 
