@@ -36,7 +36,7 @@ namespace {
 
 constexpr int kSub = 32;      // keys per stage == MFMA N
 constexpr int kWavesPerWG = 4;
-constexpr int kFlush = 512;   // scores a wave buffers in LDS between writes
+constexpr int kFlush = 1024;  // scores a wave buffers in LDS between writes
 
 template <int DI>
 struct KeyLayout {
