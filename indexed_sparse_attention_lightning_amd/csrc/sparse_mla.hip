@@ -697,6 +697,25 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_kernel(
     bal[u] = __builtin_amdgcn_ballot_w64(pos[u] >= 0);
     if (lane == 0) rowcnt[u][wave] = __builtin_popcountll(bal[u]);
   }
+  // the cache row of every entry, the page-table lookups issued together
+  // under one test of the table pointer (a lookup per entry, each behind
+  // its own branch, was issued and waited for one at a time); entries
+  // without a position look up position 0
+  int prow[kRowIter];
+  if (p.kv.page_table != nullptr) {
+    const int32_t* const pt = p.kv.page_table + (int64_t)s.b * p.kv.max_pages;
+    int pg[kRowIter];
+#pragma unroll
+    for (int u = 0; u < kRowIter; ++u) pg[u] = pt[max(pos[u], 0) >> 6];
+#pragma unroll
+    for (int u = 0; u < kRowIter; ++u) {
+      const int g = p.kv.num_pages > 0 ? min(max(pg[u], 0), p.kv.num_pages - 1) : pg[u];
+      prow[u] = g * kPage + (max(pos[u], 0) & (kPage - 1));
+    }
+  } else {
+#pragma unroll
+    for (int u = 0; u < kRowIter; ++u) prow[u] = s.b * p.kv.L + max(pos[u], 0);
+  }
   barrier(true);
   {
     const uint64_t below = (1ull << lane) - 1;
@@ -710,8 +729,7 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_kernel(
         base += rowcnt[u][w];
       }
       if (pos[u] >= 0)
-        rows[off + __builtin_popcountll(bal[u] & below)] =
-            (int)cache_row(p.kv.page_table, p.kv.max_pages, p.kv.num_pages, p.kv.L, s.b, pos[u]);
+        rows[off + __builtin_popcountll(bal[u] & below)] = prow[u];
     }
     s.ntiles = max(1, (base + kRowsT - 1) / kRowsT);
     if (base + tid < s.ntiles * kRowsT) rows[base + tid] = ~dummy;
