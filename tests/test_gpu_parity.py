@@ -62,6 +62,13 @@ SMALL = {
                                              first_pos=1100, top_k=200, H=16,
                                              quantized=True,
                                              paged_random=True, seed=113),
+    # 256 tokens or more: one attention split per token (no combine, the
+    # software-pipelined tile loop); a ragged last tile, heads that leave
+    # one wave partly and two wholly idle, and causal rows of 1 to 3 tiles
+    "prefill_nosplit": wk.scaled(W["prefill"], T=260, L=1200, first_pos=940,
+                                 top_k=300, H=48, seed=114),
+    "prefill_nosplit_short_rows": wk.scaled(W["prefill"], T=256, L=256,
+                                            first_pos=0, top_k=96, seed=115),
 }
 
 
