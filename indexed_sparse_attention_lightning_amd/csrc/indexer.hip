@@ -694,18 +694,20 @@ __global__ __launch_bounds__(256, 2) void indexer_stream_q8_kernel(
 // Query-tiled indexer for many queries per sequence (prefill chunks): a
 // workgroup of 8 waves takes 8 consecutive queries (one per wave, two waves
 // per SIMD) and one chunk of keys.  The keys are staged once per workgroup
-// in 64-key LDS stages (double-buffered, the next stage's loads in flight in
-// registers) and every wave scores them against its own query, so each key
-// byte read from HBM feeds 8 queries x 64 heads of MFMA work.  Stages past
+// in 128-key LDS stages of two pages (double-buffered, the next stage's
+// loads in flight in registers; one barrier per stage covers four 32-key
+// halves of each wave's matrix work) and every wave scores them against its
+// own query, so each key byte read from HBM feeds 8 queries x 64 heads of
+// MFMA work.  Stages past
 // the last query of the tile are skipped (causal), and each wave skips the
 // 32-key halves that lie entirely past its own query.
 constexpr int kTileQ = 8;          // queries per workgroup (one per wave)
-constexpr int kStageKeys = 64;     // keys per LDS stage (one page)
+constexpr int kStageKeys = 2 * kPage;   // keys per LDS stage (two pages)
 
 template <int DI, bool FP8>
 struct TileStage {
-  // 16-byte loads of one 64-key stage (bf16 rows are 2*DI bytes, FP8 rows DI
-  // codes plus DI/32 scales), spread over the workgroup's threads
+  // 16-byte loads of one stage (bf16 rows are 2*DI bytes, FP8 rows DI codes
+  // plus DI/32 scales), spread over the workgroup's threads
   static constexpr int kTotal = kStageKeys * (FP8 ? DI : 2 * DI) / 16;
   static constexpr int kThreads = kTileQ * kWave;
   static constexpr int kLoads = (kTotal + kThreads - 1) / kThreads;
@@ -719,16 +721,24 @@ __device__ __forceinline__ void tile_load(TileStage<DI, FP8>& st,
                                           const CacheView& kc, int b,
                                           int kbase, int tid) {
   using KL = KeyLayout<DI>;
-  // wave-uniform: the page-table lookup is then a scalar load (a vector one
-  // is waited for together with the other stage's key loads in flight)
+  // wave-uniform: the page-table lookups are then scalar loads (a vector one
+  // is waited for together with the other stage's key loads in flight).
+  // The stage's two pages (kbase is a multiple of the stage); the second
+  // page of the last stage may lie past the table's row: its keys are never
+  // scored, so it takes the row's last page, whose rows are in the pool.
   b = __builtin_amdgcn_readfirstlane(b);
   kbase = __builtin_amdgcn_readfirstlane(kbase);
-  int64_t row0;
+  int64_t row0[2];
   bool clamp = false;
   if (kc.page_table != nullptr) {
-    row0 = cache_row_uniform(kc.page_table, kc.max_pages, kc.num_pages, kc.L, b, kbase);
+#pragma unroll
+    for (int g = 0; g < 2; ++g)
+      row0[g] = cache_row_uniform(kc.page_table, kc.max_pages, kc.num_pages,
+                                  kc.L, b,
+                                  min(kbase + g * kPage, (kc.max_pages - 1) * kPage)) -
+                g * kPage;
   } else {
-    row0 = (int64_t)b * kc.L + kbase;
+    row0[0] = row0[1] = (int64_t)b * kc.L + kbase;
     clamp = kbase + kStageKeys > kc.L;
   }
 #pragma unroll
@@ -738,12 +748,12 @@ __device__ __forceinline__ void tile_load(TileStage<DI, FP8>& st,
       break;
     if constexpr (!FP8) {
       const int n = id / KL::kChunks, c = id % KL::kChunks;
-      int64_t row = row0 + n;
+      int64_t row = row0[n / kPage] + n;
       if (clamp) row = (int64_t)b * kc.L + min(kbase + n, kc.L - 1);
       st.v[i] = ld16(kc.data + row * (DI * 2) + c * 16);
     } else {
       const int n = id / KL::kCodeChunks, c = id % KL::kCodeChunks;
-      int64_t row = row0 + n;
+      int64_t row = row0[n / kPage] + n;
       if (clamp) row = (int64_t)b * kc.L + min(kbase + n, kc.L - 1);
       st.v[i] = ld16(kc.data + row * DI + c * 16);
       st.sc[i] = kc.scale[row * (DI / 32) + (c >> 1)];
@@ -839,22 +849,19 @@ __global__ __launch_bounds__(kTileQ * kWave, 2) void indexer_tile_kernel(
 
 // Query-tiled quantised indexer (prefill chunks with quantised queries over
 // MX keys): the workgroup shape and causal skipping of indexer_tile_kernel;
-// the 64-key stages hold the e4m3 codes as they are (16-byte chunk c of key
-// n at chunk slot c ^ swz(n), conflict-free for the operand reads) plus the
-// keys' scale words, and every wave runs the scaled FP8 products against its
-// own query, quantised on load.
-// Keys per LDS stage of the quantised tile kernel: two pages, so that each
-// barrier covers four 32-key halves of matrix work per wave.
-constexpr int kStageKeysQ8 = 2 * kPage;
+// the stages hold the e4m3 codes as they are (16-byte chunk c of key n at
+// chunk slot c ^ swz(n), conflict-free for the operand reads) plus the keys'
+// scale words, and every wave runs the scaled FP8 products against its own
+// query, quantised on load.
 
 template <int DI>
 struct TileStageQ8 {
-  static constexpr int kChunks = kStageKeysQ8 * DI / 16;   // 16-B code chunks
+  static constexpr int kChunks = kStageKeys * DI / 16;   // 16-B code chunks
   static constexpr int kThreads = kTileQ * kWave;
   static constexpr int kLoads = (kChunks + kThreads - 1) / kThreads;
   static_assert(kChunks % kThreads == 0 || kLoads == 1, "stage loads");
   uint4 v[kLoads];
-  uint32_t sc;   // scale word of key tid (tid < kStageKeysQ8)
+  uint32_t sc;   // scale word of key tid (tid < kStageKeys)
 };
 
 template <int DI>
@@ -879,7 +886,7 @@ __device__ __forceinline__ void tile_load_q8(TileStageQ8<DI>& st,
                 g * kPage;
   } else {
     row0[0] = row0[1] = (int64_t)b * kc.L + kbase;
-    clamp = kbase + kStageKeysQ8 > kc.L;
+    clamp = kbase + kStageKeys > kc.L;
   }
 #pragma unroll
   for (int i = 0; i < TileStageQ8<DI>::kLoads; ++i) {
@@ -891,7 +898,7 @@ __device__ __forceinline__ void tile_load_q8(TileStageQ8<DI>& st,
     st.v[i] = ld16(kc.data + row * DI + c * 16);
   }
   {
-    const int n = tid & (kStageKeysQ8 - 1);
+    const int n = tid & (kStageKeys - 1);
     int64_t row = row0[n / kPage] + n;
     if (clamp) row = (int64_t)b * kc.L + min(kbase + n, kc.L - 1);
     if constexpr (DI == 128)
@@ -914,7 +921,7 @@ __device__ __forceinline__ void tile_store_q8(const TileStageQ8<DI>& st,
       tile[n * CL::kChunks + CL::slot(n, c)] = st.v[i];
     }
   }
-  if (tid < kStageKeysQ8) scl[tid] = st.sc;
+  if (tid < kStageKeys) scl[tid] = st.sc;
 }
 
 // Scores of 32 keys of an LDS stage (keys 0..31 of `tile`, scale words
@@ -955,9 +962,9 @@ template <int DI, int MB>
 __global__ __launch_bounds__(kTileQ * kWave, 2) void indexer_tile_q8_kernel(
     IndexerLaunch p, int keys_per_wg) {
   using CL = CodeLayout<DI>;
-  constexpr int kTileU4 = kStageKeysQ8 * DI / 16;
+  constexpr int kTileU4 = kStageKeys * DI / 16;
   __shared__ uint4 lds[2][kTileU4];
-  __shared__ uint32_t scl[2][kStageKeysQ8];
+  __shared__ uint32_t scl[2][kStageKeys];
   const int tid = threadIdx.x, lane = lane_id();
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int b = blockIdx.z;
@@ -978,7 +985,7 @@ __global__ __launch_bounds__(kTileQ * kWave, 2) void indexer_tile_q8_kernel(
       srow[s] = out_val(p, -__builtin_inff());
   const int kend = min(c1, qmax + 1);
   if (kend <= c0) return;   // workgroup-uniform
-  const int nst = (kend - c0 + kStageKeysQ8 - 1) / kStageKeysQ8;
+  const int nst = (kend - c0 + kStageKeys - 1) / kStageKeys;
 
   // this wave's query: every share's loads, the first two key stages, then
   // the quantisation (a query row past T re-reads row 0 and scores nothing)
@@ -993,7 +1000,7 @@ __global__ __launch_bounds__(kTileQ * kWave, 2) void indexer_tile_q8_kernel(
   const float wraw = p.w[qrow * p.H_I + min(lane, p.H_I - 1)];
   TileStageQ8<DI> st[2];
   tile_load_q8<DI>(st[0], p.keys, b, c0, tid);
-  tile_load_q8<DI>(st[1], p.keys, b, c0 + min(1, nst - 1) * kStageKeysQ8, tid);
+  tile_load_q8<DI>(st[1], p.keys, b, c0 + min(1, nst - 1) * kStageKeys, tid);
   v8i a[MB][DI / 64];
   int as[MB][DI / 64];
 #pragma unroll
@@ -1011,11 +1018,11 @@ __global__ __launch_bounds__(kTileQ * kWave, 2) void indexer_tile_q8_kernel(
     uint4* tile = lds[i & 1];
     uint32_t* sl = scl[i & 1];
     tile_store_q8<DI>(sr, tile, sl, tid);
-    tile_load_q8<DI>(sr, p.keys, b, c0 + min(i + 2, nst - 1) * kStageKeysQ8, tid);
+    tile_load_q8<DI>(sr, p.keys, b, c0 + min(i + 2, nst - 1) * kStageKeys, tid);
     __syncthreads();
 #pragma unroll
-    for (int u = 0; u < kStageKeysQ8 / kSub; ++u) {
-      const int kb = c0 + i * kStageKeysQ8 + u * kSub;
+    for (int u = 0; u < kStageKeys / kSub; ++u) {
+      const int kb = c0 + i * kStageKeys + u * kSub;
       if (has_q && kb <= qpos) {   // wave-uniform
         const float sc = tile_scores_q8<DI, MB>(tile + u * kSub * CL::kChunks,
                                                 sl + u * kSub, a, as, wv, lane);
