@@ -939,7 +939,7 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_mla_kernel(
 // r = 0..15, each split's two 16-byte pieces read as 1 KB per instruction.
 // Every load of a lane (all splits' g, then all splits' pieces) is issued
 // before any is used, so the splits' latencies overlap.
-constexpr int kMaxSplits = 16;
+constexpr int kMaxSplits = 32;
 constexpr int kCombWaves = 4;   // waves per workgroup
 // MAXS: the split count bound the registers are sized for; QPL: 16-byte
 // pieces per lane (2: a wave merges a whole value block of its 32 heads;
@@ -1071,6 +1071,10 @@ hipError_t launch_sparse_mla(const AttnLaunch& p, hipStream_t stream) {
   if (used <= 8)
     hipLaunchKernelGGL((combine_kernel<8, 2>),
                        dim3(tokens, groups, kValue / 32 / kCombWaves),
+                       dim3(64 * kCombWaves), 0, stream, p, used);
+  else if (used <= 16)
+    hipLaunchKernelGGL((combine_kernel<16, 1>),
+                       dim3(tokens, groups, 2 * kValue / 32 / kCombWaves),
                        dim3(64 * kCombWaves), 0, stream, p, used);
   else
     hipLaunchKernelGGL((combine_kernel<kMaxSplits, 1>),
