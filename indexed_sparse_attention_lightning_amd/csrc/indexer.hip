@@ -434,9 +434,10 @@ __global__ __launch_bounds__(256, 2) void indexer_stream_kernel(
 // quantised per head and 32-feature block on load (the rule of the cache
 // append: scale 2^X, X the smallest with 448 * 2^X >= the block maximum),
 // and the products run on the 32x32x64 scaled FP8 matrix cores, which take
-// the e8m0 block scales of both operands as they are: the key codes go from
-// HBM straight into operand registers, with no LDS staging and no
-// dequantisation.
+// the e8m0 block scales of both operands as they are: the key codes are
+// never dequantised.  The decode kernel stages them like the FP8-key one
+// (coalesced non-temporal loads into the wave's LDS tile, read back in
+// operand layout); the prefill kernel shares 128-key LDS stages.
 //
 // Operand layout of k-step ks (64 features): lane l = n + 32h holds 32 codes
 // of row n (query head or key); bytes 0..15 are features 64ks + 16h + 0..15
@@ -451,42 +452,6 @@ __device__ __forceinline__ v8i join8(const uint4& lo, const uint4& hi) {
   r[0] = (int)lo.x; r[1] = (int)lo.y; r[2] = (int)lo.z; r[3] = (int)lo.w;
   r[4] = (int)hi.x; r[5] = (int)hi.y; r[6] = (int)hi.z; r[7] = (int)hi.w;
   return r;
-}
-
-// One 32-key stage in registers: lane (n, h) holds key n's codes of pieces
-// (ks, p) at byte 64ks + 32p + 16h, and the key's scale word.
-template <int DI>
-struct KeysQ8 {
-  uint4 v[DI / 32];   // v[2ks + p]
-  uint32_t sc;        // e8m0 codes of the key's DI/32 blocks, block j in byte j
-};
-
-template <int DI>
-__device__ __forceinline__ void keys_load_q8(KeysQ8<DI>& st,
-                                             const CacheView& kc, int b,
-                                             int kbase, int lane) {
-  // wave-uniform: the page-table lookup is then a scalar load (a vector one
-  // would be waited for with every key load in flight)
-  b = __builtin_amdgcn_readfirstlane(b);
-  kbase = __builtin_amdgcn_readfirstlane(kbase);
-  const int n = lane & 31, h = lane >> 5;
-  int64_t row;
-  if (kc.page_table != nullptr) {
-    // the 32 keys of a stage share one page (stages are 32-aligned, pages 64)
-    row = cache_row_uniform(kc.page_table, kc.max_pages, kc.num_pages, kc.L, b, kbase) + n;
-  } else {
-    row = (int64_t)b * kc.L + min(kbase + n, kc.L - 1);
-  }
-  const uint8_t* base = kc.data + row * DI + 16 * h;
-  // plain loads: an instruction reads 32 of a line's 128 bytes, and the
-  // line must stay in L2 for the other three (non-temporal loads, which do
-  // not keep it, fetched each line four times: 113 us against 98 per step)
-#pragma unroll
-  for (int i = 0; i < DI / 32; ++i) st.v[i] = ld16(base + 32 * i);
-  if constexpr (DI == 128)
-    st.sc = *reinterpret_cast<const uint32_t*>(kc.scale + row * 4);
-  else
-    st.sc = *reinterpret_cast<const uint16_t*>(kc.scale + row * 2);
 }
 
 // The query's A operands: quantised codes and the scale operands, plus the
@@ -556,22 +521,28 @@ __device__ __forceinline__ void spread_weights_q8(float wl, int lane,
       wv[m][r] = __shfl(wl, m * 32 + 8 * (r >> 2) + 4 * h + (r & 3));
 }
 
-// Scores of the stage's 32 keys against the query: in every lane, the score
-// of key lane % 32.
+
+// Scores of 32 keys of an LDS stage (keys 0..31 of `tile`, scale words
+// `scl`) against the wave's quantised query: in every lane, the score of key
+// lane % 32.
 template <int DI, int MB>
-__device__ __forceinline__ float scores_q8(const KeysQ8<DI>& st,
-                                           const v8i (&a)[MB][DI / 64],
-                                           const int (&as)[MB][DI / 64],
-                                           const float (&wv)[MB][16],
-                                           int lane) {
-  const int h = lane >> 5;
+__device__ __forceinline__ float tile_scores_q8(const uint4* tile,
+                                                const uint32_t* scl,
+                                                const v8i (&a)[MB][DI / 64],
+                                                const int (&as)[MB][DI / 64],
+                                                const float (&wv)[MB][16],
+                                                int lane) {
+  using CL = CodeLayout<DI>;
+  const int n = lane & 31, h = lane >> 5;
+  const uint32_t sc = scl[n];
   f32x16 acc[MB];
 #pragma unroll
   for (int m = 0; m < MB; ++m) acc[m] = f32x16{};
 #pragma unroll
   for (int ks = 0; ks < DI / 64; ++ks) {
-    const v8i bop = join8(st.v[2 * ks], st.v[2 * ks + 1]);
-    const int bs = (int)((st.sc >> (8 * (2 * ks + h))) & 0xffu);
+    const v8i bop = join8(tile[n * CL::kChunks + CL::slot(n, 4 * ks + h)],
+                          tile[n * CL::kChunks + CL::slot(n, 4 * ks + 2 + h)]);
+    const int bs = (int)((sc >> (8 * (2 * ks + h))) & 0xffu);
 #pragma unroll
     for (int m = 0; m < MB; ++m)
       acc[m] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
@@ -585,8 +556,10 @@ __device__ __forceinline__ float scores_q8(const KeysQ8<DI>& st,
   return s + swap_halves(s);
 }
 
-// Streaming indexer with quantised queries over MX keys: the grid and the
-// score buffering of indexer_stream_kernel; four stages in flight.  The four
+// Streaming indexer with quantised queries over MX keys: the grid, the
+// score buffering and the key staging of indexer_stream_kernel for FP8
+// keys (four stages in flight, coalesced non-temporal loads into the wave's
+// LDS tile, read back in the scaled products' operand layout).  The four
 // waves of a workgroup score the same query row, so each quantises one share
 // of its operands into LDS (before any wave leaves) and all read them.
 template <int DI, int MB>
@@ -595,6 +568,8 @@ __global__ __launch_bounds__(256, 2) void indexer_stream_q8_kernel(
   constexpr int kShares = MB * (DI / 64);   // (head block, k-step) pairs
   static_assert(kShares <= kWavesPerWG, "one share per wave");
   __shared__ float sbuf[kWavesPerWG][kFlush];
+  __shared__ uint4 ktile[kWavesPerWG][kSub * DI / 16];
+  __shared__ uint32_t kscl[kWavesPerWG][kSub];
   __shared__ v8i qcode[kShares][kWave];
   __shared__ int qscale[kShares][kWave];
   const int lane = lane_id();
@@ -632,11 +607,11 @@ __global__ __launch_bounds__(256, 2) void indexer_stream_q8_kernel(
   uint4 raw[4];
   load_share_q8<DI>(p.q_idx + qrow * p.H_I * DI, p.H_I, qm, qks, lane, raw);
   const float wraw = p.w[qrow * p.H_I + min(lane, p.H_I - 1)];
-  KeysQ8<DI> st[4];
+  StageF8<DI> st[4];
 #pragma unroll
   for (int u = 0; u < 4; ++u)
-    keys_load_q8<DI>(st[u], p.keys, b, work ? k0 + min(u, last) * kSub : 0,
-                     lane);
+    stage_load_f8<DI>(st[u], p.keys, b, work ? k0 + min(u, last) * kSub : 0,
+                      lane, !work || u > last);
   if (wave < kShares) {
     v8i c;
     int sc;
@@ -677,8 +652,11 @@ __global__ __launch_bounds__(256, 2) void indexer_stream_q8_kernel(
       // the products read the stage's registers, then its next load goes
       // into the same registers (no copies: moving a register whose load is
       // in flight would wait for every load)
-      const float sc = scores_q8<DI, MB>(st[u], a, as, wv, lane);
-      keys_load_q8<DI>(st[u], p.keys, b, k0 + min(i + u + 4, last) * kSub, lane);
+      stage_store_f8<DI>(st[u], ktile[wave], kscl[wave], lane);
+      stage_load_f8<DI>(st[u], p.keys, b, k0 + min(i + u + 4, last) * kSub,
+                        lane, i + u + 4 > last);
+      const float sc = tile_scores_q8<DI, MB>(ktile[wave], kscl[wave], a, as,
+                                              wv, lane);
       if (lane < 32 && i + u < nsub)
         sb[((i + u) * kSub + lane) % kFlush] = out_val(p, sc);
     }
@@ -922,40 +900,6 @@ __device__ __forceinline__ void tile_store_q8(const TileStageQ8<DI>& st,
     }
   }
   if (tid < kStageKeys) scl[tid] = st.sc;
-}
-
-// Scores of 32 keys of an LDS stage (keys 0..31 of `tile`, scale words
-// `scl`) against the wave's quantised query: in every lane, the score of key
-// lane % 32.
-template <int DI, int MB>
-__device__ __forceinline__ float tile_scores_q8(const uint4* tile,
-                                                const uint32_t* scl,
-                                                const v8i (&a)[MB][DI / 64],
-                                                const int (&as)[MB][DI / 64],
-                                                const float (&wv)[MB][16],
-                                                int lane) {
-  using CL = CodeLayout<DI>;
-  const int n = lane & 31, h = lane >> 5;
-  const uint32_t sc = scl[n];
-  f32x16 acc[MB];
-#pragma unroll
-  for (int m = 0; m < MB; ++m) acc[m] = f32x16{};
-#pragma unroll
-  for (int ks = 0; ks < DI / 64; ++ks) {
-    const v8i bop = join8(tile[n * CL::kChunks + CL::slot(n, 4 * ks + h)],
-                          tile[n * CL::kChunks + CL::slot(n, 4 * ks + 2 + h)]);
-    const int bs = (int)((sc >> (8 * (2 * ks + h))) & 0xffu);
-#pragma unroll
-    for (int m = 0; m < MB; ++m)
-      acc[m] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-          a[m][ks], bop, acc[m], 0, 0, 0, as[m][ks], 0, bs);
-  }
-  float s = 0.f;
-#pragma unroll
-  for (int m = 0; m < MB; ++m)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) s += wv[m][r] * relu(acc[m][r]);
-  return s + swap_halves(s);
 }
 
 template <int DI, int MB>
