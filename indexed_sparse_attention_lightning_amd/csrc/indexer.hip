@@ -1003,16 +1003,17 @@ hipError_t launch_tile(const IndexerLaunch& p, hipStream_t stream) {
 }
 
 // Positions per wave of the stream kernels, for about 1024 waves (one per
-// SIMD on 256 CUs) or, for FP8 keys with bf16 queries, 2048 (that kernel is
-// bound by each wave's matrix and dequantisation work, which a second wave
-// per SIMD hides).  Longer waves pay their query setup less often: the
-// quantised kernel measured 29.5 us for 1024 waves against 30.3-31.6 us for
-// 2048 on the FP8 decode batch, and the bf16 one, with the non-temporal key
-// stream, 47.7-48.8 us against 48.7-49.7 us (4096: 48.2-49.2) on the bf16
+// SIMD on 256 CUs) for bf16 keys, or 2048 for FP8 keys (half the bytes per
+// stage: a second wave per SIMD keeps as many bytes in flight and hides each
+// wave's matrix and dequantisation work).  Longer waves pay their query
+// setup less often: the bf16 kernel, with the non-temporal key stream,
+// measured 47.7-48.8 us for 1024 waves against 48.7-49.7 us for 2048 (4096:
+// 48.2-49.2) on the bf16 decode batch; the quantised one, with its stages in
+// LDS, 26.4-26.7 us for 2048 against 28.4-28.7 us for 1024 on the FP8
 // decode batch.  Whole 32-key stages, 64..4096.
 int stream_kpw(const IndexerLaunch& p) {
   const int64_t total = (int64_t)p.B * p.T * p.row_len;
-  const int64_t waves = p.keys.fp8 && !p.q8 ? 2048 : 1024;
+  const int64_t waves = p.keys.fp8 ? 2048 : 1024;
   int64_t kpw = (total + waves - 1) / waves;
   kpw = (kpw + kSub - 1) / kSub * kSub;
   return (int)(kpw < 64 ? 64 : (kpw > 4096 ? 4096 : kpw));
