@@ -586,7 +586,53 @@ __global__ __launch_bounds__(kThreads, 1) void topk_kernel(TopkLaunch p) {
 
   uint32_t thr = blo;            // relative threshold
   uint32_t eq_total = cnt0;
-  if (nsh > 0) {
+  uint32_t ctot, cbefore;        // keys listed in the threshold digit
+  waves_prefix(sm.scnt, lane, wave, cbefore, ctot);
+  if (nsh > 0 && sm.overflow == 0u && ctot <= (uint32_t)kWave) {
+    // ---- few keys in the threshold digit (the usual case: about ten in a
+    // 32K-position decode row): wave 0 orders them by key, then position,
+    // and marks the first `rem` in the above-threshold bitmap, in place of
+    // the remaining digit passes (each a histogram clear, a count and a
+    // block scan, with four barriers)
+    if (wave == 0) {
+      // lane i takes candidate i of the waves' lists, in wave order
+      const uint32_t c = lane < kWaves ? sm.scnt[lane] : 0u;
+      const uint32_t incl = wave_incl_scan(c, lane);
+      int w = 0;
+#pragma unroll
+      for (int x = 0; x < kWaves; ++x)
+        w += readlane(incl, x) <= (uint32_t)lane ? 1 : 0;
+      // list entries before wave w (read with every lane active: a lane
+      // reading an inactive lane's register gets 0)
+      const int ws = min(w, kWaves - 1);
+      const uint32_t ew = (uint32_t)__shfl((int)incl, ws) -
+                          (uint32_t)__shfl((int)c, ws);
+      uint64_t v = 0;   // (key << 32) | ~position; 0 for lanes past the list
+      if ((uint32_t)lane < ctot) {
+        const uint2 cd = sm.slab[w][lane - ew];
+        v = ((uint64_t)cd.y << 32) | (uint32_t)~cd.x;
+      }
+      // bitonic sort across the lanes, descending: larger keys first, equal
+      // keys by ascending position (relative keys of candidates are >= 1)
+#pragma unroll
+      for (int k = 2; k <= kWave; k <<= 1)
+#pragma unroll
+        for (int j = k >> 1; j > 0; j >>= 1) {
+          const uint64_t o =
+              ((uint64_t)(uint32_t)__shfl_xor((int)(uint32_t)(v >> 32), j) << 32) |
+              (uint32_t)__shfl_xor((int)(uint32_t)v, j);
+          const bool keep_max = ((lane & k) == 0) == ((lane & j) == 0);
+          v = keep_max ? (v > o ? v : o) : (v < o ? v : o);
+        }
+      if ((uint32_t)lane < rem) {
+        const uint32_t pos = ~(uint32_t)v;
+        atomicOr(&sm.gtw[pos >> 5], 1u << (pos & 31));
+      }
+    }
+    rem = 0;        // the taken keys are all in the bitmap
+    eq_total = 0;
+    __syncthreads();
+  } else if (nsh > 0) {
     // ---- the remaining digits, on the candidates only (or, if a wave's
     // list overflowed, on all keys again)
     const bool ovf = sm.overflow != 0u;
