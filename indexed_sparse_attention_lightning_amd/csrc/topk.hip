@@ -26,10 +26,11 @@
 // LDS atomics).  Each pass histograms the keys still in the window (up to 13
 // bits, 8192 bins) and a block scan in descending digit order finds the digit
 // holding the K-th key; rows need one to three passes, except that when the
-// first pass leaves at most 64 keys in that digit one wave sorts them.  Finally the keys
-// > thr and the first `need` keys == thr (in position order) are selected and
-// written at their ascending output slot, computed from ballots and per-wave
-// counts.  All integer work on bit patterns: exact and deterministic.
+// first pass leaves at most 64 keys in that digit one wave sorts them.
+// Finally the keys > thr and the first `need` keys == thr (in position
+// order) are selected and written at their ascending output slot, computed
+// from ballots and per-wave counts.  All integer work on bit patterns: exact
+// and deterministic.
 #include "dsa_device.h"
 #include "dsa_launch.h"
 
