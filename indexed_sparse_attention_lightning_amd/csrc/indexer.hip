@@ -593,13 +593,13 @@ __global__ __launch_bounds__(256, 2) void indexer_stream_q8_kernel(
   const bool work = kend > k0;   // wave-uniform
   const int nsub = work ? (kend - k0 + kSub - 1) / kSub : 1;
   const int last = nsub - 1;
-  // Every iteration issues the same loads (the tail re-reads the last stage,
-  // an L2 hit, and its scores are dropped), so the compiler waits only for
-  // the stage it consumes.
-  // this wave's share of the query first, then the first four key stages,
+  // Every iteration issues the same loads (stages past the end are parked:
+  // they read zeros through an empty range, and their scores are dropped),
+  // so the compiler waits only for the stage it consumes.
+  // This wave's share of the query first, then the first four key stages,
   // so that the quantisation waits only for the query.  Both are issued by
   // every wave (a wave without a share re-loads share 0, one without keys
-  // loads position 0): loads under a branch would make the compiler's wait
+  // parks its stages): loads under a branch would make the compiler's wait
   // before the quantisation cover the key loads as well.
   const int64_t qrow = (int64_t)b * p.T + t;
   const int share = wave < kShares ? wave : 0;
