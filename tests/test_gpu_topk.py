@@ -143,3 +143,35 @@ def test_topk_many_rows_prefill_shape():
     for t in range(T):
         want = oracle.topk_row(x[t], int(q_pos[0, t]), K)
         assert np.array_equal(got[0, t], want), f"row {t}"
+
+
+@pytest.mark.parametrize("L", [4096, 32768, 65536, 100000])
+def test_topk_threshold_digit_sizes(L):
+    """Rows whose threshold digit (after the first digit pass) holds 63, 64
+    or 65 keys -- at most 64 take the one-wave finish, more the remaining
+    digit passes -- with equal keys in it that the K-th position splits: both
+    finishes must take the higher keys, then the lower positions.  K - 40
+    keys lie far above (1000 + i), a cluster of eight distinct values in
+    [50, 50.11] (one first-pass digit: the row's key range spans about 2^28,
+    so a digit covers 2^18 or 2^19 float steps, at least 1.0 at 50) holds the
+    threshold, the rest lie in [0, 0.5)."""
+    rng = np.random.default_rng(500 + L)
+    K = 2048
+    rows = []
+    for C in (63, 64, 65):
+        x = (rng.random(L) * 0.5).astype(np.float32)
+        pos = rng.permutation(L)
+        above = K - 40
+        x[pos[:above]] = (1000.0 + np.arange(above)).astype(np.float32)
+        x[pos[above:above + C]] = (50.0 + (np.arange(C) % 8) / 64.0).astype(np.float32)
+        rows.append(x)
+    x = np.stack(rows)
+    R = len(rows)
+    q_pos = np.full((R, 1), L - 1, dtype=np.int32)
+    scores = torch.from_numpy(x).view(R, 1, L).cuda()
+    idx = dsa.topk(scores, torch.from_numpy(q_pos).cuda(), K)
+    torch.cuda.synchronize()
+    got = idx.cpu().numpy()
+    for r in range(R):
+        want = oracle.topk_row(x[r], L - 1, K)
+        assert np.array_equal(got[r, 0], want), f"L={L} cluster {63 + r}"
