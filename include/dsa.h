@@ -102,6 +102,7 @@ typedef enum dsa_op {
 #define DSA_PAGE_SIZE 64
 #define DSA_MAX_TOPK 2048
 #define DSA_MAX_CONTEXT 131072   /* longest score row / sequence */
+#define DSA_FUSED_MAX_CONTEXT 32768   /* longest row of dsa_indexer_topk */
 /* Bytes of device scratch that dsa_decode_step_static owns on each GPU. */
 #define DSA_STATIC_SCRATCH_BYTES (64ull << 20)
 
@@ -213,6 +214,37 @@ dsa_status dsa_sparse_mla_attn(int B, int T, int L, int H, int K,
                                float softmax_scale, float* out, float* lse,
                                void* workspace, size_t workspace_bytes,
                                void* stream);
+
+/*
+ * Steps 1 and 2 as one kernel over the paged key cache: scoring, head
+ * weighting and Top-K of each query row without the scores leaving the chip
+ * (page "Inference Adaptation and Performance Optimization for New Large
+ * Language Model Architectures", section 3.1 "Fused Index Computation": the
+ * three steps in one kernel that reads the paged keys and outputs only the
+ * final indices; page "Day-0 Inference Adaptation and Performance
+ * Optimization for New-Architecture Large Language Models", "Fusing the
+ * Indexer to Reduce Intermediate Write-Backs").  One workgroup per query row
+ * keeps the row's scores in its LDS, so rows are limited to
+ * DSA_FUSED_MAX_CONTEXT positions.  The same scores and the same selection
+ * as dsa_indexer_scores followed by dsa_topk (ties to the lower position).
+ *   cache         page pools as for dsa_decode_step; only the indexer-key
+ *                 fields, page_table and seq_lens are read (kv, kv_scale
+ *                 may be NULL)
+ *   max_seq_len   host upper bound of seq_lens, 1 .. DSA_FUSED_MAX_CONTEXT
+ *                 (else DSA_ERR_UNSUPPORTED) and <= max_pages_per_seq * 64
+ *   q_idx [B, T, H_I, d_I] bf16; q_mode must be DSA_Q_BF16 (the quantised
+ *                 indexer runs only in the two-kernel path:
+ *                 DSA_ERR_UNSUPPORTED)
+ *   w [B, T, H_I] fp32
+ *   q_pos [B, T] int32, or NULL when T == 1: then q_pos = seq_lens[b] - 1;
+ *                 positions are clamped to seq_lens[b] - 1
+ *   idx [B, T, K] int32 out, as dsa_topk's idx
+ * Needs no workspace and allocates nothing.
+ */
+dsa_status dsa_indexer_topk(int B, int T, int H_I, int d_I, int K,
+                            const dsa_paged_cache* cache, int max_seq_len,
+                            const void* q_idx, int q_mode, const float* w,
+                            const int32_t* q_pos, int32_t* idx, void* stream);
 
 /*
  * The whole path for T query tokens per sequence over a paged cache:

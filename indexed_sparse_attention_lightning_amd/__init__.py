@@ -15,6 +15,8 @@ Entry points (same names as the C ABI, without the ``dsa_`` prefix):
 * ``decode_step``     indexer -> Top-K -> attention over a paged cache
 * ``decode_step_static``  the same in the library's static device scratch
                       (no workspace: for callers that cannot allocate)
+* ``indexer_topk``    indexer and Top-K in one kernel over the paged keys
+                      (scores kept on chip; rows up to 32768 positions)
 * ``cache_append``    store new tokens' key / latent rows into the paged
                       pools, quantised to each pool's format
 """
@@ -32,7 +34,7 @@ __all__ = [
     "DSA_BF16", "DSA_E4M3_MX32", "DSA_E4M3_T128", "DSA_Q_BF16", "DSA_Q_MX32",
     "DsaError", "PagedCache",
     "cache_append", "decode_step", "decode_step_static", "indexer_scores",
-    "library_path", "STATIC_SCRATCH_BYTES",
+    "indexer_topk", "library_path", "FUSED_MAX_CONTEXT", "STATIC_SCRATCH_BYTES",
     "sparse_mla_attn", "topk", "workspace_size",
 ]
 
@@ -44,6 +46,7 @@ DSA_Q_BF16, DSA_Q_MX32 = 0, 1
 OP_INDEXER_SCORES, OP_TOPK, OP_SPARSE_MLA, OP_DECODE_STEP = 0, 1, 2, 3
 LATENT, VALUE, PAGE = 576, 512, 64
 STATIC_SCRATCH_BYTES = 64 << 20   # DSA_STATIC_SCRATCH_BYTES
+FUSED_MAX_CONTEXT = 32768         # DSA_FUSED_MAX_CONTEXT
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libdsa.so")
@@ -85,6 +88,8 @@ def _load():
         "dsa_decode_step_static": [I, I, I, I, I, I, F,
                                    ctypes.POINTER(_PagedCacheC),
                                    I, P, I, P, P, P, P, P, P, P],
+        "dsa_indexer_topk": [I, I, I, I, I, ctypes.POINTER(_PagedCacheC), I,
+                             P, I, P, P, P, P],
         "dsa_cache_append": [I, I, I, I, I, P, P, P, I, P, P, P, I, P, P, P],
         "dsa_workspace_size": [I, I, I, I, I, I],
         "dsa_status_string": [I],
@@ -95,7 +100,7 @@ def _load():
         fn.argtypes = args
     for name in ("dsa_indexer_scores", "dsa_topk", "dsa_sparse_mla_attn",
                  "dsa_decode_step", "dsa_decode_step_static",
-                 "dsa_cache_append"):
+                 "dsa_indexer_topk", "dsa_cache_append"):
         getattr(lib, name).restype = ctypes.c_int
     lib.dsa_workspace_size.restype = ctypes.c_size_t
     lib.dsa_status_string.restype = ctypes.c_char_p
@@ -377,6 +382,38 @@ def decode_step_static(cache: PagedCache, q_idx: torch.Tensor,
         _ptr(q_pos), _ptr(out), _ptr(lse), _ptr(idx_out), _stream()),
         "dsa_decode_step_static")
     return out, lse, idx_out
+
+
+def indexer_topk(cache: PagedCache, q_idx: torch.Tensor, w: torch.Tensor,
+                 k: int, max_seq_len: int,
+                 q_pos: Optional[torch.Tensor] = None,
+                 idx_out: Optional[torch.Tensor] = None):
+    """Indexer scores and Top-K of every query row in one kernel (the scores
+    never leave the chip) for q_idx [B, T, H_I, d_I] bf16 and w [B, T, H_I]
+    fp32 over the paged key cache; max_seq_len <= FUSED_MAX_CONTEXT.  q_pos
+    [B, T] int32, or None for T == 1.  Returns idx [B, T, k] int32, the
+    same selection as indexer_scores followed by topk."""
+    B, T, H_I, d_I = q_idx.shape
+    _need(q_idx, "q_idx", torch.bfloat16)
+    _need(w, "w", torch.float32, (B, T, H_I))
+    if q_pos is not None:
+        _need(q_pos, "q_pos", torch.int32, (B, T))
+    c = cache.as_c()
+    if cache.kidx.shape[2] != d_I:
+        raise ValueError(f"kidx rows are {cache.kidx.shape[2]} wide, the "
+                         f"indexer queries {d_I}")
+    if cache.page_table.shape[0] != B:
+        raise ValueError(f"page_table has {cache.page_table.shape[0]} rows, "
+                         f"the batch {B}")
+    if idx_out is None:
+        idx_out = torch.empty((B, T, k), dtype=torch.int32,
+                              device=q_idx.device)
+    _need(idx_out, "idx_out", torch.int32, (B, T, k))
+    _check(_lib.dsa_indexer_topk(
+        B, T, H_I, d_I, k, ctypes.byref(c), int(max_seq_len), _ptr(q_idx),
+        DSA_Q_BF16, _ptr(w), _ptr(q_pos), _ptr(idx_out), _stream()),
+        "dsa_indexer_topk")
+    return idx_out
 
 
 def cache_append(cache: PagedCache, pos: torch.Tensor,

@@ -399,6 +399,60 @@ dsa_status dsa_decode_step_static(int B, int T, int H_I, int d_I, int H, int K,
                           idx_out, nullptr, 0, stream, true);
 }
 
+dsa_status dsa_indexer_topk(int B, int T, int H_I, int d_I, int K,
+                            const dsa_paged_cache* cache, int max_seq_len,
+                            const void* q_idx, int q_mode, const float* w,
+                            const int32_t* q_pos, int32_t* idx, void* stream) {
+  if (!cache || !q_idx || !w || !idx)
+    return fail(DSA_ERR_NULL, "dsa_indexer_topk: NULL pointer");
+  if (!cache->kidx || !cache->page_table || !cache->seq_lens)
+    return fail(DSA_ERR_NULL, "dsa_indexer_topk: NULL cache pointer");
+  if (dsa_status s = check_indexer_dims(B, T, H_I, d_I)) return s;
+  if (K < 1 || K > DSA_MAX_TOPK)
+    return fail(DSA_ERR_UNSUPPORTED, "K must be in [1, %d], got %d",
+                DSA_MAX_TOPK, K);
+  if (!q_pos && T != 1)
+    return fail(DSA_ERR_NULL, "q_pos may be NULL only when T == 1");
+  if (cache->page_size != DSA_PAGE_SIZE)
+    return fail(DSA_ERR_UNSUPPORTED, "page_size must be %d", DSA_PAGE_SIZE);
+  if (cache->num_pages < 1 || cache->max_pages_per_seq < 1)
+    return fail(DSA_ERR_SHAPE, "num_pages and max_pages_per_seq must be >= 1");
+  if ((long long)cache->num_pages * DSA_PAGE_SIZE > 0x7fffffffLL)
+    return fail(DSA_ERR_UNSUPPORTED, "num_pages * 64 must fit in int32");
+  if (max_seq_len > DSA_FUSED_MAX_CONTEXT)
+    return fail(DSA_ERR_UNSUPPORTED,
+                "dsa_indexer_topk: max_seq_len must be <= %d (one row's "
+                "scores in one workgroup's LDS)", DSA_FUSED_MAX_CONTEXT);
+  if (max_seq_len < 1 ||
+      (long long)max_seq_len > (long long)cache->max_pages_per_seq * DSA_PAGE_SIZE)
+    return fail(DSA_ERR_SHAPE,
+                "max_seq_len must be in [1, max_pages_per_seq * 64]");
+  if (!valid_key_dtype(cache->kidx_dtype))
+    return fail(DSA_ERR_UNSUPPORTED, "unsupported key dtype %d",
+                cache->kidx_dtype);
+  const bool kfp8 = cache->kidx_dtype == DSA_E4M3_MX32;
+  if (kfp8 && !cache->kidx_scale)
+    return fail(DSA_ERR_NULL, "MX indexer keys need kidx_scale");
+  if (dsa_status st = check_q_mode(q_mode, kfp8)) return st;
+  if (q_mode != DSA_Q_BF16)
+    return fail(DSA_ERR_UNSUPPORTED,
+                "dsa_indexer_topk: q_mode must be DSA_Q_BF16");
+  static_assert(DSA_FUSED_MAX_CONTEXT == dsa::kFusedMaxLen, "LDS row bound");
+  dsa::IndexerLaunch a{};
+  a.B = B; a.T = T; a.H_I = H_I; a.d_I = d_I;
+  a.q_idx = static_cast<const uint16_t*>(q_idx);
+  a.w = w;
+  a.keys = dsa::CacheView{static_cast<const uint8_t*>(cache->kidx),
+                          cache->kidx_scale, cache->page_table,
+                          cache->max_pages_per_seq, 0, kfp8,
+                          (uint64_t)cache->num_pages * DSA_PAGE_SIZE * d_I *
+                              (kfp8 ? 1 : 2), false, cache->num_pages};
+  a.qp = dsa::QueryPos{q_pos, cache->seq_lens, T};
+  a.row_len = max_seq_len;
+  return hip_status(dsa::launch_index_topk(a, K, idx, (hipStream_t)stream),
+                    "dsa_indexer_topk");
+}
+
 dsa_status dsa_cache_append(int B, int T, int d_I, int num_pages,
                             int max_pages_per_seq, const int32_t* page_table,
                             const int32_t* pos, const void* k_new,

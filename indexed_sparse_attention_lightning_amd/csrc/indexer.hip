@@ -1054,6 +1054,248 @@ hipError_t launch_q8(const IndexerLaunch& p, hipStream_t stream) {
                        : launch_stream_q8<DI, MB>(p, stream);
 }
 
+// ------------------------------------------ fused indexer + Top-K (decode)
+// Scoring, head weighting and Top-K of one query row in a single kernel that
+// reads the paged keys and writes only the selected positions; the scores
+// stay in LDS (page "Inference Adaptation and Performance Optimization for
+// New Large Language Model Architectures", section 3.1 "Fused Index
+// Computation"; page "Day-0 Inference Adaptation and Performance
+// Optimization for New-Architecture Large Language Models", "Fusing the
+// Indexer to Reduce Intermediate Write-Backs").
+// One workgroup of four waves per query row:
+//   * stream: stage i of the row's 32-key stages goes to wave i % 4, which
+//     loads, transposes and scores it exactly as the stream kernel does and
+//     stores each score's order-preserving key at its position in LDS
+//     (32768 keys fill 128 KiB; the four stage tiles take the other 32 KiB);
+//   * select: a radix select over the LDS keys (digits of up to 11 bits cut
+//     from the row's key range, one histogram pass each) finds the K-th
+//     largest key; the keys above it and the first keys equal to it in
+//     position order go to their ascending output slots.
+// A row is one CU's work here, against eight or more CUs in the two-kernel
+// path, so the single kernel keeps pace only with about one row per CU.
+constexpr int kFusedWaves = 4;
+constexpr int kFusedThreads = kFusedWaves * kWave;
+constexpr int kFusedDigitBits = 11;
+constexpr int kFusedBins = 1 << kFusedDigitBits;
+
+// 16-byte words of a wave's stage tile: bf16 rows, or FP8 codes followed by
+// the stage's 32 scale words
+template <int DI, bool FP8>
+constexpr int fused_tile_words() {
+  return FP8 ? (kSub * DI + kSub * 4) / 16 : KeyLayout<DI>::kTileBytes / 16;
+}
+
+template <int DI, bool FP8>
+struct FusedShared {
+  uint32_t key[kFusedMaxLen];   // score keys of positions 0 .. n-1
+  union {
+    uint4 tile[kFusedWaves][fused_tile_words<DI, FP8>()];   // stream
+    struct {                                                // select
+      uint32_t hist[kFusedBins];
+      uint32_t mn[kFusedWaves], mx[kFusedWaves];   // key range per wave
+      uint32_t tot[kFusedWaves];                   // digit pass, per wave
+      uint32_t ngt[kFusedWaves], neq[kFusedWaves]; // emit, per wave
+      uint32_t pick, above;
+    } t;
+  } u;
+};
+
+__device__ __forceinline__ uint32_t fused_lanes_below(uint64_t m) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                   __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
+template <int DI, int MB, bool FP8>
+__global__ __launch_bounds__(kFusedThreads, 1) void index_topk_kernel(
+    IndexerLaunch p, int K, int32_t* idx) {
+  __shared__ FusedShared<DI, FP8> sm;
+  static_assert(sizeof(FusedShared<DI, FP8>) <= 160 * 1024, "LDS");
+  const int tid = threadIdx.x, lane = lane_id();
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int r = blockIdx.x, b = r / p.T, t = r % p.T;
+  const int qpos = __builtin_amdgcn_readfirstlane(query_pos(p.qp, b, t));
+  const int n = max(0, min(qpos + 1, p.row_len));   // causal positions
+  const int kk = min(K, n);
+  int32_t* out = idx + (int64_t)r * K;
+  for (int i = kk + tid; i < K; i += kFusedThreads) out[i] = -1;
+  if (kk == n) {   // every position is selected
+    for (int i = tid; i < n; i += kFusedThreads) out[i] = i;
+    return;
+  }
+
+  // ---- stream: scores of this wave's stages into sm.key
+  const int nst = (n + kSub - 1) / kSub;
+  const int nsub = nst > wave ? (nst - wave + kFusedWaves - 1) / kFusedWaves : 0;
+  uint32_t kmn = ~0u, kmx = 0u;
+  if (nsub > 0) {
+    const int64_t qrow = (int64_t)b * p.T + t;
+    uint4 a[MB][DI / 16];
+    float wv[MB][16];
+    load_query<DI, MB, FP8>(p.q_idx + qrow * p.H_I * DI, p.w + qrow * p.H_I,
+                            p.H_I, lane, a, wv);
+    uint4* tile = sm.u.tile[wave];
+    const int last = nsub - 1;
+    // first position of the wave's stage j (stages past the last repeat it
+    // and are parked: their loads read nothing)
+    const auto at = [&](int j) { return (wave + kFusedWaves * min(j, last)) * kSub; };
+    const auto put = [&](int j, float sc) {
+      const int s = (wave + kFusedWaves * j) * kSub + lane;
+      if (lane < kSub && s < n) {
+        const uint32_t k = score_key(sc);
+        sm.key[s] = k;
+        kmn = min(kmn, k);
+        kmx = max(kmx, k);
+      }
+    };
+    if constexpr (FP8) {
+      uint32_t* scl = reinterpret_cast<uint32_t*>(tile + kSub * DI / 16);
+      StageF8<DI> st[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        stage_load_f8<DI>(st[u], p.keys, b, at(u), lane, u > last);
+      for (int i = 0; i < nsub; i += 4) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          stage_store_f8<DI>(st[u], tile, scl, lane);
+          stage_load_f8<DI>(st[u], p.keys, b, at(i + u + 4), lane,
+                            i + u + 4 > last);
+          const float sc = tile_scores_f8<DI, MB>(tile, a, wv, scl, lane);
+          if (i + u < nsub) put(i + u, sc);
+        }
+      }
+    } else {
+      Stage<DI> s0, s1;
+      stage_load<DI>(s0, p.keys, b, at(0), lane, false);
+      stage_load<DI>(s1, p.keys, b, at(1), lane, 1 > last);
+      for (int i = 0; i < nsub; i += 2) {
+        stage_store<DI>(s0, tile, lane);
+        stage_load<DI>(s0, p.keys, b, at(i + 2), lane, i + 2 > last);
+        put(i, tile_scores<DI, MB>(tile, a, wv, lane));
+        stage_store<DI>(s1, tile, lane);
+        stage_load<DI>(s1, p.keys, b, at(i + 3), lane, i + 3 > last);
+        const float sc = tile_scores<DI, MB>(tile, a, wv, lane);
+        if (i + 1 < nsub) put(i + 1, sc);
+      }
+    }
+  }
+#pragma unroll
+  for (int m = 1; m < kWave; m <<= 1) {
+    kmn = min(kmn, (uint32_t)__shfl_xor((int)kmn, m));
+    kmx = max(kmx, (uint32_t)__shfl_xor((int)kmx, m));
+  }
+  __syncthreads();   // keys complete; the stage tiles are free
+  if (lane == 0) {
+    sm.u.t.mn[wave] = kmn;
+    sm.u.t.mx[wave] = kmx;
+  }
+  __syncthreads();
+  uint32_t lo = sm.u.t.mn[0], hi = sm.u.t.mx[0];
+#pragma unroll
+  for (int w = 1; w < kFusedWaves; ++w) {
+    lo = min(lo, sm.u.t.mn[w]);
+    hi = max(hi, sm.u.t.mx[w]);
+  }
+
+  // ---- select: the K-th largest key thr, digit by digit.  Invariant: the
+  // window [lo, hi] holds at least `rem` keys, and exactly kk - rem keys
+  // lie above it.  Each pass leaves a window below 2^shift wide, so a
+  // 32-bit range takes at most three passes (shifts 21, 10, 0).
+  uint32_t rem = (uint32_t)kk;
+  constexpr int kBinsPT = kFusedBins / kFusedThreads;
+  for (int pass = 0; pass < 4 && lo != hi; ++pass) {   // uniform
+    const uint32_t range = hi - lo;
+    const int shift = max(0, 32 - (int)__builtin_clz(range) - kFusedDigitBits);
+    const int nb = (int)(range >> shift) + 1;
+    for (int i = tid; i < nb; i += kFusedThreads) sm.u.t.hist[i] = 0u;
+    if (tid == 0) {
+      sm.u.t.pick = 0u;
+      sm.u.t.above = 0u;
+    }
+    __syncthreads();
+    for (int s = tid; s < n; s += kFusedThreads) {
+      const uint32_t k = sm.key[s];
+      if (k >= lo && k <= hi) atomicAdd(&sm.u.t.hist[(k - lo) >> shift], 1u);
+    }
+    __syncthreads();
+    // thread tid owns digits tid*kBinsPT .. +kBinsPT-1; keys in the digits
+    // of higher threads, by a suffix sum over the threads
+    uint32_t c[kBinsPT], own = 0u;
+#pragma unroll
+    for (int i = 0; i < kBinsPT; ++i) {
+      const int d = tid * kBinsPT + i;
+      c[i] = d < nb ? sm.u.t.hist[d] : 0u;
+      own += c[i];
+    }
+    uint32_t incl = own;   // inclusive prefix over the wave's lanes
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+      const uint32_t y = (uint32_t)__shfl_up((int)incl, o);
+      if (lane >= o) incl += y;
+    }
+    const uint32_t wtot = (uint32_t)__shfl((int)incl, kWave - 1);
+    if (lane == 0) sm.u.t.tot[wave] = wtot;
+    __syncthreads();
+    uint32_t run = wtot - incl;   // keys in higher lanes of this wave
+    for (int w = wave + 1; w < kFusedWaves; ++w) run += sm.u.t.tot[w];
+#pragma unroll
+    for (int i = kBinsPT - 1; i >= 0; --i) {
+      if (run < rem && rem <= run + c[i]) {
+        sm.u.t.pick = (uint32_t)(tid * kBinsPT + i);
+        sm.u.t.above = run;
+      }
+      run += c[i];
+    }
+    __syncthreads();
+    const uint32_t d = sm.u.t.pick;
+    rem -= sm.u.t.above;
+    const uint32_t nlo = lo + (d << shift);
+    hi = (int)d + 1 == nb ? hi : lo + ((d + 1) << shift) - 1u;
+    lo = nlo;
+    __syncthreads();   // pick and the sums are read before they are reused
+  }
+  const uint32_t thr = lo, need = rem;
+
+  // ---- emit: wave w takes positions [w*C, (w+1)*C); keys equal to thr
+  // are taken in position order, the first `need` of them
+  const int C = (n + kFusedThreads - 1) / kFusedThreads * kWave;
+  const int s0 = wave * C, s1 = min(s0 + C, n);
+  uint32_t ngt = 0u, neq = 0u;
+  for (int s = s0; s < s1; s += kWave) {
+    const uint32_t k = s + lane < s1 ? sm.key[s + lane] : 0u;
+    ngt += __builtin_popcountll(__ballot(k > thr));
+    neq += __builtin_popcountll(__ballot(k == thr));
+  }
+  if (lane == 0) {
+    sm.u.t.ngt[wave] = ngt;
+    sm.u.t.neq[wave] = neq;
+  }
+  __syncthreads();
+  uint32_t gt_before = 0u, eq_before = 0u;
+  for (int w = 0; w < wave; ++w) {
+    gt_before += sm.u.t.ngt[w];
+    eq_before += sm.u.t.neq[w];
+  }
+  uint32_t slot = gt_before + min(need, eq_before), eqr = eq_before;
+  for (int s = s0; s < s1; s += kWave) {
+    const uint32_t k = s + lane < s1 ? sm.key[s + lane] : 0u;
+    const uint64_t em = __ballot(k == thr);
+    const bool sel = k > thr || (k == thr && eqr + fused_lanes_below(em) < need);
+    const uint64_t sm_ = __ballot(sel);
+    const uint32_t o = slot + fused_lanes_below(sm_);   // < kk
+    if (sel && o < (uint32_t)K) out[o] = s + lane;
+    eqr += __builtin_popcountll(em);
+    slot += __builtin_popcountll(sm_);
+  }
+}
+
+template <int DI, int MB, bool FP8>
+hipError_t launch_fused(const IndexerLaunch& p, int K, int32_t* idx,
+                        hipStream_t stream) {
+  hipLaunchKernelGGL((index_topk_kernel<DI, MB, FP8>), dim3(p.B * p.T),
+                     dim3(kFusedThreads), 0, stream, p, K, idx);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_indexer(const IndexerLaunch& p, hipStream_t stream) {
@@ -1079,6 +1321,23 @@ hipError_t launch_indexer(const IndexerLaunch& p, hipStream_t stream) {
 
 int indexer_span_kpw(const IndexerLaunch& p) {
   return p.T >= kTileQ ? 0 : stream_kpw(p);
+}
+
+hipError_t launch_index_topk(const IndexerLaunch& p, int K, int32_t* idx,
+                             hipStream_t stream) {
+  const bool mb1 = p.H_I <= 32;
+  if (p.d_I == 128) {
+    if (p.keys.fp8)
+      return mb1 ? launch_fused<128, 1, true>(p, K, idx, stream)
+                 : launch_fused<128, 2, true>(p, K, idx, stream);
+    return mb1 ? launch_fused<128, 1, false>(p, K, idx, stream)
+               : launch_fused<128, 2, false>(p, K, idx, stream);
+  }
+  if (p.keys.fp8)
+    return mb1 ? launch_fused<64, 1, true>(p, K, idx, stream)
+               : launch_fused<64, 2, true>(p, K, idx, stream);
+  return mb1 ? launch_fused<64, 1, false>(p, K, idx, stream)
+             : launch_fused<64, 2, false>(p, K, idx, stream);
 }
 
 }  // namespace dsa

@@ -196,3 +196,43 @@ def test_decode_step_static_validation():
                               64) > dsa.STATIC_SCRATCH_BYTES
     assert f(**big) == WS
     assert b"static scratch" in lib.dsa_last_error()
+
+
+def test_indexer_topk_validation():
+    """The fused indexer + Top-K checks its arguments before any HIP call:
+    rows beyond the LDS bound, quantised queries and the cache fields it
+    reads."""
+    c = dsa._PagedCacheC(64, 10, 1024, 0, 0, 0x1000, None, None, None,
+                         0x1000, 0x1000)
+
+    def f(cache=c, **kw):
+        a = dict(B=2, T=1, H_I=64, d_I=128, K=64, msl=256, qp=None, qm=0,
+                 out=FAKE)
+        a.update(kw)
+        return lib.dsa_indexer_topk(a["B"], a["T"], a["H_I"], a["d_I"], a["K"],
+                                    ctypes.byref(cache) if cache else None,
+                                    a["msl"], FAKE, a["qm"], FAKE, a["qp"],
+                                    a["out"], None)
+    assert f(cache=None) == NULL
+    assert f(out=None) == NULL
+    assert f(T=2) == NULL                       # q_pos required for T > 1
+    assert f(K=0) == UNSUP and f(K=2049) == UNSUP
+    assert f(H_I=65) == UNSUP and f(d_I=96) == UNSUP
+    assert f(msl=dsa.FUSED_MAX_CONTEXT + 1) == UNSUP
+    assert b"LDS" in lib.dsa_last_error()
+    assert f(msl=0) == SHAPE
+    short = dsa._PagedCacheC(64, 10, 4, 0, 0, 0x1000, None, None, None,
+                             0x1000, 0x1000)
+    assert f(cache=short, msl=257) == SHAPE     # beyond max_pages * 64
+    assert f(qm=-1) == UNSUP
+    assert f(qm=1) == UNSUP                     # quantised queries: MX keys
+    mx = dsa._PagedCacheC(64, 10, 1024, 1, 0, 0x1000, 0x1000, None, None,
+                          0x1000, 0x1000)
+    assert f(cache=mx, qm=1) == UNSUP           # two-kernel path only
+    assert b"DSA_Q_BF16" in lib.dsa_last_error()
+    assert f(cache=dsa._PagedCacheC(64, 10, 1024, 1, 0, 0x1000, None, None,
+                                    None, 0x1000, 0x1000)) == NULL
+    assert f(cache=dsa._PagedCacheC(64, 10, 1024, 2, 0, 0x1000, 0x1000, None,
+                                    None, 0x1000, 0x1000)) == UNSUP
+    assert f(cache=dsa._PagedCacheC(64, 10, 1024, 0, 0, 0x1000, None, None,
+                                    None, None, 0x1000)) == NULL

@@ -1,0 +1,118 @@
+"""The single-kernel indexer + Top-K (dsa_indexer_topk) against the CPU
+oracle: the selected positions must equal the oracle's Top-K of the oracle's
+scores exactly (ties to the lower position), on the full decode batches
+(bf16 and MX keys, 32 rows of 32768), on short, ragged and paged rows, rows
+no longer than K, several queries per sequence, one head or one key, and
+inputs with few distinct scores (long runs of ties)."""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import indexed_sparse_attention_lightning_amd as dsa
+import oracle
+import workloads as wk
+from workloads.device import to_device
+
+from gpu_helpers import assert_idx_equal, paged_cache, run_decode_step
+
+pytestmark = pytest.mark.gpu
+
+W = wk.WORKLOADS
+
+
+def oracle_idx(inp, rows):
+    """Oracle indexer scores and Top-K of the requested rows (no attention)."""
+    wl = inp.wl
+    idx = np.full((wl.B, wl.T, wl.top_k), -2, dtype=np.int64)
+    for b in sorted({b for b, _ in rows}):
+        keys = oracle.cache_rows(inp.k_idx.data, inp.k_idx.scale,
+                                 inp.k_idx.quantized, inp.page_table[b],
+                                 np.arange(inp.seq_lens[b]))
+        for bb, t in rows:
+            if bb != b:
+                continue
+            qp = int(inp.q_pos[b, t])
+            n = min(qp + 1, int(inp.seq_lens[b]))
+            s = oracle.indexer_scores_row(oracle.indexer_queries(inp.q_idx[b, t]),
+                                          inp.w[b, t], keys[:n])
+            idx[b, t] = oracle.topk_row(s, qp, wl.top_k)
+    return idx
+
+
+def run_fused(inp, d, pass_qpos=None):
+    wl = inp.wl
+    use_qpos = (wl.T > 1) if pass_qpos is None else pass_qpos
+    idx = dsa.indexer_topk(paged_cache(d), d["q_idx"], d["w"], wl.top_k,
+                           max_seq_len=int(inp.seq_lens.max()),
+                           q_pos=d["q_pos"] if use_qpos else None)
+    torch.cuda.synchronize()
+    return idx.cpu().numpy()
+
+
+CASES = {
+    "tiny": W["tiny"],
+    # MX keys, d_I 64, 40 heads (a partial second block), ragged lengths
+    # with partial last stages, scattered pages
+    "paged_fp8_ragged": wk.Workload("paged_fp8_ragged", 501, B=3, T=1, H_I=40,
+                                    d_I=64, top_k=300, H=16, int_range=4,
+                                    quantized=True, paged_random=True,
+                                    L_min=700, L_max=3000),
+    # rows shorter than K (every position selected) next to longer ones
+    "short_rows": wk.Workload("short_rows", 502, B=4, T=1, H_I=64, d_I=128,
+                              top_k=1024, H=16, int_range=4, quantized=False,
+                              paged_random=True, L_min=1, L_max=4100),
+    # several queries per sequence (q_pos given), causal rows of each
+    "chunk": wk.Workload("chunk", 503, B=2, T=5, H_I=16, d_I=128, top_k=256,
+                         H=16, int_range=3, quantized=False, paged_random=True,
+                         L=2000, first_pos=1995),
+    # values in [-1, 1]: few distinct scores, long runs of equal keys
+    "ties": wk.Workload("ties", 504, B=2, T=1, H_I=8, d_I=64, top_k=500,
+                        H=16, int_range=1, quantized=False, paged_random=False,
+                        L=6000),
+    # one head, K = 1
+    "one_head_k1": wk.Workload("one_head_k1", 505, B=2, T=1, H_I=1, d_I=128,
+                               top_k=1, H=16, int_range=4, quantized=True,
+                               paged_random=True, L=5000),
+    # the longest row the fused kernel holds, MX keys, scattered pages
+    "max_row_fp8": wk.Workload("max_row_fp8", 506, B=2, T=1, H_I=64, d_I=128,
+                               top_k=2048, H=16, int_range=4, quantized=True,
+                               paged_random=True, L=32768),
+}
+
+
+@pytest.mark.parametrize("name", sorted(CASES))
+def test_fused_matches_oracle(name):
+    wl = CASES[name]
+    print(f"fused case {name}: {dataclasses.asdict(wl)}", flush=True)
+    inp = wk.generate(wl)
+    d = to_device(inp)
+    rows = [(b, t) for b in range(wl.B) for t in range(wl.T)]
+    ref = oracle_idx(inp, rows)
+    assert_idx_equal(run_fused(inp, d), ref, rows)
+    if wl.T == 1:   # q_pos given explicitly: the same rows
+        assert_idx_equal(run_fused(inp, d, pass_qpos=True), ref, rows)
+
+
+@pytest.mark.parametrize("name", ["decode", "decode_fp8"])
+def test_fused_full_decode(name):
+    """32 rows of 32768 positions, every row against the oracle and the
+    two-kernel decode step's selection."""
+    wl = W[name]
+    print(f"fused full {name}", flush=True)
+    inp = wk.generate(wl)
+    d = to_device(inp)
+    rows = [(b, 0) for b in range(wl.B)]
+    got = run_fused(inp, d)
+    assert_idx_equal(got, oracle_idx(inp, rows), rows)
+    two, _, _ = run_decode_step(inp, d)
+    assert np.array_equal(got, two)
+
+
+def test_fused_repeat_is_identical():
+    """Two launches give the same bytes (no state survives a launch)."""
+    wl = CASES["ties"]
+    inp = wk.generate(wl)
+    d = to_device(inp)
+    assert np.array_equal(run_fused(inp, d), run_fused(inp, d))
