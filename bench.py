@@ -390,6 +390,56 @@ def prefill_kernels(stream, steps=5, warmup=2, oracle_budget_s=0.0,
     }
 
 
+def fused_comparison(stream, steps=20, warmup=5):
+    """dsa_indexer_topk (scoring and Top-K in one kernel, the scores kept in
+    LDS) against dsa_indexer_scores followed by dsa_topk (scores through
+    HBM), on the bf16 decode batch's shape (32 rows of 32768) and on 256 rows
+    of 4096 (the same key bytes, one row per CU).  Integer-valued keys and
+    queries in [-4, 4], power-of-two weights; both paths' indices compared."""
+    import torch
+    import indexed_sparse_attention_lightning_amd as dsa
+    res = {}
+    for B, L in ((32, 32768), (256, 4096)):
+        P, K, d_I, H_I = B * L // 64, 2048, 128, 64
+        g = torch.Generator(device="cuda")
+        g.manual_seed(B)
+        kidx = torch.randint(-4, 5, (P, 64, d_I), device="cuda",
+                             generator=g).to(torch.bfloat16)
+        kv = torch.empty((P, 64, 576), dtype=torch.bfloat16, device="cuda")
+        pt = torch.arange(P, dtype=torch.int32, device="cuda").view(B, -1)
+        sl = torch.full((B,), L, dtype=torch.int32, device="cuda")
+        q_idx = torch.randint(-4, 5, (B, 1, H_I, d_I), device="cuda",
+                              generator=g).to(torch.bfloat16)
+        w = torch.pow(2.0, -torch.randint(0, 4, (B, 1, H_I), device="cuda",
+                                          generator=g).float())
+        q_pos = (sl - 1).view(B, 1).contiguous()
+        cache = dsa.PagedCache(kidx=kidx, kv=kv, page_table=pt, seq_lens=sl)
+        i1 = torch.empty((B, 1, K), dtype=torch.int32, device="cuda")
+        i2 = torch.empty_like(i1)
+        scores = torch.empty((B, 1, L), dtype=torch.float32, device="cuda")
+        kc = kidx.view(B, L, d_I)
+
+        def fused(i):
+            dsa.indexer_topk(cache, q_idx, w, K, L, q_pos=q_pos, idx_out=i1)
+
+        def two(i):
+            dsa.indexer_scores(q_idx, w, kc, q_pos, out=scores)
+            dsa.topk(scores, q_pos, K, out=i2)
+
+        ms_f = time_loop(fused, steps, warmup, stream)
+        ms_2 = time_loop(two, steps, warmup, stream)
+        torch.cuda.synchronize()
+        kbytes = B * L * d_I * 2
+        res[f"{B}x{L}"] = {
+            "fused_us": round(ms_f * 1e3, 2),
+            "indexer_then_topk_us": round(ms_2 * 1e3, 2),
+            "fused_key_gbps": round(kbytes / (ms_f * 1e-3) / 1e9, 1),
+            "same_idx": bool(torch.equal(i1, i2))}
+        del kidx, kv, scores, cache
+        torch.cuda.empty_cache()
+    return res
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -407,6 +457,8 @@ def main(argv=None):
                     help="time only this decode configuration (10 steps after "
                          "3 warm-up steps) and print its JSON object; for "
                          "kernel traces")
+    ap.add_argument("--no-fused", action="store_true",
+                    help="skip the fused indexer + Top-K comparison")
     ap.add_argument("--kernels-only", action="store_true",
                     help="run one 256 MiB device copy (counter calibration) "
                          "and one decode step, then exit (for rocprofv3 "
@@ -581,6 +633,8 @@ def main(argv=None):
             "algorithmic_bytes_per_launch": ib},
     }
     del reps, caches, outs, scores
+    if not args.no_fused:
+        line["fused_indexer_topk"] = fused_comparison(stream)
     if not args.no_prefill:
         line["prefill"] = prefill_kernels(
             stream, oracle_budget_s=0 if args.no_cpu_baseline else 4.0)

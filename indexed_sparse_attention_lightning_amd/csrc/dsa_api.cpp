@@ -251,6 +251,28 @@ dsa_status dsa_sparse_mla_attn(int B, int T, int L, int H, int K,
 
 namespace {
 
+// The decode step's sparse attention over the paged latent cache.
+dsa_status launch_attention(const dsa_paged_cache* cache, int B, int T, int H,
+                            int K, float softmax_scale, const void* q,
+                            float* out, float* lse, const int32_t* idx,
+                            float* partial, hipStream_t st) {
+  dsa::AttnLaunch aa{};
+  aa.B = B; aa.T = T; aa.H = H; aa.K = K;
+  aa.q = static_cast<const uint16_t*>(q);
+  aa.kv = kv_view(cache->kv, cache->kv_scale, cache->kv_dtype,
+                  cache->page_table, cache->max_pages_per_seq, 0,
+                  (uint64_t)cache->num_pages * DSA_PAGE_SIZE, cache->num_pages);
+  aa.idx = idx;
+  aa.seq_lens = cache->seq_lens;
+  aa.scale = softmax_scale;
+  aa.out = out;
+  aa.lse = lse;
+  aa.partial = partial;
+  aa.splits = dsa::attn_splits(B * T, K);
+  return hip_status(dsa::launch_sparse_mla(aa, st),
+                    "dsa_decode_step: sparse attention");
+}
+
 dsa_status decode_step_impl(int B, int T, int H_I, int d_I, int H, int K,
                            float softmax_scale, const dsa_paged_cache* cache,
                            int max_seq_len, const void* q_idx, int q_mode,
@@ -335,6 +357,19 @@ dsa_status decode_step_impl(int B, int T, int H_I, int d_I, int H, int K,
   ia.row_len = max_seq_len;
   ia.keys_out = 1;   // the Top-K below reads keys: no conversion there
   ia.q8 = q_mode == DSA_Q_MX32;
+  // With a row for every CU, the single kernel that keeps each row's scores
+  // in LDS beats the score stream plus the Top-K launch (256 rows of 4096
+  // positions: 55-60 us against 51 + 11 us and a launch; 256 of 32768:
+  // 366-376 against 365 + 15 us); with fewer rows it leaves CUs idle (128
+  // rows of 8192: 73 against 50 + 10 us).  Several queries per sequence
+  // share key reads in the query-tiled indexer instead.
+  if (!ia.q8 && T < 8 && tokens >= 256 && max_seq_len <= dsa::kFusedMaxLen) {
+    ia.row_len = max_seq_len;
+    if (hipError_t e = dsa::launch_index_topk(ia, K, idx, st))
+      return hip_status(e, "dsa_decode_step: fused indexer and Top-K");
+    return launch_attention(cache, B, T, H, K, softmax_scale, q, out, lse,
+                            idx, partial, st);
+  }
   // the stream kernels also leave each wave's key range for the Top-K
   const int span_kpw = dsa::indexer_span_kpw(ia);
   const bool spans = span_kpw > 0 &&
@@ -354,21 +389,8 @@ dsa_status decode_step_impl(int B, int T, int H_I, int d_I, int H, int K,
   if (hipError_t e = dsa::launch_topk(ta, topk_ws, topk_bytes, st))
     return hip_status(e, "dsa_decode_step: topk");
 
-  dsa::AttnLaunch aa{};
-  aa.B = B; aa.T = T; aa.H = H; aa.K = K;
-  aa.q = static_cast<const uint16_t*>(q);
-  aa.kv = kv_view(cache->kv, cache->kv_scale, cache->kv_dtype,
-                  cache->page_table, cache->max_pages_per_seq, 0,
-                  (uint64_t)cache->num_pages * DSA_PAGE_SIZE, cache->num_pages);
-  aa.idx = idx;
-  aa.seq_lens = cache->seq_lens;
-  aa.scale = softmax_scale;
-  aa.out = out;
-  aa.lse = lse;
-  aa.partial = partial;
-  aa.splits = dsa::attn_splits((int)tokens, K);
-  return hip_status(dsa::launch_sparse_mla(aa, st),
-                    "dsa_decode_step: sparse attention");
+  return launch_attention(cache, B, T, H, K, softmax_scale, q, out, lse, idx,
+                          partial, st);
 }
 
 }  // namespace

@@ -1164,17 +1164,22 @@ __global__ __launch_bounds__(kFusedThreads, 1) void index_topk_kernel(
         }
       }
     } else {
-      Stage<DI> s0, s1;
-      stage_load<DI>(s0, p.keys, b, at(0), lane, false);
-      stage_load<DI>(s1, p.keys, b, at(1), lane, 1 > last);
-      for (int i = 0; i < nsub; i += 2) {
-        stage_store<DI>(s0, tile, lane);
-        stage_load<DI>(s0, p.keys, b, at(i + 2), lane, i + 2 > last);
-        put(i, tile_scores<DI, MB>(tile, a, wv, lane));
-        stage_store<DI>(s1, tile, lane);
-        stage_load<DI>(s1, p.keys, b, at(i + 3), lane, i + 3 > last);
-        const float sc = tile_scores<DI, MB>(tile, a, wv, lane);
-        if (i + 1 < nsub) put(i + 1, sc);
+      // two stages in flight: three or four measured no faster (the wave
+      // is bound by issuing its own LDS, matrix and epilogue work)
+      constexpr int NS = 2;
+      Stage<DI> st[NS];
+#pragma unroll
+      for (int u = 0; u < NS; ++u)
+        stage_load<DI>(st[u], p.keys, b, at(u), lane, u > last);
+      for (int i = 0; i < nsub; i += NS) {
+#pragma unroll
+        for (int u = 0; u < NS; ++u) {
+          stage_store<DI>(st[u], tile, lane);
+          stage_load<DI>(st[u], p.keys, b, at(i + u + NS), lane,
+                         i + u + NS > last);
+          const float sc = tile_scores<DI, MB>(tile, a, wv, lane);
+          if (i + u < nsub) put(i + u, sc);
+        }
       }
     }
   }

@@ -15,7 +15,8 @@ import oracle
 import workloads as wk
 from workloads.device import to_device
 
-from gpu_helpers import assert_idx_equal, paged_cache, run_decode_step
+from gpu_helpers import (assert_idx_equal, check_workload, paged_cache,
+                         run_decode_step)
 
 pytestmark = pytest.mark.gpu
 
@@ -116,3 +117,29 @@ def test_fused_repeat_is_identical():
     inp = wk.generate(wl)
     d = to_device(inp)
     assert np.array_equal(run_fused(inp, d), run_fused(inp, d))
+
+
+# 256 or more query rows with fewer than 8 queries per sequence, bf16
+# queries and rows within 32768 positions: dsa_decode_step runs its indexer
+# and Top-K as the single fused kernel
+STEP_CASES = {
+    "step_256_rows": wk.Workload("step_256_rows", 601, B=256, T=1, H_I=32,
+                                 d_I=64, top_k=128, H=16, int_range=4,
+                                 quantized=False, paged_random=True,
+                                 L_min=60, L_max=1500),
+    "step_128x2_mx": wk.Workload("step_128x2_mx", 602, B=128, T=2, H_I=64,
+                                 d_I=128, top_k=256, H=16, int_range=4,
+                                 quantized=True, paged_random=True, L=1200,
+                                 first_pos=1198),
+}
+
+
+@pytest.mark.parametrize("name", sorted(STEP_CASES))
+def test_decode_step_many_rows(name):
+    """The whole decode step on 256 query rows: every row's indices exact and
+    its attention within tolerance against the oracle, and the indices equal
+    to dsa_indexer_topk's."""
+    wl = STEP_CASES[name]
+    print(f"decode step, fused rows {name}", flush=True)
+    inp, d, _, (idx, _, _) = check_workload(wl)
+    assert np.array_equal(idx, run_fused(inp, d))
