@@ -394,17 +394,27 @@ def fused_comparison(stream, steps=20, warmup=5):
     """dsa_indexer_topk (scoring and Top-K in one kernel, the scores kept in
     LDS) against dsa_indexer_scores followed by dsa_topk (scores through
     HBM), on the bf16 decode batch's shape (32 rows of 32768) and on 256 rows
-    of 4096 (the same key bytes, one row per CU).  Integer-valued keys and
-    queries in [-4, 4], power-of-two weights; both paths' indices compared."""
+    of 4096 (the same key bytes, one row per CU), bf16 keys and MX block-32
+    e4m3 keys.  Integer-valued keys and queries in [-4, 4] (exact in e4m3
+    with unit scales), power-of-two weights; both paths' indices compared."""
     import torch
     import indexed_sparse_attention_lightning_amd as dsa
     res = {}
-    for B, L in ((32, 32768), (256, 4096)):
+    for B, L, mx in ((32, 32768, False), (256, 4096, False),
+                     (256, 4096, True)):
         P, K, d_I, H_I = B * L // 64, 2048, 128, 64
         g = torch.Generator(device="cuda")
         g.manual_seed(B)
-        kidx = torch.randint(-4, 5, (P, 64, d_I), device="cuda",
-                             generator=g).to(torch.bfloat16)
+        vals = torch.randint(-4, 5, (P, 64, d_I), device="cuda", generator=g)
+        kscale = kc_scale = None
+        if mx:
+            kidx = vals.float().to(torch.float8_e4m3fn).view(torch.uint8)
+            kscale = torch.full((P, 64, d_I // 32), 127, dtype=torch.uint8,
+                                device="cuda")
+            kc_scale = kscale.view(B, L, d_I // 32)
+        else:
+            kidx = vals.to(torch.bfloat16)
+        del vals
         kv = torch.empty((P, 64, 576), dtype=torch.bfloat16, device="cuda")
         pt = torch.arange(P, dtype=torch.int32, device="cuda").view(B, -1)
         sl = torch.full((B,), L, dtype=torch.int32, device="cuda")
@@ -413,7 +423,8 @@ def fused_comparison(stream, steps=20, warmup=5):
         w = torch.pow(2.0, -torch.randint(0, 4, (B, 1, H_I), device="cuda",
                                           generator=g).float())
         q_pos = (sl - 1).view(B, 1).contiguous()
-        cache = dsa.PagedCache(kidx=kidx, kv=kv, page_table=pt, seq_lens=sl)
+        cache = dsa.PagedCache(kidx=kidx, kv=kv, page_table=pt, seq_lens=sl,
+                               kidx_scale=kscale)
         i1 = torch.empty((B, 1, K), dtype=torch.int32, device="cuda")
         i2 = torch.empty_like(i1)
         scores = torch.empty((B, 1, L), dtype=torch.float32, device="cuda")
@@ -423,19 +434,20 @@ def fused_comparison(stream, steps=20, warmup=5):
             dsa.indexer_topk(cache, q_idx, w, K, L, q_pos=q_pos, idx_out=i1)
 
         def two(i):
-            dsa.indexer_scores(q_idx, w, kc, q_pos, out=scores)
+            dsa.indexer_scores(q_idx, w, kc, q_pos, k_scale=kc_scale,
+                               out=scores)
             dsa.topk(scores, q_pos, K, out=i2)
 
         ms_f = time_loop(fused, steps, warmup, stream)
         ms_2 = time_loop(two, steps, warmup, stream)
         torch.cuda.synchronize()
-        kbytes = B * L * d_I * 2
-        res[f"{B}x{L}"] = {
+        kbytes = B * L * (d_I + d_I // 32 if mx else d_I * 2)
+        res[f"{B}x{L}" + ("_mx" if mx else "")] = {
             "fused_us": round(ms_f * 1e3, 2),
             "indexer_then_topk_us": round(ms_2 * 1e3, 2),
             "fused_key_gbps": round(kbytes / (ms_f * 1e-3) / 1e9, 1),
             "same_idx": bool(torch.equal(i1, i2))}
-        del kidx, kv, scores, cache
+        del kidx, kv, scores, cache, kscale, kc_scale
         torch.cuda.empty_cache()
     return res
 
@@ -451,7 +463,7 @@ def main(argv=None):
     ap.add_argument("--no-configs", action="store_true",
                     help="skip the FP8 and ragged decode configurations")
     ap.add_argument("--only-config",
-                    choices=["decode_fp8", "decode_fp8_q8", "ragged",
+                    choices=["decode_fp8", "decode_fp8_q8", "ragged", "fused",
                              "decode_t128", "prefill", "prefill_quantized",
                              "prefill_from_start"],
                     help="time only this decode configuration (10 steps after "
@@ -477,7 +489,9 @@ def main(argv=None):
 
     if args.only_config:
         st = torch.cuda.current_stream()
-        if args.only_config.startswith("prefill"):
+        if args.only_config == "fused":
+            res = fused_comparison(st)
+        elif args.only_config.startswith("prefill"):
             res = prefill_kernels(
                 st, quantized=args.only_config == "prefill_quantized",
                 from_start=args.only_config == "prefill_from_start")

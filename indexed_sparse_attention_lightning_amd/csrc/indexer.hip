@@ -1073,23 +1073,115 @@ hipError_t launch_q8(const IndexerLaunch& p, hipStream_t stream) {
 //     position order go to their ascending output slots.
 // A row is one CU's work here, against eight or more CUs in the two-kernel
 // path, so the single kernel keeps pace only with about one row per CU.
-constexpr int kFusedWaves = 4;
+constexpr int kFusedWaves = 8;
 constexpr int kFusedThreads = kFusedWaves * kWave;
 constexpr int kFusedDigitBits = 11;
 constexpr int kFusedBins = 1 << kFusedDigitBits;
+constexpr int kPassDI = 64;   // features of a stage in LDS at a time
 
-// 16-byte words of a wave's stage tile: bf16 rows, or FP8 codes followed by
-// the stage's 32 scale words
-template <int DI, bool FP8>
+// A wave's LDS tile holds 64 features of its stage's 32 keys (a stage of
+// 128-feature keys goes through it in two passes), laid out as a whole
+// stage of 64-feature keys: bf16 rows, or FP8 codes followed by the stage's
+// 32 scale words.  Eight such tiles and 32768 keys fill the 160 KiB.
+template <bool FP8>
 constexpr int fused_tile_words() {
-  return FP8 ? (kSub * DI + kSub * 4) / 16 : KeyLayout<DI>::kTileBytes / 16;
+  return FP8 ? (kSub * kPassDI + kSub * 4) / 16
+             : KeyLayout<kPassDI>::kTileBytes / 16;
 }
 
-template <int DI, bool FP8>
+// Pass p of a bf16 stage into the tile: chunks [8p, 8p+8) of every key
+// (the lanes holding them store; a lane's chunk index is fixed by its lane).
+template <int DI>
+__device__ __forceinline__ void stage_store_pass(const Stage<DI>& st,
+                                                 uint4* tile, int lane,
+                                                 int p) {
+  using KL = KeyLayout<DI>;
+  using KP = KeyLayout<kPassDI>;
+#pragma unroll
+  for (int i = 0; i < Stage<DI>::N; ++i) {
+    const int id = i * kWave + lane;
+    const int n = id / KL::kChunks, c = id % KL::kChunks;
+    if (c / KP::kChunks == p)
+      tile[n * KP::kChunks + KP::slot(n, c % KP::kChunks)] = st.v[i];
+  }
+}
+
+// The k-steps [4p, 4p+4) of tile_scores from a pass tile into acc.
+template <int DI, int MB>
+__device__ __forceinline__ void pass_products(const uint4* tile,
+                                              const uint4 (&a)[MB][DI / 16],
+                                              f32x16 (&acc)[MB], int lane,
+                                              int p) {
+  using KP = KeyLayout<kPassDI>;
+  const int n = lane & 31, h = lane >> 5;
+#pragma unroll
+  for (int k = 0; k < KP::kSteps; ++k) {
+    const uint4 bop = tile[n * KP::kChunks + KP::slot(n, 2 * k + h)];
+#pragma unroll
+    for (int m = 0; m < MB; ++m)
+      acc[m] = mfma32(a[m][p * KP::kSteps + k], bop, acc[m]);
+  }
+}
+
+// FP8 codes: pass p stores code chunks [4p, 4p+4) (MX blocks 2p, 2p+1).
+template <int DI>
+__device__ __forceinline__ void stage_store_f8_pass(const StageF8<DI>& st,
+                                                    uint4* tile, int lane,
+                                                    int p) {
+  using CL = CodeLayout<DI>;
+  using CP = CodeLayout<kPassDI>;
+#pragma unroll
+  for (int i = 0; i < CL::kLoads; ++i) {
+    const int id = i * kWave + lane;
+    const int n = id / CL::kChunks, c = id % CL::kChunks;
+    if (c / CP::kChunks == p)
+      tile[n * CP::kChunks + CP::slot(n, c % CP::kChunks)] = st.v[i];
+  }
+}
+
+template <int DI, int MB>
+__device__ __forceinline__ void pass_products_f8(const uint4* tile,
+                                                 const uint4 (&a)[MB][DI / 16],
+                                                 const uint32_t* scl,
+                                                 f32x16 (&acc)[MB], int lane,
+                                                 int p) {
+  using CP = CodeLayout<kPassDI>;
+  const int n = lane & 31, h = lane >> 5;
+  const uint32_t sc = scl[n];
+  uint4 cvs[kPassDI / 32];
+#pragma unroll
+  for (int jj = 0; jj < kPassDI / 32; ++jj)
+    cvs[jj] = tile[n * CP::kChunks + CP::slot(n, 2 * jj + h)];
+#pragma unroll
+  for (int jj = 0; jj < kPassDI / 32; ++jj) {
+    const int j = p * (kPassDI / 32) + jj;   // MX block of the key row
+    const uint32_t e = (sc >> (8 * j)) & 0xffu;
+    const uint4 b0 = dequant8_e4m3(make_uint2(cvs[jj].x, cvs[jj].y), e);
+    const uint4 b1 = dequant8_e4m3(make_uint2(cvs[jj].z, cvs[jj].w), e);
+#pragma unroll
+    for (int m = 0; m < MB; ++m) acc[m] = mfma32(a[m][2 * j], b0, acc[m]);
+#pragma unroll
+    for (int m = 0; m < MB; ++m) acc[m] = mfma32(a[m][2 * j + 1], b1, acc[m]);
+  }
+}
+
+// ReLU, head weights and the two wave halves: the score of key lane % 32.
+template <int MB>
+__device__ __forceinline__ float pass_epilogue(const f32x16 (&acc)[MB],
+                                               const float (&wv)[MB][16]) {
+  float s = 0.f;
+#pragma unroll
+  for (int m = 0; m < MB; ++m)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s += wv[m][r] * relu(acc[m][r]);
+  return s + swap_halves(s);
+}
+
+template <bool FP8>
 struct FusedShared {
   uint32_t key[kFusedMaxLen];   // score keys of positions 0 .. n-1
   union {
-    uint4 tile[kFusedWaves][fused_tile_words<DI, FP8>()];   // stream
+    uint4 tile[kFusedWaves][fused_tile_words<FP8>()];       // stream
     struct {                                                // select
       uint32_t hist[kFusedBins];
       uint32_t mn[kFusedWaves], mx[kFusedWaves];   // key range per wave
@@ -1108,8 +1200,8 @@ __device__ __forceinline__ uint32_t fused_lanes_below(uint64_t m) {
 template <int DI, int MB, bool FP8>
 __global__ __launch_bounds__(kFusedThreads, 1) void index_topk_kernel(
     IndexerLaunch p, int K, int32_t* idx) {
-  __shared__ FusedShared<DI, FP8> sm;
-  static_assert(sizeof(FusedShared<DI, FP8>) <= 160 * 1024, "LDS");
+  __shared__ FusedShared<FP8> sm;
+  static_assert(sizeof(FusedShared<FP8>) <= 160 * 1024, "LDS");
   const int tid = threadIdx.x, lane = lane_id();
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int r = blockIdx.x, b = r / p.T, t = r % p.T;
@@ -1147,8 +1239,9 @@ __global__ __launch_bounds__(kFusedThreads, 1) void index_topk_kernel(
         kmx = max(kmx, k);
       }
     };
+    constexpr int kPasses = DI / kPassDI;
     if constexpr (FP8) {
-      uint32_t* scl = reinterpret_cast<uint32_t*>(tile + kSub * DI / 16);
+      uint32_t* scl = reinterpret_cast<uint32_t*>(tile + kSub * kPassDI / 16);
       StageF8<DI> st[4];
 #pragma unroll
       for (int u = 0; u < 4; ++u)
@@ -1156,16 +1249,24 @@ __global__ __launch_bounds__(kFusedThreads, 1) void index_topk_kernel(
       for (int i = 0; i < nsub; i += 4) {
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-          stage_store_f8<DI>(st[u], tile, scl, lane);
-          stage_load_f8<DI>(st[u], p.keys, b, at(i + u + 4), lane,
-                            i + u + 4 > last);
-          const float sc = tile_scores_f8<DI, MB>(tile, a, wv, scl, lane);
+          f32x16 acc[MB];
+#pragma unroll
+          for (int m = 0; m < MB; ++m) acc[m] = f32x16{};
+          if (lane < kSub) scl[lane] = st[u].sc;
+#pragma unroll
+          for (int q = 0; q < kPasses; ++q) {
+            stage_store_f8_pass<DI>(st[u], tile, lane, q);
+            if (q == kPasses - 1)
+              stage_load_f8<DI>(st[u], p.keys, b, at(i + u + 4), lane,
+                                i + u + 4 > last);
+            pass_products_f8<DI, MB>(tile, a, scl, acc, lane, q);
+          }
+          const float sc = pass_epilogue<MB>(acc, wv);
           if (i + u < nsub) put(i + u, sc);
         }
       }
     } else {
-      // two stages in flight: three or four measured no faster (the wave
-      // is bound by issuing its own LDS, matrix and epilogue work)
+      // two stages in flight: three or four measured no faster
       constexpr int NS = 2;
       Stage<DI> st[NS];
 #pragma unroll
@@ -1174,10 +1275,18 @@ __global__ __launch_bounds__(kFusedThreads, 1) void index_topk_kernel(
       for (int i = 0; i < nsub; i += NS) {
 #pragma unroll
         for (int u = 0; u < NS; ++u) {
-          stage_store<DI>(st[u], tile, lane);
-          stage_load<DI>(st[u], p.keys, b, at(i + u + NS), lane,
-                         i + u + NS > last);
-          const float sc = tile_scores<DI, MB>(tile, a, wv, lane);
+          f32x16 acc[MB];
+#pragma unroll
+          for (int m = 0; m < MB; ++m) acc[m] = f32x16{};
+#pragma unroll
+          for (int q = 0; q < kPasses; ++q) {
+            stage_store_pass<DI>(st[u], tile, lane, q);
+            if (q == kPasses - 1)
+              stage_load<DI>(st[u], p.keys, b, at(i + u + NS), lane,
+                             i + u + NS > last);
+            pass_products<DI, MB>(tile, a, acc, lane, q);
+          }
+          const float sc = pass_epilogue<MB>(acc, wv);
           if (i + u < nsub) put(i + u, sc);
         }
       }
