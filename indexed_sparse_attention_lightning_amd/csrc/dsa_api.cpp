@@ -358,12 +358,12 @@ dsa_status decode_step_impl(int B, int T, int H_I, int d_I, int H, int K,
   ia.keys_out = 1;   // the Top-K below reads keys: no conversion there
   ia.q8 = q_mode == DSA_Q_MX32;
   // With a row for every CU, the single kernel that keeps each row's scores
-  // in LDS beats the score stream plus the Top-K launch (256 rows of 4096
-  // positions: 58 us against 51 + 11 us and a launch, 39 against 32 + 11
-  // with MX keys; 256 of 32768: 377 against 365 + 15 us); with fewer rows
-  // it leaves CUs idle (128 rows of 8192: 70 against 50 + 10 us).  Several
-  // queries per sequence share key reads in the query-tiled indexer
-  // instead.
+  // in LDS matches or beats the score stream plus the Top-K launch (256 rows
+  // of 4096 positions: 56 us against 47.5 + 9.7 us and a launch with bf16
+  // keys, 38 against 32 + 9.7 us with MX keys; 256 of 32768: 377 against
+  // 365 + 15 us); with fewer rows it leaves CUs idle (128 rows of 8192: 70
+  // against 50 + 10 us).  Several queries per sequence share key reads in
+  // the query-tiled indexer instead.
   if (!ia.q8 && T < 8 && tokens >= 256 && max_seq_len <= dsa::kFusedMaxLen) {
     ia.row_len = max_seq_len;
     if (hipError_t e = dsa::launch_index_topk(ia, K, idx, st))

@@ -8,15 +8,19 @@ top_k larger than the history, single heads, prefill chunks that start at
 position 0 or run to the end of the context, scattered pages, MX keys and
 KV, and the fully quantised indexer.  The bars are those of the other
 parity tests (exact Top-K sets and scores, attention within its tolerance).
+Cases with bf16 indexer queries also run the single-kernel indexer + Top-K
+(dsa_indexer_topk), whose indices must equal the oracle's.
 """
 import dataclasses
 
 import numpy as np
 import pytest
+import torch
 
+import indexed_sparse_attention_lightning_amd as dsa
 import workloads as wk
 
-from gpu_helpers import check_workload
+from gpu_helpers import assert_idx_equal, check_workload, paged_cache
 
 pytestmark = pytest.mark.gpu
 
@@ -60,4 +64,11 @@ CASES = [draw_case(i) for i in range(N_CASES)]
 def test_random_shapes(i):
     wl, q8 = CASES[i]
     print(f"case {i}: {dataclasses.asdict(wl)} q8={q8}", flush=True)
-    check_workload(wl, quantize_queries=q8)
+    inp, d, ref, _ = check_workload(wl, quantize_queries=q8)
+    if not q8:
+        idx = dsa.indexer_topk(paged_cache(d), d["q_idx"], d["w"], wl.top_k,
+                               max_seq_len=int(inp.seq_lens.max()),
+                               q_pos=d["q_pos"])
+        torch.cuda.synchronize()
+        rows = [(b, t) for b in range(wl.B) for t in range(wl.T)]
+        assert_idx_equal(idx.cpu().numpy(), ref["idx"], rows)
