@@ -1062,11 +1062,12 @@ hipError_t launch_q8(const IndexerLaunch& p, hipStream_t stream) {
 // Computation"; page "Day-0 Inference Adaptation and Performance
 // Optimization for New-Architecture Large Language Models", "Fusing the
 // Indexer to Reduce Intermediate Write-Backs").
-// One workgroup of four waves per query row:
-//   * stream: stage i of the row's 32-key stages goes to wave i % 4, which
-//     loads, transposes and scores it exactly as the stream kernel does and
-//     stores each score's order-preserving key at its position in LDS
-//     (32768 keys fill 128 KiB; the four stage tiles take the other 32 KiB);
+// One workgroup of eight waves (two per SIMD) per query row:
+//   * stream: stage i of the row's 32-key stages goes to wave i % 8, which
+//     loads it as the stream kernel does, transposes it through its LDS tile
+//     64 features at a time, scores it with the same products and stores
+//     each score's order-preserving key at its position in LDS (32768 keys
+//     fill 128 KiB; the eight tiles take the other 32 KiB);
 //   * select: a radix select over the LDS keys (digits of up to 11 bits cut
 //     from the row's key range, one histogram pass each) finds the K-th
 //     largest key; the keys above it and the first keys equal to it in
