@@ -1327,9 +1327,26 @@ __global__ __launch_bounds__(kFusedThreads, 1) void index_topk_kernel(
       sm.u.t.above = 0u;
     }
     __syncthreads();
-    for (int s = tid; s < n; s += kFusedThreads) {
-      const uint32_t k = sm.key[s];
-      if (k >= lo && k <= hi) atomicAdd(&sm.u.t.hist[(k - lo) >> shift], 1u);
+    // sixteen keys of a thread are read before their atomics (a read
+    // issued after an LDS atomic waits for it); 16-byte reads stay inside
+    // the key array (their first position is a multiple of 4 below n)
+    for (int s0 = tid * 4; s0 < n; s0 += kFusedThreads * 16) {
+      uint4 kv[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int s = s0 + u * kFusedThreads * 4;
+        kv[u] = s < n ? *reinterpret_cast<const uint4*>(&sm.key[s])
+                      : make_uint4(0, 0, 0, 0);
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int s = s0 + u * kFusedThreads * 4;
+        const uint32_t ks[4] = {kv[u].x, kv[u].y, kv[u].z, kv[u].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (s + e < n && ks[e] >= lo && ks[e] <= hi)
+            atomicAdd(&sm.u.t.hist[(ks[e] - lo) >> shift], 1u);
+      }
     }
     __syncthreads();
     // thread tid owns digits tid*kBinsPT .. +kBinsPT-1; keys in the digits
@@ -1375,10 +1392,18 @@ __global__ __launch_bounds__(kFusedThreads, 1) void index_topk_kernel(
   const int C = (n + kFusedThreads - 1) / kFusedThreads * kWave;
   const int s0 = wave * C, s1 = min(s0 + C, n);
   uint32_t ngt = 0u, neq = 0u;
-  for (int s = s0; s < s1; s += kWave) {
-    const uint32_t k = s + lane < s1 ? sm.key[s + lane] : 0u;
-    ngt += __builtin_popcountll(__ballot(k > thr));
-    neq += __builtin_popcountll(__ballot(k == thr));
+  for (int s = s0; s < s1; s += 4 * kWave) {   // four steps' reads first
+    uint32_t k[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int q = s + u * kWave + lane;
+      k[u] = q < s1 ? sm.key[q] : 0u;
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      ngt += __builtin_popcountll(__ballot(k[u] > thr));
+      neq += __builtin_popcountll(__ballot(k[u] == thr));
+    }
   }
   if (lane == 0) {
     sm.u.t.ngt[wave] = ngt;
@@ -1391,15 +1416,24 @@ __global__ __launch_bounds__(kFusedThreads, 1) void index_topk_kernel(
     eq_before += sm.u.t.neq[w];
   }
   uint32_t slot = gt_before + min(need, eq_before), eqr = eq_before;
-  for (int s = s0; s < s1; s += kWave) {
-    const uint32_t k = s + lane < s1 ? sm.key[s + lane] : 0u;
-    const uint64_t em = __ballot(k == thr);
-    const bool sel = k > thr || (k == thr && eqr + fused_lanes_below(em) < need);
-    const uint64_t sm_ = __ballot(sel);
-    const uint32_t o = slot + fused_lanes_below(sm_);   // < kk
-    if (sel && o < (uint32_t)K) out[o] = s + lane;
-    eqr += __builtin_popcountll(em);
-    slot += __builtin_popcountll(sm_);
+  for (int s = s0; s < s1; s += 4 * kWave) {
+    uint32_t k[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int q = s + u * kWave + lane;
+      k[u] = q < s1 ? sm.key[q] : 0u;
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const uint64_t em = __ballot(k[u] == thr);
+      const bool sel =
+          k[u] > thr || (k[u] == thr && eqr + fused_lanes_below(em) < need);
+      const uint64_t selm = __ballot(sel);
+      const uint32_t o = slot + fused_lanes_below(selm);   // < kk
+      if (sel && o < (uint32_t)K) out[o] = s + u * kWave + lane;
+      eqr += __builtin_popcountll(em);
+      slot += __builtin_popcountll(selm);
+    }
   }
 }
 
