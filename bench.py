@@ -395,13 +395,14 @@ def fused_comparison(stream, steps=20, warmup=5):
     LDS) against dsa_indexer_scores followed by dsa_topk (scores through
     HBM), on the bf16 decode batch's shape (32 rows of 32768) and on 256 rows
     of 4096 (the same key bytes, one row per CU), bf16 keys and MX block-32
-    e4m3 keys.  Integer-valued keys and queries in [-4, 4] (exact in e4m3
-    with unit scales), power-of-two weights; both paths' indices compared."""
+    e4m3 keys, the latter also with the fully quantised indexer.
+    Integer-valued keys and queries in [-4, 4] (exact in e4m3 with unit
+    scales), power-of-two weights; both paths' indices compared."""
     import torch
     import indexed_sparse_attention_lightning_amd as dsa
     res = {}
-    for B, L, mx in ((32, 32768, False), (256, 4096, False),
-                     (256, 4096, True)):
+    for B, L, mx, q8 in ((32, 32768, False, False), (256, 4096, False, False),
+                         (256, 4096, True, False), (256, 4096, True, True)):
         P, K, d_I, H_I = B * L // 64, 2048, 128, 64
         g = torch.Generator(device="cuda")
         g.manual_seed(B)
@@ -431,18 +432,19 @@ def fused_comparison(stream, steps=20, warmup=5):
         kc = kidx.view(B, L, d_I)
 
         def fused(i):
-            dsa.indexer_topk(cache, q_idx, w, K, L, q_pos=q_pos, idx_out=i1)
+            dsa.indexer_topk(cache, q_idx, w, K, L, q_pos=q_pos, idx_out=i1,
+                             quantize_queries=q8)
 
         def two(i):
             dsa.indexer_scores(q_idx, w, kc, q_pos, k_scale=kc_scale,
-                               out=scores)
+                               out=scores, quantize_queries=q8)
             dsa.topk(scores, q_pos, K, out=i2)
 
         ms_f = time_loop(fused, steps, warmup, stream)
         ms_2 = time_loop(two, steps, warmup, stream)
         torch.cuda.synchronize()
         kbytes = B * L * (d_I + d_I // 32 if mx else d_I * 2)
-        res[f"{B}x{L}" + ("_mx" if mx else "")] = {
+        res[f"{B}x{L}" + ("_mx" if mx else "") + ("_q8" if q8 else "")] = {
             "fused_us": round(ms_f * 1e3, 2),
             "indexer_then_topk_us": round(ms_2 * 1e3, 2),
             "fused_key_gbps": round(kbytes / (ms_f * 1e-3) / 1e9, 1),

@@ -223,18 +223,18 @@ dsa_status dsa_sparse_mla_attn(int B, int T, int L, int H, int K,
  * three steps in one kernel that reads the paged keys and outputs only the
  * final indices; page "Day-0 Inference Adaptation and Performance
  * Optimization for New-Architecture Large Language Models", "Fusing the
- * Indexer to Reduce Intermediate Write-Backs").  One workgroup per query row
- * keeps the row's scores in its LDS, so rows are limited to
- * DSA_FUSED_MAX_CONTEXT positions.  The same scores and the same selection
- * as dsa_indexer_scores followed by dsa_topk (ties to the lower position).
+ * Indexer to Reduce Intermediate Write-Backs"; both name a bf16 and a
+ * quantised path).  One workgroup per query row keeps the row's scores in
+ * its LDS, so rows are limited to DSA_FUSED_MAX_CONTEXT positions.  The same
+ * scores and the same selection as dsa_indexer_scores followed by dsa_topk
+ * (ties to the lower position).
  *   cache         page pools as for dsa_decode_step; only the indexer-key
  *                 fields, page_table and seq_lens are read (kv, kv_scale
  *                 may be NULL)
  *   max_seq_len   host upper bound of seq_lens, 1 .. DSA_FUSED_MAX_CONTEXT
  *                 (else DSA_ERR_UNSUPPORTED) and <= max_pages_per_seq * 64
- *   q_idx [B, T, H_I, d_I] bf16; q_mode must be DSA_Q_BF16 (the quantised
- *                 indexer runs only in the two-kernel path:
- *                 DSA_ERR_UNSUPPORTED)
+ *   q_idx [B, T, H_I, d_I] bf16; q_mode as for dsa_indexer_scores
+ *                 (DSA_Q_MX32 needs MX keys)
  *   w [B, T, H_I] fp32
  *   q_pos [B, T] int32, or NULL when T == 1: then q_pos = seq_lens[b] - 1;
  *                 positions are clamped to seq_lens[b] - 1

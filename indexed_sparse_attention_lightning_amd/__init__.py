@@ -387,12 +387,14 @@ def decode_step_static(cache: PagedCache, q_idx: torch.Tensor,
 def indexer_topk(cache: PagedCache, q_idx: torch.Tensor, w: torch.Tensor,
                  k: int, max_seq_len: int,
                  q_pos: Optional[torch.Tensor] = None,
-                 idx_out: Optional[torch.Tensor] = None):
+                 idx_out: Optional[torch.Tensor] = None,
+                 quantize_queries: bool = False):
     """Indexer scores and Top-K of every query row in one kernel (the scores
     never leave the chip) for q_idx [B, T, H_I, d_I] bf16 and w [B, T, H_I]
     fp32 over the paged key cache; max_seq_len <= FUSED_MAX_CONTEXT.  q_pos
-    [B, T] int32, or None for T == 1.  Returns idx [B, T, k] int32, the
-    same selection as indexer_scores followed by topk."""
+    [B, T] int32, or None for T == 1.  quantize_queries as for
+    indexer_scores (MX keys).  Returns idx [B, T, k] int32, the same
+    selection as indexer_scores followed by topk."""
     B, T, H_I, d_I = q_idx.shape
     _need(q_idx, "q_idx", torch.bfloat16)
     _need(w, "w", torch.float32, (B, T, H_I))
@@ -411,7 +413,8 @@ def indexer_topk(cache: PagedCache, q_idx: torch.Tensor, w: torch.Tensor,
     _need(idx_out, "idx_out", torch.int32, (B, T, k))
     _check(_lib.dsa_indexer_topk(
         B, T, H_I, d_I, k, ctypes.byref(c), int(max_seq_len), _ptr(q_idx),
-        DSA_Q_BF16, _ptr(w), _ptr(q_pos), _ptr(idx_out), _stream()),
+        DSA_Q_MX32 if quantize_queries else DSA_Q_BF16, _ptr(w), _ptr(q_pos),
+        _ptr(idx_out), _stream()),
         "dsa_indexer_topk")
     return idx_out
 

@@ -360,11 +360,12 @@ dsa_status decode_step_impl(int B, int T, int H_I, int d_I, int H, int K,
   // With a row for every CU, the single kernel that keeps each row's scores
   // in LDS matches or beats the score stream plus the Top-K launch (256 rows
   // of 4096 positions: 56 us against 47.5 + 9.7 us and a launch with bf16
-  // keys, 38 against 32 + 9.7 us with MX keys; 256 of 32768: 377 against
-  // 365 + 15 us); with fewer rows it leaves CUs idle (128 rows of 8192: 70
-  // against 50 + 10 us).  Several queries per sequence share key reads in
-  // the query-tiled indexer instead.
-  if (!ia.q8 && T < 8 && tokens >= 256 && max_seq_len <= dsa::kFusedMaxLen) {
+  // keys, 38 against 32 + 9.7 us with MX keys, 36 against 38 us through the
+  // entry points with quantised queries; 256 of 32768: 377 against 365 + 15
+  // us); with fewer rows it leaves CUs idle (128 rows of 8192: 70 against
+  // 50 + 10 us).  Several queries per sequence share key reads in the
+  // query-tiled indexer instead.
+  if (T < 8 && tokens >= 256 && max_seq_len <= dsa::kFusedMaxLen) {
     ia.row_len = max_seq_len;
     if (hipError_t e = dsa::launch_index_topk(ia, K, idx, st))
       return hip_status(e, "dsa_decode_step: fused indexer and Top-K");
@@ -457,9 +458,6 @@ dsa_status dsa_indexer_topk(int B, int T, int H_I, int d_I, int K,
   if (kfp8 && !cache->kidx_scale)
     return fail(DSA_ERR_NULL, "MX indexer keys need kidx_scale");
   if (dsa_status st = check_q_mode(q_mode, kfp8)) return st;
-  if (q_mode != DSA_Q_BF16)
-    return fail(DSA_ERR_UNSUPPORTED,
-                "dsa_indexer_topk: q_mode must be DSA_Q_BF16");
   static_assert(DSA_FUSED_MAX_CONTEXT == dsa::kFusedMaxLen, "LDS row bound");
   dsa::IndexerLaunch a{};
   a.B = B; a.T = T; a.H_I = H_I; a.d_I = d_I;
@@ -472,6 +470,7 @@ dsa_status dsa_indexer_topk(int B, int T, int H_I, int d_I, int K,
                               (kfp8 ? 1 : 2), false, cache->num_pages};
   a.qp = dsa::QueryPos{q_pos, cache->seq_lens, T};
   a.row_len = max_seq_len;
+  a.q8 = q_mode == DSA_Q_MX32;
   return hip_status(dsa::launch_index_topk(a, K, idx, (hipStream_t)stream),
                     "dsa_indexer_topk");
 }

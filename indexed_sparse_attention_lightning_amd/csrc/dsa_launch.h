@@ -70,8 +70,9 @@ hipError_t launch_indexer(const IndexerLaunch& a, hipStream_t stream);
 // runs, or 0 when it keeps no key ranges (a tile kernel for several queries
 // per sequence, or the FP8-key kernel with bf16 queries).
 int indexer_span_kpw(const IndexerLaunch& a);
-// Indexer and Top-K of each query row in one kernel (bf16 queries): one
-// workgroup per row holds the row's score keys in LDS, so rows are limited to
+// Indexer and Top-K of each query row in one kernel (bf16 or, with a.q8,
+// quantised queries): one workgroup per row holds the row's score keys in
+// LDS, so rows are limited to
 // kFusedMaxLen positions (a.row_len <= kFusedMaxLen); writes idx [B*T, K]
 // (ascending positions, -1 padded), no scores.
 constexpr int kFusedMaxLen = 32768;

@@ -1166,6 +1166,26 @@ __device__ __forceinline__ void pass_products_f8(const uint4* tile,
   }
 }
 
+// Quantised queries: k-step p of the scaled FP8 products (64 features, MX
+// blocks 2p and 2p+1) from a pass tile of key codes, as tile_scores_q8.
+template <int DI, int MB>
+__device__ __forceinline__ void pass_products_q8(const uint4* tile,
+                                                 const uint32_t* scl,
+                                                 const v8i (&a)[MB][DI / 64],
+                                                 const int (&as)[MB][DI / 64],
+                                                 f32x16 (&acc)[MB], int lane,
+                                                 int p) {
+  using CP = CodeLayout<kPassDI>;
+  const int n = lane & 31, h = lane >> 5;
+  const v8i bop = join8(tile[n * CP::kChunks + CP::slot(n, h)],
+                        tile[n * CP::kChunks + CP::slot(n, 2 + h)]);
+  const int bs = (int)((scl[n] >> (8 * (2 * p + h))) & 0xffu);
+#pragma unroll
+  for (int m = 0; m < MB; ++m)
+    acc[m] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+        a[m][p], bop, acc[m], 0, 0, 0, as[m][p], 0, bs);
+}
+
 // ReLU, head weights and the two wave halves: the score of key lane % 32.
 template <int MB>
 __device__ __forceinline__ float pass_epilogue(const f32x16 (&acc)[MB],
@@ -1183,6 +1203,10 @@ struct FusedShared {
   uint32_t key[kFusedMaxLen];   // score keys of positions 0 .. n-1
   union {
     uint4 tile[kFusedWaves][fused_tile_words<FP8>()];       // stream
+    struct {   // quantised queries: the (head block, k-step) shares
+      v8i code[4][kWave];
+      int scale[4][kWave];
+    } q;
     struct {                                                // select
       uint32_t hist[kFusedBins];
       uint32_t mn[kFusedWaves], mx[kFusedWaves];   // key range per wave
@@ -1198,9 +1222,10 @@ __device__ __forceinline__ uint32_t fused_lanes_below(uint64_t m) {
                                    __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
 }
 
-template <int DI, int MB, bool FP8>
+template <int DI, int MB, bool FP8, bool Q8>
 __global__ __launch_bounds__(kFusedThreads, 1) void index_topk_kernel(
     IndexerLaunch p, int K, int32_t* idx) {
+  static_assert(!Q8 || FP8, "quantised queries take MX keys");
   __shared__ FusedShared<FP8> sm;
   static_assert(sizeof(FusedShared<FP8>) <= 160 * 1024, "LDS");
   const int tid = threadIdx.x, lane = lane_id();
@@ -1220,12 +1245,45 @@ __global__ __launch_bounds__(kFusedThreads, 1) void index_topk_kernel(
   const int nst = (n + kSub - 1) / kSub;
   const int nsub = nst > wave ? (nst - wave + kFusedWaves - 1) / kFusedWaves : 0;
   uint32_t kmn = ~0u, kmx = 0u;
+  const int64_t qrow = (int64_t)b * p.T + t;
+  // quantised queries: wave i < MB * DI/64 quantises share i of the query
+  // into LDS (as the quantised stream kernel), every wave reads all shares
+  // into its operands, and a second barrier frees the space for the tiles
+  v8i qa[MB][DI / 64];
+  int qas[MB][DI / 64];
+  float qwv[MB][16];
+  if constexpr (Q8) {
+    constexpr int kShares = MB * (DI / 64);
+    static_assert(kShares <= 4 && kShares <= kFusedWaves, "query shares");
+    if (wave < kShares) {
+      const int qm = wave / (DI / 64), qks = wave % (DI / 64);
+      uint4 raw[4];
+      load_share_q8<DI>(p.q_idx + qrow * p.H_I * DI, p.H_I, qm, qks, lane,
+                        raw);
+      v8i c;
+      int sc;
+      quantise_share_q8(raw, qm * 32 + (lane & 31) < p.H_I, lane, c, sc);
+      sm.u.q.code[wave][lane] = c;
+      sm.u.q.scale[wave][lane] = sc;
+    }
+    const float wraw = p.w[qrow * p.H_I + min(lane, p.H_I - 1)];
+    __syncthreads();
+#pragma unroll
+    for (int m = 0; m < MB; ++m)
+#pragma unroll
+      for (int ks = 0; ks < DI / 64; ++ks) {
+        qa[m][ks] = sm.u.q.code[m * (DI / 64) + ks][lane];
+        qas[m][ks] = sm.u.q.scale[m * (DI / 64) + ks][lane];
+      }
+    spread_weights_q8<MB>(lane < p.H_I ? wraw : 0.f, lane, qwv);
+    __syncthreads();
+  }
   if (nsub > 0) {
-    const int64_t qrow = (int64_t)b * p.T + t;
     uint4 a[MB][DI / 16];
     float wv[MB][16];
-    load_query<DI, MB, FP8>(p.q_idx + qrow * p.H_I * DI, p.w + qrow * p.H_I,
-                            p.H_I, lane, a, wv);
+    if constexpr (!Q8)
+      load_query<DI, MB, FP8>(p.q_idx + qrow * p.H_I * DI, p.w + qrow * p.H_I,
+                              p.H_I, lane, a, wv);
     uint4* tile = sm.u.tile[wave];
     const int last = nsub - 1;
     // first position of the wave's stage j (stages past the last repeat it
@@ -1260,9 +1318,12 @@ __global__ __launch_bounds__(kFusedThreads, 1) void index_topk_kernel(
             if (q == kPasses - 1)
               stage_load_f8<DI>(st[u], p.keys, b, at(i + u + 4), lane,
                                 i + u + 4 > last);
-            pass_products_f8<DI, MB>(tile, a, scl, acc, lane, q);
+            if constexpr (Q8)
+              pass_products_q8<DI, MB>(tile, scl, qa, qas, acc, lane, q);
+            else
+              pass_products_f8<DI, MB>(tile, a, scl, acc, lane, q);
           }
-          const float sc = pass_epilogue<MB>(acc, wv);
+          const float sc = pass_epilogue<MB>(acc, Q8 ? qwv : wv);
           if (i + u < nsub) put(i + u, sc);
         }
       }
@@ -1437,10 +1498,10 @@ __global__ __launch_bounds__(kFusedThreads, 1) void index_topk_kernel(
   }
 }
 
-template <int DI, int MB, bool FP8>
+template <int DI, int MB, bool FP8, bool Q8 = false>
 hipError_t launch_fused(const IndexerLaunch& p, int K, int32_t* idx,
                         hipStream_t stream) {
-  hipLaunchKernelGGL((index_topk_kernel<DI, MB, FP8>), dim3(p.B * p.T),
+  hipLaunchKernelGGL((index_topk_kernel<DI, MB, FP8, Q8>), dim3(p.B * p.T),
                      dim3(kFusedThreads), 0, stream, p, K, idx);
   return hipGetLastError();
 }
@@ -1475,6 +1536,13 @@ int indexer_span_kpw(const IndexerLaunch& p) {
 hipError_t launch_index_topk(const IndexerLaunch& p, int K, int32_t* idx,
                              hipStream_t stream) {
   const bool mb1 = p.H_I <= 32;
+  if (p.q8) {   // quantised queries over MX keys
+    if (p.d_I == 128)
+      return mb1 ? launch_fused<128, 1, true, true>(p, K, idx, stream)
+                 : launch_fused<128, 2, true, true>(p, K, idx, stream);
+    return mb1 ? launch_fused<64, 1, true, true>(p, K, idx, stream)
+               : launch_fused<64, 2, true, true>(p, K, idx, stream);
+  }
   if (p.d_I == 128) {
     if (p.keys.fp8)
       return mb1 ? launch_fused<128, 1, true>(p, K, idx, stream)

@@ -200,8 +200,8 @@ def test_decode_step_static_validation():
 
 def test_indexer_topk_validation():
     """The fused indexer + Top-K checks its arguments before any HIP call:
-    rows beyond the LDS bound, quantised queries and the cache fields it
-    reads."""
+    rows beyond the LDS bound, quantised queries without MX keys and the
+    cache fields it reads."""
     c = dsa._PagedCacheC(64, 10, 1024, 0, 0, 0x1000, None, None, None,
                          0x1000, 0x1000)
 
@@ -226,10 +226,7 @@ def test_indexer_topk_validation():
     assert f(cache=short, msl=257) == SHAPE     # beyond max_pages * 64
     assert f(qm=-1) == UNSUP
     assert f(qm=1) == UNSUP                     # quantised queries: MX keys
-    mx = dsa._PagedCacheC(64, 10, 1024, 1, 0, 0x1000, 0x1000, None, None,
-                          0x1000, 0x1000)
-    assert f(cache=mx, qm=1) == UNSUP           # two-kernel path only
-    assert b"DSA_Q_BF16" in lib.dsa_last_error()
+    assert b"MX32 keys" in lib.dsa_last_error()
     assert f(cache=dsa._PagedCacheC(64, 10, 1024, 1, 0, 0x1000, None, None,
                                     None, 0x1000, 0x1000)) == NULL
     assert f(cache=dsa._PagedCacheC(64, 10, 1024, 2, 0, 0x1000, 0x1000, None,

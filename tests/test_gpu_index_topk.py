@@ -23,8 +23,9 @@ pytestmark = pytest.mark.gpu
 W = wk.WORKLOADS
 
 
-def oracle_idx(inp, rows):
-    """Oracle indexer scores and Top-K of the requested rows (no attention)."""
+def oracle_idx(inp, rows, quantize=False):
+    """Oracle indexer scores and Top-K of the requested rows (no attention);
+    ``quantize``: the fully quantised indexer's queries."""
     wl = inp.wl
     idx = np.full((wl.B, wl.T, wl.top_k), -2, dtype=np.int64)
     for b in sorted({b for b, _ in rows}):
@@ -36,18 +37,20 @@ def oracle_idx(inp, rows):
                 continue
             qp = int(inp.q_pos[b, t])
             n = min(qp + 1, int(inp.seq_lens[b]))
-            s = oracle.indexer_scores_row(oracle.indexer_queries(inp.q_idx[b, t]),
-                                          inp.w[b, t], keys[:n])
+            s = oracle.indexer_scores_row(
+                oracle.indexer_queries(inp.q_idx[b, t], quantize), inp.w[b, t],
+                keys[:n])
             idx[b, t] = oracle.topk_row(s, qp, wl.top_k)
     return idx
 
 
-def run_fused(inp, d, pass_qpos=None):
+def run_fused(inp, d, pass_qpos=None, q8=False):
     wl = inp.wl
     use_qpos = (wl.T > 1) if pass_qpos is None else pass_qpos
     idx = dsa.indexer_topk(paged_cache(d), d["q_idx"], d["w"], wl.top_k,
                            max_seq_len=int(inp.seq_lens.max()),
-                           q_pos=d["q_pos"] if use_qpos else None)
+                           q_pos=d["q_pos"] if use_qpos else None,
+                           quantize_queries=q8)
     torch.cuda.synchronize()
     return idx.cpu().numpy()
 
@@ -143,3 +146,49 @@ def test_decode_step_many_rows(name):
     print(f"decode step, fused rows {name}", flush=True)
     inp, d, _, (idx, _, _) = check_workload(wl)
     assert np.array_equal(idx, run_fused(inp, d))
+
+
+def test_decode_step_many_rows_quantised():
+    """The same with the fully quantised indexer (queries with fractional
+    parts, MX keys): the step's fused kernel quantises the queries."""
+    wl = STEP_CASES["step_128x2_mx"]
+    q = wk.eighths(7004, (wl.B, wl.T, wl.H_I, wl.d_I))
+    print("decode step, fused rows, quantised queries", flush=True)
+    inp, d, _, (idx, _, _) = check_workload(wl, q_idx=q, quantize_queries=True)
+    assert np.array_equal(idx, run_fused(inp, d, q8=True))
+
+
+# The fully quantised indexer in the fused kernel: queries with fractional
+# parts (multiples of 1/8, so that the MX quantisation changes them) over MX
+# keys; the oracle quantises the same queries.
+Q8_CASES = {
+    "q8_paged_ragged": (wk.Workload("q8_paged_ragged", 701, B=3, T=1, H_I=40,
+                                    d_I=64, top_k=300, H=16, int_range=4,
+                                    quantized=True, paged_random=True,
+                                    L_min=700, L_max=3000), 7001),
+    "q8_chunk": (wk.Workload("q8_chunk", 702, B=2, T=3, H_I=64, d_I=128,
+                             top_k=512, H=16, int_range=4, quantized=True,
+                             paged_random=True, L=4000, first_pos=3997), 7002),
+    "q8_full_decode_fp8": (W["decode_fp8"], 7003),
+}
+
+
+@pytest.mark.parametrize("name", sorted(Q8_CASES))
+def test_fused_quantised_queries(name):
+    """Every row against the oracle's quantised indexer, and (T = 1) the same
+    indices as the two-kernel decode step with quantised queries."""
+    wl, qseed = Q8_CASES[name]
+    print(f"fused q8 case {name}", flush=True)
+    inp = wk.generate(wl)
+    inp = dataclasses.replace(
+        inp, q_idx=wk.eighths(qseed, (wl.B, wl.T, wl.H_I, wl.d_I)))
+    d = to_device(inp)
+    rows = [(b, t) for b in range(wl.B) for t in range(wl.T)]
+    got = run_fused(inp, d, q8=True)
+    ref = oracle_idx(inp, rows, quantize=True)
+    assert_idx_equal(got, ref, rows)
+    plain = oracle_idx(inp, rows[:2])   # the quantisation matters here
+    assert any(not np.array_equal(plain[r], ref[r]) for r in rows[:2])
+    if wl.T == 1:
+        two, _, _ = run_decode_step(inp, d, quantize_queries=True)
+        assert np.array_equal(got, two)
