@@ -157,6 +157,22 @@ __device__ __forceinline__ void stage_store_f8(const StageF8<DI>& st,
   if (lane < kSub) scl[lane] = st.sc;
 }
 
+// ReLU and head weighting of a lane's accumulators, then the two wave
+// halves: the score of key lane % 32, the sum over heads of
+// w * max(0, q.k), accumulated in one running fp32 sum in head order.
+// (Four independent partial sums instead, which shorten the chain of
+// dependent instructions, measured the same on the prefill chunk.)
+template <int MB>
+__device__ __forceinline__ float head_weighted_relu(const f32x16 (&acc)[MB],
+                                                    const float (&wv)[MB][16]) {
+  float s = 0.f;
+#pragma unroll
+  for (int m = 0; m < MB; ++m)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s += wv[m][r] * relu(acc[m][r]);
+  return s + swap_halves(s);
+}
+
 // tile_scores for a code tile; `scl` holds the scale words of its keys.
 template <int DI, int MB>
 __device__ __forceinline__ float tile_scores_f8(const uint4* tile,
@@ -185,12 +201,7 @@ __device__ __forceinline__ float tile_scores_f8(const uint4* tile,
 #pragma unroll
     for (int m = 0; m < MB; ++m) acc[m] = mfma32(a[m][2 * j + 1], b1, acc[m]);
   }
-  float s = 0.f;
-#pragma unroll
-  for (int m = 0; m < MB; ++m)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) s += wv[m][r] * relu(acc[m][r]);
-  return s + swap_halves(s);
+  return head_weighted_relu<MB>(acc, wv);
 }
 
 // The value stored for a score: the score (+0 folds -0), or, for the fused
@@ -259,12 +270,7 @@ __device__ __forceinline__ float tile_scores(const uint4* tile,
 #pragma unroll
     for (int m = 0; m < MB; ++m) acc[m] = mfma32(a[m][ks], bop, acc[m]);
   }
-  float s = 0.f;
-#pragma unroll
-  for (int m = 0; m < MB; ++m)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) s += wv[m][r] * relu(acc[m][r]);
-  return s + swap_halves(s);
+  return head_weighted_relu<MB>(acc, wv);
 }
 
 // Loads one query's indexer vectors as MFMA A operands and its head weights
@@ -548,12 +554,7 @@ __device__ __forceinline__ float tile_scores_q8(const uint4* tile,
       acc[m] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
           a[m][ks], bop, acc[m], 0, 0, 0, as[m][ks], 0, bs);
   }
-  float s = 0.f;
-#pragma unroll
-  for (int m = 0; m < MB; ++m)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) s += wv[m][r] * relu(acc[m][r]);
-  return s + swap_halves(s);
+  return head_weighted_relu<MB>(acc, wv);
 }
 
 // Streaming indexer with quantised queries over MX keys: the grid, the
@@ -1186,18 +1187,6 @@ __device__ __forceinline__ void pass_products_q8(const uint4* tile,
         a[m][p], bop, acc[m], 0, 0, 0, as[m][p], 0, bs);
 }
 
-// ReLU, head weights and the two wave halves: the score of key lane % 32.
-template <int MB>
-__device__ __forceinline__ float pass_epilogue(const f32x16 (&acc)[MB],
-                                               const float (&wv)[MB][16]) {
-  float s = 0.f;
-#pragma unroll
-  for (int m = 0; m < MB; ++m)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) s += wv[m][r] * relu(acc[m][r]);
-  return s + swap_halves(s);
-}
-
 template <bool FP8>
 struct FusedShared {
   uint32_t key[kFusedMaxLen];   // score keys of positions 0 .. n-1
@@ -1323,7 +1312,7 @@ __global__ __launch_bounds__(kFusedThreads, 1) void index_topk_kernel(
             else
               pass_products_f8<DI, MB>(tile, a, scl, acc, lane, q);
           }
-          const float sc = pass_epilogue<MB>(acc, Q8 ? qwv : wv);
+          const float sc = head_weighted_relu<MB>(acc, Q8 ? qwv : wv);
           if (i + u < nsub) put(i + u, sc);
         }
       }
@@ -1348,7 +1337,7 @@ __global__ __launch_bounds__(kFusedThreads, 1) void index_topk_kernel(
                              i + u + NS > last);
             pass_products<DI, MB>(tile, a, acc, lane, q);
           }
-          const float sc = pass_epilogue<MB>(acc, wv);
+          const float sc = head_weighted_relu<MB>(acc, wv);
           if (i + u < nsub) put(i + u, sc);
         }
       }
