@@ -984,9 +984,24 @@ __global__ __launch_bounds__(kTileQ * kWave, 2) void indexer_tile_q8_kernel(
   if (i < nst) stage(i, st[0]);
 }
 
+// Keys per workgroup of the query-tiled kernels.  Each workgroup loads its
+// eight queries and fills its two-stage pipeline once, so long chunks pay
+// that over more stages: on the 4096-query prefill chunk (512 query tiles
+// of 61K-65K causal keys) 2048 keys per workgroup took 3.61 ms, 8192 3.43,
+// 32768 3.31 (quantised indexer 2.70, 2.44, 2.33 ms); from position 0
+// (rows up to 4096) 0.198 ms at 2048 against 0.166 at 4096.  The chunk is
+// sized for about 512 workgroups (two per CU) and kept within [2048, 32768]
+// keys, so that small grids keep the 2048-key chunks.
+int tile_kpw(const IndexerLaunch& p) {
+  const int64_t tiles = (int64_t)p.B * ((p.T + kTileQ - 1) / kTileQ);
+  int64_t kpw = (int64_t)p.row_len * tiles / 512;
+  kpw = (kpw + kStageKeys - 1) / kStageKeys * kStageKeys;
+  return (int)(kpw < 2048 ? 2048 : (kpw > 32768 ? 32768 : kpw));
+}
+
 template <int DI, int MB>
 hipError_t launch_tile_q8(const IndexerLaunch& p, hipStream_t stream) {
-  const int kpw = 2048;
+  const int kpw = tile_kpw(p);
   dim3 grid((p.row_len + kpw - 1) / kpw, (p.T + kTileQ - 1) / kTileQ, p.B);
   hipLaunchKernelGGL((indexer_tile_q8_kernel<DI, MB>), grid,
                      dim3(kTileQ * kWave), 0, stream, p, kpw);
@@ -995,8 +1010,7 @@ hipError_t launch_tile_q8(const IndexerLaunch& p, hipStream_t stream) {
 
 template <int DI, int MB, bool FP8>
 hipError_t launch_tile(const IndexerLaunch& p, hipStream_t stream) {
-  // chunks of 2048 keys: enough workgroups for 256 CUs at prefill sizes
-  const int kpw = 2048;
+  const int kpw = tile_kpw(p);
   dim3 grid((p.row_len + kpw - 1) / kpw, (p.T + kTileQ - 1) / kTileQ, p.B);
   hipLaunchKernelGGL((indexer_tile_kernel<DI, MB, FP8>), grid,
                      dim3(kTileQ * kWave), 0, stream, p, kpw);
