@@ -172,6 +172,24 @@ def test_full_prefill_sampled_rows():
     check_workload(W["prefill"], rows=rows, separate=True)
 
 
+@pytest.mark.parametrize("quantized", [False, True])
+def test_prefill_key_chunks_off_power_of_two(quantized):
+    """A mid-size prefill step (2 x 1200 queries at 7760..8959 of an 8960
+    context): the query-tiled indexers cut each tile's keys into chunks
+    sized for about two workgroups per CU, here 5376 keys, so every causal
+    row crosses a chunk boundary that is no multiple of 2048.  Sampled rows
+    of both sequences through the decode step and the separate entry points:
+    scores bit for bit, indices exactly, attention within tolerance; bf16
+    keys, or MX keys with the quantised indexer."""
+    wl = wk.scaled(W["prefill"], B=2, T=1200, L=8960, first_pos=7760,
+                   top_k=256, H=16, quantized=quantized,
+                   seed=131 if quantized else 130)
+    rows = [(b, t) for b in range(2)
+            for _, t in prefill_rows(T=1200, seed=78 + b, n_random=40)]
+    assert len(rows) == 2 * 72
+    check_workload(wl, rows=rows, separate=True, quantize_queries=quantized)
+
+
 def test_full_ragged_paged():
     check_workload(W["ragged"])
 
